@@ -1,0 +1,143 @@
+"""Differential attention forward for MI355X (gfx950): Python binding of libdiffattn.so.
+
+This module only marshals arguments (shapes, device pointers, the current HIP stream) into the C ABI declared in
+include/diffattn.h; every step of the computation runs in the library's HIP kernels.  torch supplies device memory
+and streams.  If the library has not been built, importing the binding's functions fails loudly: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdiffattn.so")
+
+DIFFATTN_BF16 = 0
+DIFFATTN_F32 = 1
+STATUS = {0: "DIFFATTN_OK", -1: "DIFFATTN_ERR_NULL", -2: "DIFFATTN_ERR_SHAPE", -3: "DIFFATTN_ERR_UNSUPPORTED",
+          -4: "DIFFATTN_ERR_ALIGN", -5: "DIFFATTN_ERR_LAYER", -6: "DIFFATTN_ERR_LAMBDA",
+          -7: "DIFFATTN_ERR_WORKSPACE", -8: "DIFFATTN_ERR_ALIAS", -9: "DIFFATTN_ERR_HIP"}
+EXPORTS = ["diffattn_fwd", "diffattn_decode", "diffattn_decode_workspace_bytes", "diffattn_lambda_init",
+           "diffattn_status_str", "diffattn_abi_version"]
+
+_lib = None
+
+
+class DiffAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_str(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdiffattn.so (built in-tree by build.py); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libdiffattn.so is not built ({LIB_PATH}); run differential_attention_fwd_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, c_int, c_float = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    L.diffattn_fwd.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, c_int, c_int, P]
+    L.diffattn_fwd.restype = c_int
+    L.diffattn_decode.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, c_int, c_int, P,
+                                  ctypes.c_size_t, P]
+    L.diffattn_decode.restype = c_int
+    L.diffattn_decode_workspace_bytes.argtypes = [i64, i64, i64, c_int]
+    L.diffattn_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.diffattn_lambda_init.argtypes = [c_int]
+    L.diffattn_lambda_init.restype = ctypes.c_double
+    L.diffattn_status_str.argtypes = [c_int]
+    L.diffattn_status_str.restype = ctypes.c_char_p
+    L.diffattn_abi_version.restype = c_int
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().diffattn_status_str(int(status)).decode()
+
+
+def diffattn_status_str(status: int) -> str:
+    return status_str(status)
+
+
+def diffattn_lambda_init(layer: int) -> float:
+    return float(lib().diffattn_lambda_init(int(layer)))
+
+
+def diffattn_abi_version() -> int:
+    return int(lib().diffattn_abi_version())
+
+
+def diffattn_decode_workspace_bytes(B: int, H: int, L: int, d: int) -> int:
+    return int(lib().diffattn_decode_workspace_bytes(int(B), int(H), int(L), int(d)))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DIFFATTN_BF16
+    if t.dtype == torch.float32:
+        return DIFFATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(stream, device) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return int(s.cuda_stream)
+
+
+def _check_tensors(ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def diffattn_fwd(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool, out=None, stream=None):
+    """Prefill: q1,k1,q2,k2 [B][H][N][d], v [B][H][N][2d] -> out [B][H][N][2d] (same dtype), on `stream`."""
+    import torch
+    _check_tensors((q1, k1, q2, k2, v))
+    B, H, N, d = q1.shape
+    if out is None:
+        out = torch.empty((B, H, N, 2 * d), dtype=q1.dtype, device=q1.device)
+    _check_tensors((out,))
+    for t, shp in ((k1, q1.shape), (q2, q1.shape), (k2, q1.shape), (v, (B, H, N, 2 * d)), (out, (B, H, N, 2 * d))):
+        if tuple(t.shape) != tuple(shp) or t.dtype != q1.dtype:
+            raise ValueError(f"shape/dtype mismatch: {tuple(t.shape)} {t.dtype}, expected {tuple(shp)} {q1.dtype}")
+    st = lib().diffattn_fwd(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
+                            out.data_ptr(), B, H, N, d, _dtype_code(q1), float(lam), int(layer), int(bool(causal)),
+                            _stream_handle(stream, q1.device))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_fwd")
+    return out
+
+
+def diffattn_decode(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool = True, out=None, workspace=None,
+                    stream=None):
+    """Decode: q1,q2 [B][H][d]; k1,k2 [B][H][L][d]; v [B][H][L][2d] -> out [B][H][2d], on `stream`."""
+    import torch
+    _check_tensors((q1, k1, q2, k2, v))
+    B, H, d = q1.shape
+    L = k1.shape[2]
+    if out is None:
+        out = torch.empty((B, H, 2 * d), dtype=q1.dtype, device=q1.device)
+    for t, shp in ((q2, (B, H, d)), (k1, (B, H, L, d)), (k2, (B, H, L, d)), (v, (B, H, L, 2 * d)),
+                   (out, (B, H, 2 * d))):
+        if tuple(t.shape) != tuple(shp) or t.dtype != q1.dtype:
+            raise ValueError(f"shape/dtype mismatch: {tuple(t.shape)} {t.dtype}, expected {tuple(shp)} {q1.dtype}")
+    need = diffattn_decode_workspace_bytes(B, H, L, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q1.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().diffattn_decode(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
+                               out.data_ptr(), B, H, L, d, _dtype_code(q1), float(lam), int(layer),
+                               int(bool(causal)), ws_ptr, ws_bytes, _stream_handle(stream, q1.device))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_decode")
+    return out

@@ -1,0 +1,248 @@
+// Split-K differential attention decode for gfx950 (bf16 caches, fp32 math, d = 64, 2d = 128).
+//
+// Operation (Ultralytics glossary "Differential Transformer", section on how differential attention works): one
+// query token per (batch, head) attends to the whole cache with the two softmax maps; output
+// sum_j (a_j - lambda b_j) v_j, then optionally the per-head RMS normalisation and the (1 - lambda_init) scale.
+//
+// The pass is HBM-bound (each cached byte is read once, 1.5 FLOP per byte), so the design is about streaming:
+//   * decode_split: one workgroup per (head, key split).  Phase 1 reads K1 and K2 rows with 16-byte loads, eight
+//     lanes per 128-byte row so every wave-wide load covers 1 KiB of contiguous cache, and keeps the split's
+//     scores in LDS.  Phase 2 takes the split's exact maximum and sum per map.  Phase 3 streams V rows (sixteen
+//     lanes per 256-byte row) and accumulates both maps' partial outputs in fp32.  The split's state
+//     (m, l, O[128]) per map goes to the workspace.
+//   * decode_merge: one wave per head merges the splits by log-sum-exp and applies the epilogue.
+#include "launch.h"
+
+namespace diffattn {
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 64;
+constexpr int DV = 128;
+constexpr int THREADS = 256;
+constexpr int MAX_SPLIT_KEYS = 1024;          // keys per split (scores of both maps fit in 8 KiB of LDS)
+constexpr int PART_FLOATS = 4 + 2 * DV;       // m1, l1, m2, l2, O1[128], O2[128]
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a[k]), __builtin_bit_cast(bf16x2, b[k]), acc,
+                                              false);
+    return acc;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) x += __shfl_xor(x, s);
+    return x;
+}
+
+struct SplitPlan {
+    int splits;      // key splits per head
+    int split_keys;  // keys per split (the last split may be shorter)
+};
+
+__host__ __device__ inline SplitPlan plan_splits(int64_t BH, int64_t L) {
+    // At least ceil(L / MAX_SPLIT_KEYS) splits; more for few heads so that the grid has >= ~2048 workgroups,
+    // but never below 64 keys per split.
+    int64_t s = (L + MAX_SPLIT_KEYS - 1) / MAX_SPLIT_KEYS;
+    const int64_t want = (2048 + BH - 1) / (BH > 0 ? BH : 1);
+    const int64_t cap = (L + 63) / 64;
+    if (s < want) s = want < cap ? want : cap;
+    if (s < 1) s = 1;
+    int64_t keys = (L + s - 1) / s;
+    s = (L + keys - 1) / keys;  // no empty split
+    return SplitPlan{(int)s, (int)keys};
+}
+
+__global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* __restrict__ gq1,
+                                                               const uint16_t* __restrict__ gk1,
+                                                               const uint16_t* __restrict__ gq2,
+                                                               const uint16_t* __restrict__ gk2,
+                                                               const uint16_t* __restrict__ gv,
+                                                               float* __restrict__ ws, int L, int splits,
+                                                               int split_keys) {
+    __shared__ float sc1[MAX_SPLIT_KEYS], sc2[MAX_SPLIT_KEYS];
+    __shared__ float red[4][8];
+    __shared__ float part[4][2 * DV];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int bh = blockIdx.x / splits;
+    const int sp = blockIdx.x % splits;
+    const int j0 = sp * split_keys;
+    const int n = min(L, j0 + split_keys) - j0;
+    const float c = LOG2E * 0.125f;  // log2(e) / sqrt(64)
+
+    const uint16_t* k1 = gk1 + ((size_t)bh * L + j0) * D;
+    const uint16_t* k2 = gk2 + ((size_t)bh * L + j0) * D;
+    const uint16_t* v = gv + ((size_t)bh * L + j0) * DV;
+
+    // Phase 1: scores.  Lane handles 16-byte chunk (lane % 8) of row (lane / 8) of an 8-row group; the workgroup
+    // covers 32 rows per step.
+    const int ch = lane & 7;
+    const u32x4 qa = *(const u32x4*)(gq1 + (size_t)bh * D + ch * 8);
+    const u32x4 qb = *(const u32x4*)(gq2 + (size_t)bh * D + ch * 8);
+    float mx1 = -INFINITY, mx2 = -INFINITY;
+    const int r_in = wave * 8 + (lane >> 3);
+#pragma unroll 4
+    for (int r0 = 0; r0 < n; r0 += 32) {
+        const int r = r0 + r_in;
+        const int rr = min(r, n - 1);
+        const u32x4 ka = *(const u32x4*)(k1 + (size_t)rr * D + ch * 8);
+        const u32x4 kb = *(const u32x4*)(k2 + (size_t)rr * D + ch * 8);
+        float s1 = dot8(qa, ka, 0.f), s2 = dot8(qb, kb, 0.f);
+        s1 += __shfl_xor(s1, 1); s2 += __shfl_xor(s2, 1);
+        s1 += __shfl_xor(s1, 2); s2 += __shfl_xor(s2, 2);
+        s1 += __shfl_xor(s1, 4); s2 += __shfl_xor(s2, 4);
+        s1 *= c;
+        s2 *= c;
+        if (r < n) {
+            if (ch == 0) { sc1[r] = s1; sc2[r] = s2; }
+            mx1 = fmaxf(mx1, s1);
+            mx2 = fmaxf(mx2, s2);
+        }
+    }
+    // Phase 2: exact split maximum and sum per map.
+    mx1 = wave_max(mx1);
+    mx2 = wave_max(mx2);
+    if (lane == 0) { red[wave][0] = mx1; red[wave][1] = mx2; }
+    __syncthreads();
+    const float m1 = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
+    const float m2 = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1]));
+    float z1 = 0.f, z2 = 0.f;
+    for (int r = tid; r < n; r += THREADS) {
+        const float p1 = __builtin_amdgcn_exp2f(sc1[r] - m1);
+        const float p2 = __builtin_amdgcn_exp2f(sc2[r] - m2);
+        sc1[r] = p1;
+        sc2[r] = p2;
+        z1 += p1;
+        z2 += p2;
+    }
+    z1 = wave_sum(z1);
+    z2 = wave_sum(z2);
+    if (lane == 0) { red[wave][2] = z1; red[wave][3] = z2; }
+    __syncthreads();
+
+    // Phase 3: partial outputs.  Lane handles channels 8*(lane % 16) .. +7 of row (lane / 16) of a 4-row group;
+    // the workgroup covers 16 rows per step.
+    const int vc = lane & 15;
+    const int vr_in = wave * 4 + (lane >> 4);
+    float a1[8], a2[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) { a1[k] = 0.f; a2[k] = 0.f; }
+#pragma unroll 4
+    for (int r0 = 0; r0 < n; r0 += 16) {
+        const int r = r0 + vr_in;
+        if (r < n) {
+            const u32x4 w = *(const u32x4*)(v + (size_t)r * DV + vc * 8);
+            const float p1 = sc1[r], p2 = sc2[r];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float lo = bf_lo(w[k]), hi = bf_hi(w[k]);
+                a1[2 * k] = __builtin_fmaf(p1, lo, a1[2 * k]);
+                a1[2 * k + 1] = __builtin_fmaf(p1, hi, a1[2 * k + 1]);
+                a2[2 * k] = __builtin_fmaf(p2, lo, a2[2 * k]);
+                a2[2 * k + 1] = __builtin_fmaf(p2, hi, a2[2 * k + 1]);
+            }
+        }
+    }
+    // Reduce the 4 row slots of the wave (lanes vc, vc+16, vc+32, vc+48), then the 4 waves through LDS.
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        a1[k] += __shfl_xor(a1[k], 16);
+        a1[k] += __shfl_xor(a1[k], 32);
+        a2[k] += __shfl_xor(a2[k], 16);
+        a2[k] += __shfl_xor(a2[k], 32);
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            part[wave][vc * 8 + k] = a1[k];
+            part[wave][DV + vc * 8 + k] = a2[k];
+        }
+    }
+    __syncthreads();
+    float* dst = ws + ((size_t)bh * splits + sp) * PART_FLOATS;
+    if (tid == 0) {
+        dst[0] = m1;
+        dst[1] = red[0][2] + red[1][2] + red[2][2] + red[3][2];
+        dst[2] = m2;
+        dst[3] = red[0][3] + red[1][3] + red[2][3] + red[3][3];
+    }
+    for (int k = tid; k < 2 * DV; k += THREADS) dst[4 + k] = part[0][k] + part[1][k] + part[2][k] + part[3][k];
+}
+
+// One wave per head: lane owns channels 2*lane and 2*lane + 1.
+__global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ ws, uint16_t* __restrict__ gout,
+                                                          int splits, Epilogue ep) {
+    const int bh = blockIdx.x;
+    const int lane = threadIdx.x;
+    const float* part = ws + (size_t)bh * splits * PART_FLOATS;
+    float M1 = -INFINITY, M2 = -INFINITY;
+    for (int s = 0; s < splits; ++s) {
+        M1 = fmaxf(M1, part[s * PART_FLOATS + 0]);
+        M2 = fmaxf(M2, part[s * PART_FLOATS + 2]);
+    }
+    float L1 = 0.f, L2 = 0.f, o1a = 0.f, o1b = 0.f, o2a = 0.f, o2b = 0.f;
+    for (int s = 0; s < splits; ++s) {
+        const float* p = part + s * PART_FLOATS;
+        const float w1 = __builtin_amdgcn_exp2f(p[0] - M1);
+        const float w2 = __builtin_amdgcn_exp2f(p[2] - M2);
+        L1 += w1 * p[1];
+        L2 += w2 * p[3];
+        o1a += w1 * p[4 + 2 * lane];
+        o1b += w1 * p[4 + 2 * lane + 1];
+        o2a += w2 * p[4 + DV + 2 * lane];
+        o2b += w2 * p[4 + DV + 2 * lane + 1];
+    }
+    const float inv1 = 1.f / L1, inv2 = ep.lambda / L2;
+    float ya = o1a * inv1 - o2a * inv2;
+    float yb = o1b * inv1 - o2b * inv2;
+    if (ep.normalise) {
+        const float ss = wave_sum(ya * ya + yb * yb);
+        const float r = __builtin_amdgcn_rsqf(ss * (1.f / DV) + 1e-5f) * ep.out_scale;
+        ya *= r;
+        yb *= r;
+    }
+    const unsigned w = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)ya) |
+                       ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)yb) << 16);
+    *(unsigned*)(gout + (size_t)bh * DV + 2 * lane) = w;
+}
+
+}  // namespace
+
+size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L) {
+    if (BH <= 0 || L <= 0) return 0;
+    const SplitPlan p = plan_splits(BH, L);
+    return (size_t)BH * (size_t)p.splits * PART_FLOATS * sizeof(float);
+}
+
+hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
+                                  const uint16_t* v, uint16_t* out, int64_t BH, int64_t L, Epilogue ep,
+                                  void* workspace, hipStream_t stream) {
+    const SplitPlan p = plan_splits(BH, L);
+    const int64_t blocks = BH * (int64_t)p.splits;
+    if (blocks > 0x7fffffff || BH > 0x7fffffff) return hipErrorInvalidValue;
+    float* ws = (float*)workspace;
+    hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1, q2, k2, v, ws,
+                       (int)L, p.splits, p.split_keys);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)BH), dim3(64), 0, stream, (const float*)ws, out, p.splits,
+                       ep);
+    return hipGetLastError();
+}
+
+}  // namespace diffattn

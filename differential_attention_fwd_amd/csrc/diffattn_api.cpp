@@ -1,0 +1,167 @@
+// C-ABI layer of libdiffattn.so: argument validation (before any HIP call), epilogue constants, dispatch.
+// The operation and every argument's meaning are documented in include/diffattn.h.
+#include "../../include/diffattn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+using diffattn::Epilogue;
+
+constexpr int ABI_VERSION = 1;
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// a * b with overflow check against a bound; returns false on overflow.
+bool mul_ok(int64_t a, int64_t b, int64_t* r) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *r = a * b;
+    return true;
+}
+
+int check_dtype_d(int dtype, int d) {
+    if (dtype == DIFFATTN_BF16) return d == 64 ? DIFFATTN_OK : DIFFATTN_ERR_UNSUPPORTED;
+    if (dtype == DIFFATTN_F32) return (d == 8 || d == 64) ? DIFFATTN_OK : DIFFATTN_ERR_UNSUPPORTED;
+    return DIFFATTN_ERR_UNSUPPORTED;
+}
+
+size_t elem_bytes(int dtype) { return dtype == DIFFATTN_BF16 ? 2 : 4; }
+
+int make_epilogue(float lambda, int layer, Epilogue* ep) {
+    if (layer < 0) return DIFFATTN_ERR_LAYER;
+    if (!isfinite(lambda)) return DIFFATTN_ERR_LAMBDA;
+    ep->lambda = lambda;
+    ep->normalise = layer >= 1 ? 1 : 0;
+    ep->out_scale = layer >= 1 ? (float)(1.0 - diffattn_lambda_init(layer)) : 1.0f;
+    return DIFFATTN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+double diffattn_lambda_init(int layer) {
+    if (layer < 1) return NAN;
+    return 0.8 - 0.6 * exp(-0.3 * (double)(layer - 1));
+}
+
+const char* diffattn_status_str(int status) {
+    switch (status) {
+        case DIFFATTN_OK: return "ok";
+        case DIFFATTN_ERR_NULL: return "a required pointer is NULL";
+        case DIFFATTN_ERR_SHAPE: return "invalid or unsupported size";
+        case DIFFATTN_ERR_UNSUPPORTED: return "unsupported dtype / head width combination";
+        case DIFFATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case DIFFATTN_ERR_LAYER: return "layer index must be >= 0";
+        case DIFFATTN_ERR_LAMBDA: return "lambda must be finite";
+        case DIFFATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case DIFFATTN_ERR_ALIAS: return "output or workspace overlaps another argument";
+        case DIFFATTN_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+int diffattn_abi_version(void) { return ABI_VERSION; }
+
+int diffattn_fwd(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out, int64_t B,
+                 int64_t H, int64_t N, int d, int dtype, float lambda, int layer, int causal, void* stream) {
+    if (B < 0 || H < 0 || N < 0) return DIFFATTN_ERR_SHAPE;
+    int st = check_dtype_d(dtype, d);
+    if (st) return st;
+    Epilogue ep;
+    st = make_epilogue(lambda, layer, &ep);
+    if (st) return st;
+    if (N > DIFFATTN_MAX_LEN) return DIFFATTN_ERR_SHAPE;
+    int64_t BH, rows, qk_elems, v_elems;
+    if (!mul_ok(B, H, &BH) || BH > INT32_MAX || !mul_ok(BH, N, &rows) || !mul_ok(rows, d, &qk_elems) ||
+        !mul_ok(rows, 2 * (int64_t)d, &v_elems))
+        return DIFFATTN_ERR_SHAPE;
+    if (rows == 0) return DIFFATTN_OK;
+    if (!q1 || !k1 || !q2 || !k2 || !v || !out) return DIFFATTN_ERR_NULL;
+    if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2) || !aligned16(v) || !aligned16(out))
+        return DIFFATTN_ERR_ALIGN;
+    const size_t eb = elem_bytes(dtype);
+    const size_t qk_bytes = (size_t)qk_elems * eb, v_bytes = (size_t)v_elems * eb;
+    const Span o{(uintptr_t)out, (uintptr_t)out + v_bytes};
+    const Span ins[5] = {{(uintptr_t)q1, (uintptr_t)q1 + qk_bytes}, {(uintptr_t)k1, (uintptr_t)k1 + qk_bytes},
+                         {(uintptr_t)q2, (uintptr_t)q2 + qk_bytes}, {(uintptr_t)k2, (uintptr_t)k2 + qk_bytes},
+                         {(uintptr_t)v, (uintptr_t)v + v_bytes}};
+    for (const Span& s : ins)
+        if (overlaps(o, s)) return DIFFATTN_ERR_ALIAS;
+
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == DIFFATTN_BF16)
+        return hip_status(diffattn::launch_prefill_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1,
+                                                            (const uint16_t*)q2, (const uint16_t*)k2,
+                                                            (const uint16_t*)v, (uint16_t*)out, BH, N, causal, ep, s));
+    return hip_status(diffattn::launch_attn_f32((const float*)q1, (const float*)k1, (const float*)q2, (const float*)k2,
+                                                (const float*)v, (float*)out, BH, N, N, d, causal, ep, s));
+}
+
+size_t diffattn_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
+    int64_t BH;
+    if (B < 0 || H < 0 || L <= 0 || L > DIFFATTN_MAX_LEN || d != 64 || !mul_ok(B, H, &BH) || BH > INT32_MAX)
+        return 0;
+    return diffattn::decode_bf16_workspace_bytes(BH, L);
+}
+
+int diffattn_decode(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
+                    int64_t B, int64_t H, int64_t L, int d, int dtype, float lambda, int layer, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    (void)causal;  // the single query is the last position: every cached key is visible either way
+    if (B < 0 || H < 0 || L < 0) return DIFFATTN_ERR_SHAPE;
+    if (L == 0 || L > DIFFATTN_MAX_LEN) return DIFFATTN_ERR_SHAPE;
+    int st = check_dtype_d(dtype, d);
+    if (st) return st;
+    Epilogue ep;
+    st = make_epilogue(lambda, layer, &ep);
+    if (st) return st;
+    int64_t BH, q_elems, kv_rows, k_elems, v_elems;
+    if (!mul_ok(B, H, &BH) || BH > INT32_MAX || !mul_ok(BH, d, &q_elems) || !mul_ok(BH, L, &kv_rows) ||
+        !mul_ok(kv_rows, d, &k_elems) || !mul_ok(kv_rows, 2 * (int64_t)d, &v_elems))
+        return DIFFATTN_ERR_SHAPE;
+    if (BH == 0) return DIFFATTN_OK;
+    if (!q1 || !k1 || !q2 || !k2 || !v || !out) return DIFFATTN_ERR_NULL;
+    if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2) || !aligned16(v) || !aligned16(out))
+        return DIFFATTN_ERR_ALIGN;
+    const size_t eb = elem_bytes(dtype);
+    const Span o{(uintptr_t)out, (uintptr_t)out + (size_t)q_elems * 2 * eb};
+    const Span ins[5] = {{(uintptr_t)q1, (uintptr_t)q1 + (size_t)q_elems * eb},
+                         {(uintptr_t)k1, (uintptr_t)k1 + (size_t)k_elems * eb},
+                         {(uintptr_t)q2, (uintptr_t)q2 + (size_t)q_elems * eb},
+                         {(uintptr_t)k2, (uintptr_t)k2 + (size_t)k_elems * eb},
+                         {(uintptr_t)v, (uintptr_t)v + (size_t)v_elems * eb}};
+    for (const Span& s : ins)
+        if (overlaps(o, s)) return DIFFATTN_ERR_ALIAS;
+
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == DIFFATTN_F32)  // exact fp32 path: one query row per head at the end of the cache
+        return hip_status(diffattn::launch_attn_f32((const float*)q1, (const float*)k1, (const float*)q2,
+                                                    (const float*)k2, (const float*)v, (float*)out, BH, 1, L, d, 1, ep,
+                                                    s));
+
+    const size_t need = diffattn::decode_bf16_workspace_bytes(BH, L);
+    if (!workspace || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DIFFATTN_ERR_ALIGN;
+    const Span w{(uintptr_t)workspace, (uintptr_t)workspace + need};
+    if (overlaps(w, o)) return DIFFATTN_ERR_ALIAS;
+    for (const Span& sp : ins)
+        if (overlaps(w, sp)) return DIFFATTN_ERR_ALIAS;
+    return hip_status(diffattn::launch_decode_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
+                                                       (const uint16_t*)k2, (const uint16_t*)v, (uint16_t*)out, BH, L,
+                                                       ep, workspace, s));
+}
+
+}  // extern "C"

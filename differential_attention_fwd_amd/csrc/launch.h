@@ -1,0 +1,33 @@
+// Internal launcher declarations shared by the C-ABI layer and the kernel translation units.
+// Every launcher assumes its arguments were validated by the ABI layer and only enqueues work on `stream`;
+// it returns the hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace diffattn {
+
+// Per-call epilogue parameters: raw output (layer 0) or RMS-normalised and scaled by (1 - lambda_init).
+struct Epilogue {
+    float lambda;      // weight of the second softmax map
+    int normalise;     // 0: raw (map1 - lambda map2) V; 1: RMS norm (eps 1e-5, no affine) then * out_scale
+    float out_scale;   // 1 - lambda_init(layer) when normalise
+};
+
+// bf16 prefill, d = 64, 2d = 128: fused one-pass kernel (two online softmaxes, two MFMA accumulators).
+hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
+                                   const uint16_t* v, uint16_t* out, int64_t BH, int64_t N, int causal,
+                                   Epilogue ep, hipStream_t stream);
+
+// fp32 path (d = 8 or 64), general Nq <= Nk with end-aligned causal mask; exact three-pass softmax per row.
+hipError_t launch_attn_f32(const float* q1, const float* k1, const float* q2, const float* k2, const float* v,
+                           float* out, int64_t BH, int64_t Nq, int64_t Nk, int d, int causal, Epilogue ep,
+                           hipStream_t stream);
+
+// bf16 decode, d = 64: split kernel writing per-split partial states, then the merge + epilogue kernel.
+size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L);
+hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
+                                  const uint16_t* v, uint16_t* out, int64_t BH, int64_t L, Epilogue ep,
+                                  void* workspace, hipStream_t stream);
+
+}  // namespace diffattn

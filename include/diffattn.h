@@ -1,0 +1,101 @@
+/*
+ * diffattn.h -- C ABI of the MI355X (gfx950) differential attention forward library, libdiffattn.so.
+ *
+ * Pages this API implements (the operation is restated here, not quoted):
+ *   [U] Ultralytics glossary entry "Differential Transformer", section on how differential attention works:
+ *       the worked PyTorch example (two query/key halves of width d per head, values of width 2d, two softmax
+ *       maps with scores divided by sqrt(d), their difference with weight lambda, times V) and the paragraph
+ *       after it (per-head normalisation of the output, then the (1 - lambda_init) scale with
+ *       lambda_init(l) = 0.8 - 0.6 exp(-0.3 (l - 1))).
+ *   [J] jisaku.com glossary entry "Differential Transformer (Diff Attention)", section "main features /
+ *       mechanism" (two query/key pairs, difference of the two softmax maps, learnable lambda).
+ *
+ * For each batch b, head h and query row i the library computes
+ *     a = softmax_j(q1_i . k1_j / sqrt(d)),  b = softmax_j(q2_i . k2_j / sqrt(d))     over the visible keys j
+ *     o = sum_j (a_j - lambda * b_j) v_j                                                (2d channels)
+ *     layer == 0: out_i = o
+ *     layer >= 1: out_i = o / sqrt(mean_c(o_c^2) + 1e-5) * (1 - lambda_init(layer))   (RMS norm, no affine)
+ * With `causal` set, key j is visible to query row i when j <= i + (Nk - Nq) (the lower triangle for a square
+ * prefill; a single decode query sees the whole cache).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library never allocates, frees or
+ *     synchronises.  Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream).  Outputs
+ *     are valid once the stream reaches the call; inputs must stay alive until then.
+ *   - Layouts are dense row-major ("contiguous"):
+ *         prefill: q1, k1, q2, k2 [B][H][N][d];  v, out [B][H][N][2d]
+ *         decode:  q1, q2 [B][H][d];  k1, k2 [B][H][L][d];  v [B][H][L][2d];  out [B][H][2d]
+ *   - Element type `dtype`: DIFFATTN_BF16 (inputs and output bf16, fp32 accumulation) or DIFFATTN_F32 (fp32
+ *     throughout).  Supported: bf16 with d = 64; fp32 with d = 8 or 64.  Anything else -> DIFFATTN_ERR_UNSUPPORTED.
+ *   - Every pointer must be 16-byte aligned.  `out` (and the decode workspace) must not overlap any input.
+ *   - Arguments are validated before any HIP call; on error nothing is launched and the status says why.
+ *     Nothing is printed and nothing is thrown across the ABI.
+ *   - Thread safety: no mutable global state; concurrent calls on different streams are independent.
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum diffattn_dtype { DIFFATTN_BF16 = 0, DIFFATTN_F32 = 1 };
+
+enum diffattn_status {
+    DIFFATTN_OK = 0,
+    DIFFATTN_ERR_NULL = -1,        /* a required pointer is NULL while there is work to do */
+    DIFFATTN_ERR_SHAPE = -2,       /* negative size, decode L == 0, or a size beyond the documented limits */
+    DIFFATTN_ERR_UNSUPPORTED = -3, /* (dtype, d) combination not implemented */
+    DIFFATTN_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    DIFFATTN_ERR_LAYER = -5,       /* layer < 0 */
+    DIFFATTN_ERR_LAMBDA = -6,      /* lambda is NaN or infinite */
+    DIFFATTN_ERR_WORKSPACE = -7,   /* decode workspace NULL or smaller than diffattn_decode_workspace_bytes() */
+    DIFFATTN_ERR_ALIAS = -8,       /* out or workspace overlaps an input (or each other) */
+    DIFFATTN_ERR_HIP = -9          /* the HIP runtime reported an error at launch */
+};
+
+/* Largest sequence / cache length accepted (per-head offsets are 32-bit inside the kernels). */
+#define DIFFATTN_MAX_LEN (1 << 24)
+
+/*
+ * Prefill (square, Nq = Nk = N): the whole forward pass for B x H heads of N tokens.
+ *   q1,k1,q2,k2: [B][H][N][d]; v, out: [B][H][N][2d]; element type `dtype`.
+ *   lambda: weight of the second map (finite).  layer: 0 = raw output, >= 1 = normalised and scaled by
+ *   1 - lambda_init(layer).  causal: 0 or non-zero.
+ * N == 0 or B*H == 0 is a successful no-op.  Returns a diffattn_status.
+ */
+int diffattn_fwd(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
+                 int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda, int layer, int causal,
+                 void *stream);
+
+/*
+ * Decode: one new query token per (b, h) against a cache of L keys (the query is position L - 1, so every key
+ * is visible and `causal` has no effect).  Split over the cache, then merged; the split partials live in a
+ * caller-provided device workspace of at least diffattn_decode_workspace_bytes(B, H, L, d) bytes (16-byte
+ * aligned, not overlapping anything else; its contents on entry are ignored and on exit are unspecified).
+ *   q1,q2: [B][H][d]; k1,k2: [B][H][L][d]; v: [B][H][L][2d]; out: [B][H][2d].
+ * L == 0 is DIFFATTN_ERR_SHAPE (a softmax over no keys is undefined); B*H == 0 is a no-op.
+ * The fp32 path evaluates the single row exactly and uses no workspace (it may be NULL); the workspace size
+ * function returns the bf16 requirement for d = 64 and 0 for any other d or for an empty problem.
+ */
+size_t diffattn_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int d);
+int diffattn_decode(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
+                    int64_t B, int64_t H, int64_t L, int d, int dtype, float lambda, int layer, int causal,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* lambda_init(layer) = 0.8 - 0.6 exp(-0.3 (layer - 1)) in double, for layer >= 1 ([U]); NaN for layer < 1. */
+double diffattn_lambda_init(int layer);
+
+/* Static description of a status code (never NULL). */
+const char *diffattn_status_str(int status);
+
+/* ABI version: bumped on any incompatible change. */
+int diffattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DIFFATTN_H */

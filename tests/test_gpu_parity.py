@@ -1,0 +1,283 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Tolerances: fp32 path max-abs <= 1e-5; bf16 path (outputs after normalisation) max-abs <= 2e-2 and
+mean-abs <= 2e-3.  Raw (layer 0) bf16 outputs are compared with the same bounds.
+"""
+import numpy as np
+import pytest
+
+import diffattn_inputs as di
+import differential_attention_fwd_amd as da
+import oracle
+
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("gpu")]
+
+F32_TOL = 1e-5
+BF16_MAX, BF16_MEAN = 2e-2, 2e-3
+
+
+def torch_mod():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return torch
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def dev_bf16(bits):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def dev_f32(x):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda:0")
+
+
+def host_bf16(t):
+    torch = torch_mod()
+    return di.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+
+
+def widen(inp):
+    return {k: di.bf16_bits_to_f32(v) for k, v in inp.items()}
+
+
+def lam_of(spec):
+    if isinstance(spec, tuple):
+        return float(np.float32(oracle.lambda_init(spec[1])))
+    return float(np.float32(spec))
+
+
+def check_bf16(got, ref, what):
+    err = np.abs(np.asarray(got, dtype=np.float64) - ref)
+    say(f"{what}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert np.isfinite(got).all(), what
+    assert err.max() <= BF16_MAX, f"{what}: max-abs {err.max():.3e}"
+    assert err.mean() <= BF16_MEAN, f"{what}: mean-abs {err.mean():.3e}"
+
+
+def run_prefill_bf16(inp, lam, layer, causal):
+    torch = torch_mod()
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    out = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], lam, layer, causal)
+    torch.cuda.synchronize()
+    return host_bf16(out)
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# The pages' worked example (fp32): n=6, d=8, lambda 0.8, non-causal, raw output and the difference map.
+# ---------------------------------------------------------------------------------------------------------------
+
+def test_worked_example_f32():
+    torch = torch_mod()
+    ex = di.worked_example()
+    say("case: worked example fp32 n6 d8")
+    dev = {k: dev_f32(ex[k]) for k in ("q1", "k1", "q2", "k2", "v")}
+    out = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.8, 0, False)
+    # V = [I | 0] copies the difference map into the first n output channels.
+    eye = np.zeros((1, 1, 6, 16), dtype=np.float32)
+    eye[0, 0, :, :6] = np.eye(6, dtype=np.float32)
+    wmap = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev_f32(eye), 0.8, 0, False)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    got_w = wmap.cpu().numpy()[0, 0, :, :6].astype(np.float64)
+    ref, ref_w = oracle.diffattn(ex["q1"], ex["k1"], ex["q2"], ex["k2"], ex["v"], float(np.float32(0.8)), 0, False,
+                                 want_diff=True)
+    assert np.abs(got - ref).max() <= F32_TOL
+    assert np.abs(got_w - ref_w[0, 0]).max() <= F32_TOL
+    assert np.abs(got_w.sum(axis=1) - 0.2).max() <= F32_TOL        # every row sums to 1 - lambda
+    assert int((got_w < 0).sum()) == 13                              # the pages' printed count
+
+
+@pytest.mark.parametrize("N,d,causal,layer", [(1, 8, True, 0), (37, 8, True, 2), (100, 64, False, 1),
+                                              (129, 64, True, 0)])
+def test_f32_path_vs_oracle(N, d, causal, layer):
+    torch = torch_mod()
+    inp = di.prefill_f32(2, 2, N, d, seed=20 + N)
+    say(f"case: fp32 prefill B2 H2 N{N} d{d} causal={causal} layer={layer}")
+    dev = {k: dev_f32(v) for k, v in inp.items()}
+    out = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.6, layer, causal)
+    torch.cuda.synchronize()
+    ref = oracle.diffattn(inp["q1"], inp["k1"], inp["q2"], inp["k2"], inp["v"], float(np.float32(0.6)), layer, causal)
+    assert np.abs(out.cpu().numpy() - ref).max() <= F32_TOL
+
+
+def test_f32_decode_vs_oracle():
+    torch = torch_mod()
+    B, H, L, d = 2, 3, 300, 8
+    q1, q2 = di.normal_f32(30, "q1", (B, H, d)), di.normal_f32(30, "q2", (B, H, d))
+    k1, k2 = di.normal_f32(30, "k1", (B, H, L, d)), di.normal_f32(30, "k2", (B, H, L, d))
+    v = di.normal_f32(30, "v", (B, H, L, 2 * d))
+    say("case: fp32 decode B2 H3 L300 d8")
+    out = da.diffattn_decode(dev_f32(q1), dev_f32(k1), dev_f32(q2), dev_f32(k2), dev_f32(v), 0.8, 1)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q1, k1, q2, k2, v, float(np.float32(0.8)), 1)
+    assert np.abs(out.cpu().numpy() - ref).max() <= F32_TOL
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# bf16 prefill: the workloads, ragged and edge shapes, invariants.
+# ---------------------------------------------------------------------------------------------------------------
+
+def test_prefill_n1024_full():
+    c = di.CONFIGS["prefill_n1024"]
+    inp = di.prefill_bf16(c["B"], c["H"], c["N"], c["d"], c["seed"])
+    lam = lam_of(c["lam"])
+    say("case: prefill B1 H8 N1024 causal layer 1 (full oracle)")
+    got = run_prefill_bf16(inp, lam, c["layer"], c["causal"])
+    f = widen(inp)
+    ref = oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam, c["layer"], c["causal"])
+    check_bf16(got, ref, "prefill N1024")
+
+
+def test_prefill_n4096_full():
+    c = di.CONFIGS["prefill_n4096"]
+    inp = di.prefill_bf16(c["B"], c["H"], c["N"], c["d"], c["seed"], outliers=True)
+    lam = lam_of(c["lam"])
+    say("case: prefill B4 H12 N4096 causal layer 12 outliers (full oracle)")
+    got = run_prefill_bf16(inp, lam, c["layer"], c["causal"])
+    f = widen(inp)
+    ref = oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam, c["layer"], c["causal"])
+    check_bf16(got, ref, "prefill N4096")
+
+
+def test_prefill_n65536_sampled():
+    c = di.CONFIGS["prefill_n65536"]
+    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
+    inp = di.prefill_bf16(B, H, N, d, c["seed"])
+    lam = lam_of(c["lam"])
+    say("case: prefill B1 H16 N65536 causal layer 24 (256 sampled rows)")
+    got = run_prefill_bf16(inp, lam, c["layer"], c["causal"])
+    fixed = [(h, i) for h in (0, H - 1) for i in (0, 1, 63, 64, 127, 128, 4095, 4096, N - 1)]
+    rng = np.random.default_rng(4)
+    rand = [(int(rng.integers(H)), int(rng.integers(N))) for _ in range(256 - len(fixed))]
+    pairs = fixed + rand
+    rows = np.array([h * N + i for h, i in pairs], dtype=np.int64)
+    f = widen(inp)
+    ref = oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam, c["layer"], True, rows=rows)
+    sub = got.reshape(B * H * N, 2 * d)[rows]
+    check_bf16(sub, ref, "prefill N65536 sampled")
+
+
+@pytest.mark.parametrize("B,H,N,causal,layer", [
+    (1, 1, 1, True, 1), (1, 2, 5, True, 0), (2, 1, 31, True, 2), (1, 2, 33, False, 1), (1, 1, 127, True, 0),
+    (2, 2, 129, True, 5), (1, 3, 200, False, 0), (1, 1, 257, True, 1), (3, 1, 1000, True, 3),
+    (1, 2, 1000, False, 7),
+])
+def test_prefill_ragged(B, H, N, causal, layer):
+    inp = di.prefill_bf16(B, H, N, 64, seed=100 + N)
+    lam = 0.8 if layer == 0 else lam_of(("lambda_init", layer))
+    say(f"case: prefill ragged B{B} H{H} N{N} causal={causal} layer={layer}")
+    got = run_prefill_bf16(inp, lam, layer, causal)
+    f = widen(inp)
+    ref = oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam, layer, causal)
+    check_bf16(got, ref, f"prefill N{N}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_row_sums_with_unit_values(causal):
+    """V all ones and raw output: every channel equals the row sum of the difference map, 1 - lambda."""
+    B, H, N = 1, 2, 300
+    inp = di.prefill_bf16(B, H, N, 64, seed=7)
+    inp["v"] = di.f32_to_bf16_bits(np.ones((B, H, N, 128), dtype=np.float32))
+    say(f"case: prefill unit values N{N} causal={causal}")
+    got = run_prefill_bf16(inp, 0.8, 0, causal)
+    check_bf16(got, np.full(got.shape, 0.2), "row sums")
+
+
+def test_prefill_identity_values_extract_map():
+    """V = [I | 0] (N <= 128): the raw output's first N channels are the difference map; its signs match."""
+    B, H, N = 1, 1, 96
+    inp = di.prefill_bf16(B, H, N, 64, seed=8)
+    eye = np.zeros((B, H, N, 128), dtype=np.float32)
+    eye[0, 0, :, :N] = np.eye(N, dtype=np.float32)
+    inp["v"] = di.f32_to_bf16_bits(eye)
+    say("case: prefill identity values N96")
+    got = run_prefill_bf16(inp, 0.8, 0, True)[0, 0, :, :N]
+    f = widen(inp)
+    _, ref_w = oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], float(np.float32(0.8)), 0, True,
+                               want_diff=True)
+    ref_w = ref_w[0, 0]
+    check_bf16(got, ref_w, "difference map")
+    clear = np.abs(ref_w) > 1e-2  # signs of weights well away from zero must agree
+    assert np.array_equal(np.sign(got[clear]), np.sign(ref_w[clear]))
+
+
+def test_prefill_lambda_zero_and_layer_ratio():
+    """lambda = 0 is plain attention (oracle); outputs at two layers differ by the ratio of their scales."""
+    inp = di.prefill_bf16(1, 2, 333, 64, seed=9)
+    f = widen(inp)
+    say("case: prefill lambda 0 N333")
+    got0 = run_prefill_bf16(inp, 0.0, 1, True)
+    check_bf16(got0, oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], 0.0, 1, True), "lambda 0")
+    got_a = run_prefill_bf16(inp, 0.5, 2, True)
+    got_b = run_prefill_bf16(inp, 0.5, 30, True)
+    ratio = (1 - oracle.lambda_init(30)) / (1 - oracle.lambda_init(2))
+    big = np.abs(got_a) > 0.05
+    rel = np.abs(got_b[big] / got_a[big] - ratio) / ratio
+    assert np.median(rel) < 1e-2 and rel.max() < 5e-2
+
+
+def test_prefill_deterministic():
+    torch = torch_mod()
+    inp = di.prefill_bf16(2, 3, 700, 64, seed=10)
+    say("case: prefill determinism N700")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    a = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.7, 4, True)
+    b = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.7, 4, True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# bf16 decode
+# ---------------------------------------------------------------------------------------------------------------
+
+def run_decode_bf16(inp, lam, layer):
+    torch = torch_mod()
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    out = da.diffattn_decode(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], lam, layer)
+    torch.cuda.synchronize()
+    return host_bf16(out)
+
+
+@pytest.mark.parametrize("B,H,L,layer", [(1, 1, 1, 1), (2, 3, 7, 0), (1, 2, 64, 1), (2, 2, 1000, 2),
+                                         (1, 4, 1025, 1), (3, 1, 4097, 0), (1, 1, 20000, 1)])
+def test_decode_ragged(B, H, L, layer):
+    inp = di.decode_bf16(B, H, L, 64, seed=200 + L)
+    say(f"case: decode B{B} H{H} L{L} layer={layer}")
+    got = run_decode_bf16(inp, 0.8, layer)
+    f = widen(inp)
+    ref = oracle.decode(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], float(np.float32(0.8)), layer)
+    check_bf16(got, ref, f"decode L{L}")
+
+
+def test_decode_l8192_full():
+    c = di.CONFIGS["decode_l8192"]
+    B, H, L, d = c["B"], c["H"], c["L"], c["d"]
+    inp = di.decode_bf16(B, H, L, d, c["seed"])
+    say("case: decode B64 H16 L8192 layer 1 (full oracle)")
+    got = run_decode_bf16(inp, lam_of(c["lam"]), c["layer"])
+    errs = []
+    for b0 in range(0, B, 8):   # widen and check 8 sequences at a time to bound host memory
+        f = {k: di.bf16_bits_to_f32(v[b0:b0 + 8]) for k, v in inp.items()}
+        ref = oracle.decode(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam_of(c["lam"]), c["layer"])
+        errs.append(np.abs(got[b0:b0 + 8] - ref))
+    err = np.concatenate(errs)
+    say(f"decode L8192: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
+
+
+def test_decode_matches_prefill_last_row():
+    """The decode of token L-1 equals the causal prefill's last row (same inputs, both on the GPU)."""
+    B, H, L = 1, 2, 513
+    inp = di.prefill_bf16(B, H, L, 64, seed=13)
+    say("case: decode vs prefill last row L513")
+    pre = run_prefill_bf16(inp, 0.8, 1, True)[:, :, -1]
+    dinp = {"q1": inp["q1"][:, :, -1], "q2": inp["q2"][:, :, -1], "k1": inp["k1"], "k2": inp["k2"], "v": inp["v"]}
+    dec = run_decode_bf16(dinp, 0.8, 1)
+    assert np.abs(pre - dec).max() <= 2e-2
