@@ -30,11 +30,15 @@ constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Note: the vector element is copied to a scalar before __builtin_bit_cast; bit-casting a subscripted vector
+// element directly (bit_cast(T, v[k])) compiles to element 0 for every k with this compiler.
 __device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a[k]), __builtin_bit_cast(bf16x2, b[k]), acc,
+    for (int k = 0; k < 4; ++k) {
+        const unsigned ak = a[k], bk = b[k];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ak), __builtin_bit_cast(bf16x2, bk), acc,
                                               false);
+    }
     return acc;
 }
 
