@@ -1,0 +1,241 @@
+"""Benchmark: differential attention causal prefill (B4 H12 N4096) and decode (B64 H16 L8192) on one MI355X.
+
+One step = one pass of the whole hot path on resident synthetic inputs: the fused prefill kernel at
+B=4, H=12, N=4096, d=64, 2d=128 (causal, layer 12, lambda = lambda_init(12), outlier query rows) followed by the
+split-K decode (split + merge kernels) at B=64, H=16, L=8192 (lambda 0.8, layer 1).  Each kernel is timed with HIP
+events recorded on the stream it is launched on.  Prints ONE JSON line.
+
+  value     prefill TFLOP/s, counting 12*d FLOP per unmasked (query, key) pair (two Q.K^T products of width d and
+            two P.V products of width 2d), i.e. B*H*N*(N+1)/2 pairs
+  roofline  the prefill kernel against the bf16 dense MFMA peak; decode carries its own against HBM bandwidth
+  cpu_baseline  the double-precision CPU oracle on a bounded row sample of the same prefill workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "diff-attn causal fwd TFLOP/s @N=4096 (% MFMA peak); decode GB/s (% HBM)"
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12   # 2516.6: 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+PREFILL = dict(B=4, H=12, N=4096, d=64, layer=12, seed=3)
+DECODE = dict(B=64, H=16, L=8192, d=64, layer=1, lam=0.8, seed=5)
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def prefill_pairs(B, H, N):
+    return B * H * N * (N + 1) // 2
+
+
+def decode_bytes(B, H, L, d):
+    """Algorithmic HBM bytes of one decode: K1, K2, V read once, Q1, Q2 read, out written (bf16)."""
+    return 2 * (2 * B * H * L * d + B * H * L * 2 * d + 2 * B * H * d + B * H * 2 * d)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def read_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches the current kernel source."""
+    import hashlib
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    rec = {}
+    for line in open(PROFILE_TRAFFIC):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            rec[k.strip()] = v.strip()
+    src = rec.get(f"{kernel}.source")
+    if not src:
+        return None
+    path = os.path.join(ROOT, src)
+    if not os.path.exists(path):
+        return None
+    digest = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    if digest != rec.get(f"{kernel}.source_sha256_16"):
+        return None  # kernel changed since the counters were taken
+    try:
+        return float(rec[f"{kernel}.hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp_bits, lam, layer, N, target_rows):
+    """Time the oracle on every k-th query row of the prefill workload (uniform over the causal row costs)."""
+    import numpy as np
+
+    import diffattn_inputs as di
+    import oracle
+
+    f = {k: di.bf16_bits_to_f32(v) for k, v in inp_bits.items()}
+    B, H = f["q1"].shape[:2]
+    total = B * H * N
+    stride = max(1, total // target_rows)
+    rows = np.arange(0, total, stride, dtype=np.int64)
+    pairs = int(((rows % N) + 1).sum())
+    threads = oracle.max_threads()
+    oracle.diffattn(f["q1"][:1, :1, :8], f["k1"][:1, :1, :8], f["q2"][:1, :1, :8], f["k2"][:1, :1, :8],
+                    f["v"][:1, :1, :8], lam, layer, True)  # load the library outside the timed region
+    t0 = time.perf_counter()
+    oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam, layer, True, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(pairs * 12 * 64 / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows.size} of {total} query rows (every {stride}th row, {pairs} unmasked pairs) of the "
+                      f"B4 H12 N4096 causal prefill, double precision, {dt:.2f} s on {threads} threads of "
+                      f"'{cpu_model()}'",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--cpu-rows", type=int, default=65536, help="oracle row sample size for cpu_baseline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (HBM counter calibration under rocprofv3)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import diffattn_inputs as di
+    import differential_attention_fwd_amd as da
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    da.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    P = PREFILL
+    p_bits = di.prefill_bf16(P["B"], P["H"], P["N"], P["d"], P["seed"], outliers=True)
+    p_lam = float(np.float32(da.diffattn_lambda_init(P["layer"])))
+    pq1, pk1, pq2, pk2, pv = (to_dev(p_bits[k]) for k in ("q1", "k1", "q2", "k2", "v"))
+    pout = torch.empty_like(pv)
+
+    Dc = DECODE
+    d_bits = di.decode_bf16(Dc["B"], Dc["H"], Dc["L"], Dc["d"], Dc["seed"])
+    dq1, dk1, dq2, dk2, dv = (to_dev(d_bits[k]) for k in ("q1", "k1", "q2", "k2", "v"))
+    del d_bits
+    dout = torch.empty((Dc["B"], Dc["H"], 2 * Dc["d"]), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(da.diffattn_decode_workspace_bytes(Dc["B"], Dc["H"], Dc["L"], Dc["d"]), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        da.diffattn_fwd(pq1, pk1, pq2, pk2, pv, p_lam, P["layer"], True, out=pout, stream=stream)
+
+    def decode():
+        da.diffattn_decode(dq1, dk1, dq2, dk2, dv, Dc["lam"], Dc["layer"], True, out=dout, workspace=ws,
+                           stream=stream)
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(stream)
+        prefill()
+        ev[k][1].record(stream)
+        decode()
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]
+    dec_ms = [ev[k][1].elapsed_time(ev[k][2]) for k in range(K)]
+    step_ms = [ev[k][0].elapsed_time(ev[k][2]) for k in range(K)]
+
+    pairs = prefill_pairs(P["B"], P["H"], P["N"])
+    f_exec = pairs * 12 * P["d"]
+    f_formula = pairs * 8 * P["d"]
+    pre_avg = sum(pre_ms) / K
+    pre_tflops = f_exec / (pre_avg * 1e-3) / 1e12
+    dbytes = decode_bytes(Dc["B"], Dc["H"], Dc["L"], Dc["d"])
+    dec_avg = sum(dec_ms) / K
+    dec_gbs = dbytes / (dec_avg * 1e-3) / 1e9
+
+    pre_traffic = read_traffic("prefill")
+    dec_traffic = read_traffic("decode")
+    result = {
+        "metric": METRIC,
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(sum(step_ms) / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal prefill B4 H12 N4096 d64 dv128 (layer 12, outlier rows) + decode B64 H16 L8192 "
+                        "d64 dv128 (lambda 0.8, layer 1)",
+            "prefill": {"B": P["B"], "H": P["H"], "N": P["N"], "d": P["d"], "dv": 2 * P["d"], "causal": True,
+                        "layer": P["layer"], "lambda": p_lam},
+            "decode": {"B": Dc["B"], "H": Dc["H"], "L": Dc["L"], "d": Dc["d"], "dv": 2 * Dc["d"],
+                       "layer": Dc["layer"], "lambda": Dc["lam"]},
+            "parallelism": "single GPU",
+        },
+        "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": pre_traffic},
+        "prefill": {"ms": round(pre_avg, 4), "ms_min": round(min(pre_ms), 4), "flops_exec": f_exec,
+                    "flops_formula": f_formula,
+                    "tflops_formula": round(f_formula / (pre_avg * 1e-3) / 1e12, 2)},
+        "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "ms": round(dec_avg, 4), "ms_min": round(min(dec_ms), 4),
+                   "bytes": dbytes,
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": dec_traffic}},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p_bits, p_lam, P["layer"], P["N"], args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -57,8 +57,9 @@ enum diffattn_status {
     DIFFATTN_ERR_HIP = -9          /* the HIP runtime reported an error at launch */
 };
 
-/* Largest sequence / cache length accepted (per-head offsets are 32-bit inside the kernels). */
-#define DIFFATTN_MAX_LEN (1 << 24)
+/* Largest sequence / cache length accepted: one head's V (L x 2d bf16) must stay below 4 GiB because the kernels
+ * address a head through a 32-bit buffer offset. */
+#define DIFFATTN_MAX_LEN (1 << 23)
 
 /*
  * Prefill (square, Nq = Nk = N): the whole forward pass for B x H heads of N tokens.

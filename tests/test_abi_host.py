@@ -83,7 +83,7 @@ def dec(lib, q1=A[0], k1=A[1], q2=A[2], k2=A[3], v=A[4], out=A[5], B=2, H=2, L=1
 
 @pytest.mark.parametrize("case,expect", [
     (dict(q1=None), E_NULL), (dict(k2=None), E_NULL), (dict(out=None), E_NULL),
-    (dict(B=-1), E_SHAPE), (dict(N=-5), E_SHAPE), (dict(N=(1 << 24) + 1), E_SHAPE), (dict(H=1 << 40), E_SHAPE),
+    (dict(B=-1), E_SHAPE), (dict(N=-5), E_SHAPE), (dict(N=(1 << 23) + 1), E_SHAPE), (dict(H=1 << 40), E_SHAPE),
     (dict(d=32), E_UNSUP), (dict(d=128), E_UNSUP), (dict(dtype=7), E_UNSUP), (dict(dtype=F32, d=16), E_UNSUP),
     (dict(q2=A[2] + 8), E_ALIGN), (dict(out=A[5] + 2), E_ALIGN),
     (dict(layer=-1), E_LAYER), (dict(lam=float("nan")), E_LAMBDA), (dict(lam=float("inf")), E_LAMBDA),
