@@ -39,6 +39,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = 64;
 constexpr int DV = 128;
@@ -47,7 +49,18 @@ constexpr int BN = 32;                          // keys per tile
 constexpr int THREADS = 256;
 constexpr int K_TILE_BYTES = BN * D * 2;        // 4 KiB
 constexpr int V_TILE_BYTES = BN * DV * 2;       // 8 KiB
-constexpr int STAGE_BYTES = 2 * K_TILE_BYTES + V_TILE_BYTES;
+constexpr int K_STAGES = 3;                     // K1+K2 ring: tile t in slot t % 3, loaded two tiles ahead
+constexpr int K_SLOT_BYTES = 2 * K_TILE_BYTES;
+constexpr int VR_STAGES = 3;                    // raw (row-major) V ring: tile t in slot t % 3, loaded three ahead
+
+// Compile-time ring slot.  Each ring slot is its own __shared__ array, so the compiler can tell an LDS read of one
+// slot from a direct load still landing in another and does not drain the prefetches before every LDS read.
+template <int V> struct Slot { static constexpr int value = V; };
+template <int S, class T> __device__ __forceinline__ T* pick3(T* a, T* b, T* c) {
+    if constexpr (S % 3 == 0) return a;
+    else if constexpr (S % 3 == 1) return b;
+    else return c;
+}
 constexpr float RESCALE_THRESHOLD = 8.0f;       // log2 units: p never exceeds 2^8 between rescales
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -66,6 +79,10 @@ __device__ __forceinline__ int vt_off(int c, int chunk) {
     return prow * 64 + ((chunk ^ ((c >> 2) & 3)) << 4);
 }
 __device__ __forceinline__ int key_pos(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
+
+// Raw V tile as loaded: row r (key) of 256 bytes = 16 chunks of 16 bytes; chunk c lives at c ^ (2 (r & 3)), so the
+// 4 rows x 32 bytes read by each 16-lane group of a transposing read hit 8 distinct bank quads.
+__device__ __forceinline__ int vr_off(int row, int chunk) { return row * 256 + ((chunk ^ ((row & 3) << 1)) << 4); }
 
 // Combine a per-lane value with the value of lane (l ^ 32).
 __device__ __forceinline__ float pair_max(float x) {
@@ -126,12 +143,28 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8): wait until at most `vm` vector
+// memory operations of this wave are outstanding and all LDS operations are done.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14); }
+
+// Workgroup barrier without the memory-model fence of __syncthreads (which would drain every outstanding load,
+// including prefetches meant to stay in flight).  Callers first wait for their own LDS traffic with s_waitcnt;
+// LDS is coherent inside the workgroup.  The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1,
                              const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
                              const uint16_t* __restrict__ gv, uint16_t* __restrict__ gout, int BH, int N,
                              int n_row_tiles, int causal, Epilogue ep) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char kr0[K_SLOT_BYTES], kr1[K_SLOT_BYTES], kr2[K_SLOT_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char vr0[V_TILE_BYTES], vr1[V_TILE_BYTES], vr2[V_TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char vtb[2 * V_TILE_BYTES];   // transposed V, double buffer
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -175,56 +208,65 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     // i.e. tile row 8 w + L / 8, stored chunk L % 8, which holds logical chunk (L % 8) ^ ((row >> 1) & 7).
     const int kd_row = 8 * wave + (lane >> 3);
     const unsigned kd_voff = kd_row * 128 + (((lane & 7) ^ ((kd_row >> 1) & 7)) << 4);
-    // V loads: thread owns keys 4 kg .. 4 kg + 3 and channels 4 cg .. 4 cg + 3, with kg = lane / 8 and
-    // cg = 8 wave + lane % 8 (a wave covers 32 channels of all 32 keys).
-    const int kg = lane >> 3, cg = 8 * wave + (lane & 7);
-    const unsigned v_voff = (4 * kg) * 256 + cg * 8;
-    // Transposed store targets of the thread's 4 channels (see vt_off): channel 4 cg + i lands in physical row
-    // 4 cg + (i ^ b), b = (cg >> 2) & 1, so rows i and i ^ 1 swap when b is set.
-    const int vpos = key_pos(4 * kg);
-    const int vt_base = vt_off(4 * cg, vpos >> 3) + (vpos & 7) * 2;  // = physical row 4 cg + b
-    const int vb = (cg >> 2) & 1;
-    const int vt_w0 = vt_base;                       // channel 4cg     -> row 4cg + b      (4cg+2: +128)
-    const int vt_w1 = vt_base + 64 - 128 * vb;       // channel 4cg + 1 -> row 4cg + (1^b)  (4cg+3: +128)
-    u32x2 st_v[4];
-
-    auto issue_loads = [&](int t, int buf) {
-        const int kv0 = t * BN;
-        unsigned char* base = lds + buf * STAGE_BYTES;
-        // The tile offset goes into the VGPR offset: the SGPR offset is not part of the buffer range check.
-        const unsigned ko = kd_voff + (unsigned)kv0 * 128u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk1, (lds_void*)(base + 1024 * wave), 16, (int)ko, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk2, (lds_void*)(base + K_TILE_BYTES + 1024 * wave), 16, (int)ko, 0, 0,
-                                                 0);
-        const unsigned vo = v_voff + (unsigned)kv0 * 256u;
+    // Raw V direct loads: wave w fills LDS bytes [1024 (w + 4 j), + 1024) of the raw tile for j = 0, 1; position
+    // p holds row p / 256 and stored chunk (p / 16) % 16, i.e. logical chunk stored ^ (2 (row & 3)).
+    unsigned vd_voff[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st_v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(vo + 256u * i), 0, 0);
+    for (int j = 0; j < 2; ++j) {
+        const int p = 1024 * (wave + 4 * j) + 16 * lane;
+        const int row = p >> 8, pchunk = (p >> 4) & 15;
+        vd_voff[j] = row * 256 + ((pchunk ^ ((row & 3) << 1)) << 4);
+    }
+    // Transpose raw V -> V^T with ds_read_b64_tr_b16.  A 16-lane group reads a block of 4 keys x 16 channels (lane
+    // 4 jj + q supplies key jj, channels 4 q .. 4 q + 3) and lane i receives channel i of the block for the 4 keys:
+    // 8 bytes of one V^T row, stored with one 64-bit write.  The 16 groups of the workgroup take 4 of the 64
+    // blocks each.
+    // Group g takes blocks g + 16 b (b = 0..3): keys 4 (g / 8) + 8 b .. + 3, channels 16 (g % 8) .. + 15.  Block b
+    // reads 2048 b bytes further into the raw tile; its keys sit at positions key_pos(4 (g / 8)) + {0, 4, 16, 20}[b],
+    // i.e. b = 1 is 8 bytes after b = 0 in the same chunk and b = 2, 3 are chunk ^ 2 (offset tr_wr_hi).
+    const int grp = tid >> 4, gl = tid & 15;
+    const int kgb0 = grp >> 3, cgb = grp & 7;
+    const int tr_ch = 16 * cgb + 4 * (gl & 3);   // first channel of the 8 bytes this lane supplies
+    const int tr_rd = vr_off(4 * kgb0 + (gl >> 2), tr_ch >> 3) + (tr_ch & 7) * 2;
+    const int tr_pos = key_pos(4 * kgb0);         // 0 or 8
+    const int tr_wr_lo = vt_off(16 * cgb + gl, tr_pos >> 3) + (tr_pos & 7) * 2;
+    const int tr_wr_hi = vt_off(16 * cgb + gl, (tr_pos >> 3) + 2) + (tr_pos & 7) * 2;
+
+    auto vslot = [&](int t) { return vtb + (t & 1) * V_TILE_BYTES; };
+    auto issue_k = [&](auto S, int t) {   // S = t % 3
+        unsigned char* slot = pick3<decltype(S)::value>(kr0, kr1, kr2);
+        // The tile offset goes into the VGPR offset: the SGPR offset is not part of the buffer range check.
+        const unsigned ko = kd_voff + (unsigned)t * (BN * 128u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk1, (lds_void*)(slot + 1024 * wave), 16, (int)ko, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk2, (lds_void*)(slot + K_TILE_BYTES + 1024 * wave), 16, (int)ko, 0, 0,
+                                                 0);
     };
-    // Transpose the thread's 4 keys x 4 channels and store channel-major.
-    auto store_v = [&](int buf) {
-        unsigned char* vt = lds + buf * STAGE_BYTES + 2 * K_TILE_BYTES;
-        u32x2 w[4];
-        w[0][0] = __builtin_amdgcn_perm(st_v[1][0], st_v[0][0], 0x05040100u);
-        w[0][1] = __builtin_amdgcn_perm(st_v[3][0], st_v[2][0], 0x05040100u);
-        w[1][0] = __builtin_amdgcn_perm(st_v[1][0], st_v[0][0], 0x07060302u);
-        w[1][1] = __builtin_amdgcn_perm(st_v[3][0], st_v[2][0], 0x07060302u);
-        w[2][0] = __builtin_amdgcn_perm(st_v[1][1], st_v[0][1], 0x05040100u);
-        w[2][1] = __builtin_amdgcn_perm(st_v[3][1], st_v[2][1], 0x05040100u);
-        w[3][0] = __builtin_amdgcn_perm(st_v[1][1], st_v[0][1], 0x07060302u);
-        w[3][1] = __builtin_amdgcn_perm(st_v[3][1], st_v[2][1], 0x07060302u);
-        *(u32x2*)(vt + vt_w0) = w[0];
-        *(u32x2*)(vt + vt_w1) = w[1];
-        *(u32x2*)(vt + vt_w0 + 128) = w[2];
-        *(u32x2*)(vt + vt_w1 + 128) = w[3];
+    auto issue_v = [&](auto S, int t) {   // S = t % 3
+        unsigned char* slot = pick3<decltype(S)::value>(vr0, vr1, vr2);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(slot + 1024 * (wave + 4 * j)), 16,
+                                                     (int)(vd_voff[j] + (unsigned)t * (BN * 256u)), 0, 0, 0);
+    };
+    auto transpose_v = [&](auto S, int t) {   // S = t % 3
+        const unsigned char* raw = pick3<decltype(S)::value>(vr0, vr1, vr2);
+        unsigned char* vt = vslot(t);
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(raw + tr_rd));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(raw + tr_rd + 2048));
+        const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(raw + tr_rd + 4096));
+        const s16x4 x3 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(raw + tr_rd + 6144));
+        *(s16x4*)(vt + tr_wr_lo) = x0;
+        *(s16x4*)(vt + tr_wr_lo + 8) = x1;
+        *(s16x4*)(vt + tr_wr_hi) = x2;
+        *(s16x4*)(vt + tr_wr_hi + 8) = x3;
     };
 
     // Per-lane read offsets: K A-operand (row l32, chunk 2 kc + h) and V^T A-operand (channel 32 cb + l32,
     // chunk 2 ks + h; the four channel blocks are 2 KiB apart).
-    int k_rd[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) k_rd[kc] = k_off(l32, 2 * kc + h);
-    const int v_rd0 = 2 * K_TILE_BYTES + vt_off(l32, h);
-    const int v_rd1 = 2 * K_TILE_BYTES + vt_off(l32, 2 + h);
+    // k_off(l32, 2 kc + h) = k_rd0 ^ (32 kc): the chunk swizzle is an XOR on bits 4..6 of the offset.
+    const int k_rd0 = k_off(l32, h);
+    const int v_rd0 = vt_off(l32, h);
+    const int v_rd1 = vt_off(l32, 2 + h);
 
     f32x16 o1[4], o2[4];
 #pragma unroll
@@ -234,22 +276,37 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
     const float c = LOG2E * 0.125f;  // log2(e) / sqrt(64)
 
-    issue_loads(0, 0);
-    store_v(0);
-    for (int t = 0; t < n_tiles; ++t) {
-        __builtin_amdgcn_s_waitcnt(0);   // this thread's direct K loads and V stores of tile t are complete
-        __syncthreads();
-        if (t + 1 < n_tiles) issue_loads(t + 1, (t + 1) & 1);
+    // Load schedule.  Iteration t (between two workgroup barriers) issues the direct loads of K(t + 2) and raw
+    // V(t + 3), transposes raw V(t + 1) into the V^T buffer of tile t + 1, and computes tile t.  At its end it waits
+    // for everything but its own loads, so a load issued in iteration u is usable from iteration u + 1 on
+    // (and has had the whole of iteration u to land).
+    issue_k(Slot<0>{}, 0);
+    issue_v(Slot<0>{}, 0);
+    issue_k(Slot<1>{}, 1);
+    issue_v(Slot<1>{}, 1);
+    issue_v(Slot<2>{}, 2);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2));   // K(0), V(0), K(1), V(1) landed; V(2) may be in flight
+    lds_barrier();
+    transpose_v(Slot<0>{}, 0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2));
+    lds_barrier();
+    auto step = [&](auto S, int t) {   // S = t % 3
+        constexpr int s0 = decltype(S)::value;
+        issue_k(Slot<(s0 + 2) % 3>{}, t + 2);
+        issue_v(Slot<s0>{}, t + 3);
+        transpose_v(Slot<(s0 + 1) % 3>{}, t + 1);
         const int kv0 = t * BN;
         if (!causal || kv0 <= q0w + 31) {
-            const unsigned char* base = lds + (t & 1) * STAGE_BYTES;
+            const unsigned char* kb_ = pick3<s0>(kr0, kr1, kr2);
+            const unsigned char* vb_ = vslot(t);
             f32x16 s1, s2;
 #pragma unroll
             for (int i = 0; i < 16; ++i) { s1[i] = 0.f; s2[i] = 0.f; }
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
-                const bf16x8 ka = *(const bf16x8*)(base + k_rd[kc]);
-                const bf16x8 kb = *(const bf16x8*)(base + K_TILE_BYTES + k_rd[kc]);
+                const int kro = k_rd0 ^ (32 * kc);
+                const bf16x8 ka = *(const bf16x8*)(kb_ + kro);
+                const bf16x8 kb = *(const bf16x8*)(kb_ + K_TILE_BYTES + kro);
                 s1 = mfma(ka, qa[kc], s1);
                 s2 = mfma(kb, qb[kc], s2);
             }
@@ -270,12 +327,12 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
             exp_pack(s1, m1, l1, c, p1[0], p1[1]);
             bf16x8 va[4][2];
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) va[cb][0] = *(const bf16x8*)(base + v_rd0 + 2048 * cb);
+            for (int cb = 0; cb < 4; ++cb) va[cb][0] = *(const bf16x8*)(vb_ + v_rd0 + 2048 * cb);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o1[cb] = mfma(va[cb][0], p1[0], o1[cb]);
             exp_pack(s2, m2, l2, c, p2[0], p2[1]);
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) va[cb][1] = *(const bf16x8*)(base + v_rd1 + 2048 * cb);
+            for (int cb = 0; cb < 4; ++cb) va[cb][1] = *(const bf16x8*)(vb_ + v_rd1 + 2048 * cb);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o2[cb] = mfma(va[cb][0], p2[0], o2[cb]);
 #pragma unroll
@@ -283,8 +340,18 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o2[cb] = mfma(va[cb][1], p2[1], o2[cb]);
         }
-        if (t + 1 < n_tiles) store_v((t + 1) & 1);
+        // K(t + 2) and V(t + 3) (2 + 2 operations per thread) may stay in flight past the barrier; everything older,
+        // in particular K(t + 1) and V(t + 2), has landed, and the transposed V(t + 1) is written.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4));
+        lds_barrier();
+    };
+    for (int t = 0; t < n_tiles; t += 3) {
+        step(Slot<0>{}, t);
+        if (t + 1 < n_tiles) step(Slot<1>{}, t + 1);
+        if (t + 2 < n_tiles) step(Slot<2>{}, t + 2);
     }
+    // Drain the trailing prefetches before the workgroup can retire (their LDS writes must not outlive it).
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
     // Epilogue: lane owns query row q0w + l32 and channels cb*32 + 8*(i/4) + 4h + i%4.
     l1 = pair_sum(l1);
