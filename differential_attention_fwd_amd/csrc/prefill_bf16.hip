@@ -44,22 +44,24 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = 64;
 constexpr int DV = 128;
-constexpr int BM = 128;                         // query rows per workgroup
+constexpr int WAVES = 4;                        // waves per workgroup, 32 query rows each
+constexpr int BM = 32 * WAVES;                  // query rows per workgroup
 constexpr int BN = 32;                          // keys per tile
-constexpr int THREADS = 256;
+constexpr int THREADS = 64 * WAVES;
 constexpr int K_TILE_BYTES = BN * D * 2;        // 4 KiB
 constexpr int V_TILE_BYTES = BN * DV * 2;       // 8 KiB
-constexpr int K_STAGES = 3;                     // K1+K2 ring: tile t in slot t % 3, loaded two tiles ahead
+constexpr int RING = 4;                         // ring slots: K tile t in slot t % 4 (loaded three tiles ahead),
+                                                // raw V tile t in slot t % 4 (loaded four ahead)
 constexpr int K_SLOT_BYTES = 2 * K_TILE_BYTES;
-constexpr int VR_STAGES = 3;                    // raw (row-major) V ring: tile t in slot t % 3, loaded three ahead
 
 // Compile-time ring slot.  Each ring slot is its own __shared__ array, so the compiler can tell an LDS read of one
 // slot from a direct load still landing in another and does not drain the prefetches before every LDS read.
 template <int V> struct Slot { static constexpr int value = V; };
-template <int S, class T> __device__ __forceinline__ T* pick3(T* a, T* b, T* c) {
-    if constexpr (S % 3 == 0) return a;
-    else if constexpr (S % 3 == 1) return b;
-    else return c;
+template <int S, class T> __device__ __forceinline__ T* pick4(T* a, T* b, T* c, T* d) {
+    if constexpr (S % 4 == 0) return a;
+    else if constexpr (S % 4 == 1) return b;
+    else if constexpr (S % 4 == 2) return c;
+    else return d;
 }
 constexpr float RESCALE_THRESHOLD = 8.0f;       // log2 units: p never exceeds 2^8 between rescales
 constexpr float LOG2E = 1.4426950408889634f;
@@ -162,13 +164,15 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
                              const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
                              const uint16_t* __restrict__ gv, uint16_t* __restrict__ gout, int BH, int N,
                              int n_row_tiles, int causal, Epilogue ep) {
-    __shared__ __attribute__((aligned(16))) unsigned char kr0[K_SLOT_BYTES], kr1[K_SLOT_BYTES], kr2[K_SLOT_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char vr0[V_TILE_BYTES], vr1[V_TILE_BYTES], vr2[V_TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char kr0[K_SLOT_BYTES], kr1[K_SLOT_BYTES], kr2[K_SLOT_BYTES],
+        kr3[K_SLOT_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char vr0[V_TILE_BYTES], vr1[V_TILE_BYTES], vr2[V_TILE_BYTES],
+        vr3[V_TILE_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char vtb[2 * V_TILE_BYTES];   // transposed V, double buffer
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int h = lane >> 5;     // which half of the accumulator's key rows this lane holds
     const int l32 = lane & 31;   // this lane's query row inside the wave
 
@@ -204,61 +208,77 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     const int q_last = min(N, q0 + BM) - 1;
     const int n_tiles = causal ? (q_last / BN + 1) : (N + BN - 1) / BN;
 
-    // K direct loads: wave w fills LDS bytes [1024 w, 1024 w + 1024) of each K tile, lane L position 16 L of that,
-    // i.e. tile row 8 w + L / 8, stored chunk L % 8, which holds logical chunk (L % 8) ^ ((row >> 1) & 7).
-    const int kd_row = 8 * wave + (lane >> 3);
-    const unsigned kd_voff = kd_row * 128 + (((lane & 7) ^ ((kd_row >> 1) & 7)) << 4);
-    // Raw V direct loads: wave w fills LDS bytes [1024 (w + 4 j), + 1024) of the raw tile for j = 0, 1; position
-    // p holds row p / 256 and stored chunk (p / 16) % 16, i.e. logical chunk stored ^ (2 (row & 3)).
-    unsigned vd_voff[2];
+    // Direct loads: each wave moves one 1 KiB piece per tile and tensor role.  K1 and K2 tiles (4 KiB each) are 8
+    // pieces, the raw V tile (8 KiB) another 8; piece x of a tile covers its bytes [1024 x, 1024 x + 1024) and lane L
+    // writes position 16 L of it.  Loads are issued unconditionally, also for tiles past the end: those buffer loads
+    // are out of range and read zeros, and they land in ring slots no wave reads again.  The number of vector-memory
+    // operations per iteration is therefore fixed, which makes the waits below exact.
+    constexpr int K_PIECES_PER_WAVE = 8 / WAVES;   // K1 + K2 pieces per wave and tile
+    constexpr int V_PIECES_PER_WAVE = 8 / WAVES;
+    unsigned kd_voff[K_PIECES_PER_WAVE], vd_voff[V_PIECES_PER_WAVE];
+    int kd_lds[K_PIECES_PER_WAVE];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int p = 1024 * (wave + 4 * j) + 16 * lane;
+    for (int j = 0; j < K_PIECES_PER_WAVE; ++j) {
+        const int piece = wave + WAVES * j;        // 0..3: K1, 4..7: K2
+        // K tile row 8 (piece % 4) + L / 8, stored chunk L % 8 = logical chunk ^ ((row >> 1) & 7) (see k_off).
+        const int row = 8 * (piece & 3) + (lane >> 3);
+        kd_voff[j] = row * 128 + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
+        kd_lds[j] = (piece >> 2) * K_TILE_BYTES + 1024 * (piece & 3);
+    }
+#pragma unroll
+    for (int j = 0; j < V_PIECES_PER_WAVE; ++j) {
+        // Raw V: position p holds row p / 256 and stored chunk (p / 16) % 16 = logical chunk ^ (2 (row & 3)).
+        const int p = 1024 * (wave + WAVES * j) + 16 * lane;
         const int row = p >> 8, pchunk = (p >> 4) & 15;
         vd_voff[j] = row * 256 + ((pchunk ^ ((row & 3) << 1)) << 4);
     }
     // Transpose raw V -> V^T with ds_read_b64_tr_b16.  A 16-lane group reads a block of 4 keys x 16 channels (lane
     // 4 jj + q supplies key jj, channels 4 q .. 4 q + 3) and lane i receives channel i of the block for the 4 keys:
-    // 8 bytes of one V^T row, stored with one 64-bit write.  The 16 groups of the workgroup take 4 of the 64
-    // blocks each.
-    // Group g takes blocks g + 16 b (b = 0..3): keys 4 (g / 8) + 8 b .. + 3, channels 16 (g % 8) .. + 15.  Block b
-    // reads 2048 b bytes further into the raw tile; its keys sit at positions key_pos(4 (g / 8)) + {0, 4, 16, 20}[b],
-    // i.e. b = 1 is 8 bytes after b = 0 in the same chunk and b = 2, 3 are chunk ^ 2 (offset tr_wr_hi).
+    // 8 bytes of one V^T row, stored with one 64-bit write.  The 64 blocks of a tile are shared out over the
+    // workgroup's 16-lane groups: group g takes blocks g + GROUPS b (keys 4 ((g + GROUPS b) / 8) .. + 3, channels
+    // 16 (g % 8) .. + 15); consecutive blocks of a group lie (GROUPS / 8) x 1 KiB apart in the raw tile.
+    constexpr int GROUPS = THREADS / 16;
+    constexpr int TR_BLOCKS = 64 / GROUPS;
     const int grp = tid >> 4, gl = tid & 15;
-    const int kgb0 = grp >> 3, cgb = grp & 7;
+    const int cgb = grp & 7;
     const int tr_ch = 16 * cgb + 4 * (gl & 3);   // first channel of the 8 bytes this lane supplies
-    const int tr_rd = vr_off(4 * kgb0 + (gl >> 2), tr_ch >> 3) + (tr_ch & 7) * 2;
-    const int tr_pos = key_pos(4 * kgb0);         // 0 or 8
-    const int tr_wr_lo = vt_off(16 * cgb + gl, tr_pos >> 3) + (tr_pos & 7) * 2;
-    const int tr_wr_hi = vt_off(16 * cgb + gl, (tr_pos >> 3) + 2) + (tr_pos & 7) * 2;
+    const int tr_rd = vr_off(4 * (grp >> 3) + (gl >> 2), tr_ch >> 3) + (tr_ch & 7) * 2;
+    int tr_wr[TR_BLOCKS];
+#pragma unroll
+    for (int b = 0; b < TR_BLOCKS; ++b) {
+        const int pos = key_pos(4 * ((grp + GROUPS * b) >> 3));   // the block's 4 keys sit at 4 consecutive positions
+        tr_wr[b] = vt_off(16 * cgb + gl, pos >> 3) + (pos & 7) * 2;
+    }
 
     auto vslot = [&](int t) { return vtb + (t & 1) * V_TILE_BYTES; };
-    auto issue_k = [&](auto S, int t) {   // S = t % 3
-        unsigned char* slot = pick3<decltype(S)::value>(kr0, kr1, kr2);
-        // The tile offset goes into the VGPR offset: the SGPR offset is not part of the buffer range check.
-        const unsigned ko = kd_voff + (unsigned)t * (BN * 128u);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk1, (lds_void*)(slot + 1024 * wave), 16, (int)ko, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk2, (lds_void*)(slot + K_TILE_BYTES + 1024 * wave), 16, (int)ko, 0, 0,
-                                                 0);
-    };
-    auto issue_v = [&](auto S, int t) {   // S = t % 3
-        unsigned char* slot = pick3<decltype(S)::value>(vr0, vr1, vr2);
+    auto issue_k = [&](auto S, int t) {   // S = t % 4
+        unsigned char* slot = pick4<decltype(S)::value>(kr0, kr1, kr2, kr3);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(slot + 1024 * (wave + 4 * j)), 16,
+        for (int j = 0; j < K_PIECES_PER_WAVE; ++j) {
+            // The tile offset goes into the VGPR offset: the SGPR offset is not part of the buffer range check.
+            const unsigned ko = kd_voff[j] + (unsigned)t * (BN * 128u);
+            if ((wave + WAVES * j) < 4)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk1, (lds_void*)(slot + kd_lds[j]), 16, (int)ko, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk2, (lds_void*)(slot + kd_lds[j]), 16, (int)ko, 0, 0, 0);
+        }
+    };
+    auto issue_v = [&](auto S, int t) {   // S = t % 4
+        unsigned char* slot = pick4<decltype(S)::value>(vr0, vr1, vr2, vr3);
+#pragma unroll
+        for (int j = 0; j < V_PIECES_PER_WAVE; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(slot + 1024 * (wave + WAVES * j)), 16,
                                                      (int)(vd_voff[j] + (unsigned)t * (BN * 256u)), 0, 0, 0);
     };
-    auto transpose_v = [&](auto S, int t) {   // S = t % 3
-        const unsigned char* raw = pick3<decltype(S)::value>(vr0, vr1, vr2);
+    auto transpose_v = [&](auto S, int t) {   // S = t % 4
+        const unsigned char* raw = pick4<decltype(S)::value>(vr0, vr1, vr2, vr3);
         unsigned char* vt = vslot(t);
-        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(raw + tr_rd));
-        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(raw + tr_rd + 2048));
-        const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(raw + tr_rd + 4096));
-        const s16x4 x3 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(raw + tr_rd + 6144));
-        *(s16x4*)(vt + tr_wr_lo) = x0;
-        *(s16x4*)(vt + tr_wr_lo + 8) = x1;
-        *(s16x4*)(vt + tr_wr_hi) = x2;
-        *(s16x4*)(vt + tr_wr_hi + 8) = x3;
+        s16x4 x[TR_BLOCKS];
+#pragma unroll
+        for (int b = 0; b < TR_BLOCKS; ++b)
+            x[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(raw + tr_rd + (GROUPS / 8) * 1024 * b));
+#pragma unroll
+        for (int b = 0; b < TR_BLOCKS; ++b) *(s16x4*)(vt + tr_wr[b]) = x[b];
     };
 
     // Per-lane read offsets: K A-operand (row l32, chunk 2 kc + h) and V^T A-operand (channel 32 cb + l32,
@@ -284,20 +304,22 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     issue_v(Slot<0>{}, 0);
     issue_k(Slot<1>{}, 1);
     issue_v(Slot<1>{}, 1);
+    issue_k(Slot<2>{}, 2);
     issue_v(Slot<2>{}, 2);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2));   // K(0), V(0), K(1), V(1) landed; V(2) may be in flight
+    issue_v(Slot<3>{}, 3);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     lds_barrier();
     transpose_v(Slot<0>{}, 0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     lds_barrier();
-    auto step = [&](auto S, int t) {   // S = t % 3
+    auto step = [&](auto S, int t) {   // S = t % 4
         constexpr int s0 = decltype(S)::value;
-        issue_k(Slot<(s0 + 2) % 3>{}, t + 2);
-        issue_v(Slot<s0>{}, t + 3);
-        transpose_v(Slot<(s0 + 1) % 3>{}, t + 1);
+        issue_k(Slot<(s0 + 3) % 4>{}, t + 3);
+        issue_v(Slot<s0>{}, t + 4);
+        transpose_v(Slot<(s0 + 1) % 4>{}, t + 1);
         const int kv0 = t * BN;
         if (!causal || kv0 <= q0w + 31) {
-            const unsigned char* kb_ = pick3<s0>(kr0, kr1, kr2);
+            const unsigned char* kb_ = pick4<s0>(kr0, kr1, kr2, kr3);
             const unsigned char* vb_ = vslot(t);
             f32x16 s1, s2;
 #pragma unroll
@@ -340,15 +362,17 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o2[cb] = mfma(va[cb][1], p2[1], o2[cb]);
         }
-        // K(t + 2) and V(t + 3) (2 + 2 operations per thread) may stay in flight past the barrier; everything older,
-        // in particular K(t + 1) and V(t + 2), has landed, and the transposed V(t + 1) is written.
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4));
+        // The loads of this iteration and the previous one (K(t + 2), V(t + 3), K(t + 3), V(t + 4)) may stay in
+        // flight past the barrier; everything older, in particular K(t + 1) and V(t + 2), has landed, and the
+        // transposed V(t + 1) is written.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * (K_PIECES_PER_WAVE + V_PIECES_PER_WAVE)));
         lds_barrier();
     };
-    for (int t = 0; t < n_tiles; t += 3) {
+    for (int t = 0; t < n_tiles; t += 4) {
         step(Slot<0>{}, t);
         if (t + 1 < n_tiles) step(Slot<1>{}, t + 1);
         if (t + 2 < n_tiles) step(Slot<2>{}, t + 2);
+        if (t + 3 < n_tiles) step(Slot<3>{}, t + 3);
     }
     // Drain the trailing prefetches before the workgroup can retire (their LDS writes must not outlive it).
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
