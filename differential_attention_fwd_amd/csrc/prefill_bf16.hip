@@ -108,14 +108,24 @@ __device__ __forceinline__ float max16(const f32x16& s) {
     return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[15]));
 }
 
-// Move the running max of one map if the tile's max exceeds it by more than the threshold (wave-uniform branch);
-// rescales that map's O accumulator and partial sum.
-__device__ __forceinline__ void update_max(const f32x16& s, float& m, float& l, f32x16 (&o)[4], float c) {
-    const float m_new = fmaxf(m, pair_max(max16(s)) * c);
-    if (__any(m_new > m + RESCALE_THRESHOLD)) {
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-        m = m_new;
-        l *= alpha;
+// Online-softmax state of one map for the lane's query row.  The running max is kept in score units (ms) and in
+// log2 units (ml = ms * c, the exponent offset); it only moves when a tile's max exceeds it by more than
+// RESCALE_THRESHOLD log2 units (mt = ms + RESCALE_THRESHOLD / c), a wave-uniform decision, so the rescale of O and l
+// is rare.
+struct MapState {
+    float ms, ml, mt, l;
+};
+
+__device__ __forceinline__ void update_max(const f32x16& s, MapState& st, f32x16 (&o)[4], float c, float thr) {
+    const float x = pair_max(max16(s));
+    if (__any(x > st.mt)) {
+        const float ms = fmaxf(st.ms, x);
+        const float ml = ms * c;
+        const float alpha = __builtin_amdgcn_exp2f(st.ml - ml);
+        st.ms = ms;
+        st.ml = ml;
+        st.mt = ms + thr;
+        st.l *= alpha;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -123,14 +133,11 @@ __device__ __forceinline__ void update_max(const f32x16& s, float& m, float& l, 
     }
 }
 
-// p = exp2(s * c - m) for the lane's 16 keys; adds them to l and packs P^T as two bf16x8 B operands.
-__device__ __forceinline__ void exp_pack(const f32x16& s, float m, float& l, float c, bf16x8& lo, bf16x8& hi) {
+// p = exp2(s * c - ml) for the lane's 16 keys, packed as P^T: two bf16x8 B operands.
+__device__ __forceinline__ void exp_pack(const f32x16& s, float ml, float c, bf16x8& lo, bf16x8& hi) {
     float p[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m));
-    float t0 = (p[0] + p[1]) + (p[2] + p[3]), t1 = (p[4] + p[5]) + (p[6] + p[7]);
-    float t2 = (p[8] + p[9]) + (p[10] + p[11]), t3 = (p[12] + p[13]) + (p[14] + p[15]);
-    l += (t0 + t1) + (t2 + t3);
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -ml));
     u32x4 a, b;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -139,6 +146,21 @@ __device__ __forceinline__ void exp_pack(const f32x16& s, float m, float& l, flo
     }
     lo = __builtin_bit_cast(bf16x8, a);
     hi = __builtin_bit_cast(bf16x8, b);
+}
+
+// Adds the lane's 16 packed probabilities to l: pairwise bf16 dot products with (1, 1), so the sum is of the same
+// bf16-rounded values that multiply V.
+__device__ __forceinline__ float sum_packed(const bf16x8& lo, const bf16x8& hi, float l) {
+    const u32x4 a = __builtin_bit_cast(u32x4, lo), b = __builtin_bit_cast(u32x4, hi);
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const unsigned ak = a[k], bk = b[k];   // scalar copies: bit_cast of a vector element misreads it
+        t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ak), one, t0, false);
+        t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, bk), one, t1, false);
+    }
+    return l + (t0 + t1);
 }
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -270,15 +292,19 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(slot + 1024 * (wave + WAVES * j)), 16,
                                                      (int)(vd_voff[j] + (unsigned)t * (BN * 256u)), 0, 0, 0);
     };
-    auto transpose_v = [&](auto S, int t) {   // S = t % 4
+    // Transposition of raw V slot S into the V^T buffer of tile t, in two steps (read, then write) so that the
+    // tile's computation hides the latency of the transposing reads.
+    s16x4 trx[TR_BLOCKS];
+    auto transpose_read = [&](auto S) {
         const unsigned char* raw = pick4<decltype(S)::value>(vr0, vr1, vr2, vr3);
-        unsigned char* vt = vslot(t);
-        s16x4 x[TR_BLOCKS];
 #pragma unroll
         for (int b = 0; b < TR_BLOCKS; ++b)
-            x[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(raw + tr_rd + (GROUPS / 8) * 1024 * b));
+            trx[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(raw + tr_rd + (GROUPS / 8) * 1024 * b));
+    };
+    auto transpose_write = [&](int t) {
+        unsigned char* vt = vslot(t);
 #pragma unroll
-        for (int b = 0; b < TR_BLOCKS; ++b) *(s16x4*)(vt + tr_wr[b]) = x[b];
+        for (int b = 0; b < TR_BLOCKS; ++b) *(s16x4*)(vt + tr_wr[b]) = trx[b];
     };
 
     // Per-lane read offsets: K A-operand (row l32, chunk 2 kc + h) and V^T A-operand (channel 32 cb + l32,
@@ -293,8 +319,9 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) { o1[cb][i] = 0.f; o2[cb][i] = 0.f; }
-    float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
     const float c = LOG2E * 0.125f;  // log2(e) / sqrt(64)
+    const float thr = RESCALE_THRESHOLD / c;
+    MapState st1 = {-INFINITY, -INFINITY, -INFINITY, 0.f}, st2 = st1;
 
     // Load schedule.  Iteration t (between two workgroup barriers) issues the direct loads of K(t + 2) and raw
     // V(t + 3), transposes raw V(t + 1) into the V^T buffer of tile t + 1, and computes tile t.  At its end it waits
@@ -309,14 +336,15 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     issue_v(Slot<3>{}, 3);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     lds_barrier();
-    transpose_v(Slot<0>{}, 0);
+    transpose_read(Slot<0>{});
+    transpose_write(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     lds_barrier();
     auto step = [&](auto S, int t) {   // S = t % 4
         constexpr int s0 = decltype(S)::value;
         issue_k(Slot<(s0 + 3) % 4>{}, t + 3);
         issue_v(Slot<s0>{}, t + 4);
-        transpose_v(Slot<(s0 + 1) % 4>{}, t + 1);
+        transpose_read(Slot<(s0 + 1) % 4>{});
         const int kv0 = t * BN;
         if (!causal || kv0 <= q0w + 31) {
             const unsigned char* kb_ = pick4<s0>(kr0, kr1, kr2, kr3);
@@ -342,17 +370,17 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
                     s2[i] = vis ? s2[i] : -INFINITY;
                 }
             }
-            update_max(s1, m1, l1, o1, c);
-            update_max(s2, m2, l2, o2, c);
+            update_max(s1, st1, o1, c, thr);
+            update_max(s2, st2, o2, c, thr);
 
             bf16x8 p1[2], p2[2];
-            exp_pack(s1, m1, l1, c, p1[0], p1[1]);
+            exp_pack(s1, st1.ml, c, p1[0], p1[1]);
             bf16x8 va[4][2];
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) va[cb][0] = *(const bf16x8*)(vb_ + v_rd0 + 2048 * cb);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o1[cb] = mfma(va[cb][0], p1[0], o1[cb]);
-            exp_pack(s2, m2, l2, c, p2[0], p2[1]);
+            exp_pack(s2, st2.ml, c, p2[0], p2[1]);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) va[cb][1] = *(const bf16x8*)(vb_ + v_rd1 + 2048 * cb);
 #pragma unroll
@@ -361,7 +389,10 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
             for (int cb = 0; cb < 4; ++cb) o1[cb] = mfma(va[cb][1], p1[1], o1[cb]);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o2[cb] = mfma(va[cb][1], p2[1], o2[cb]);
+            st1.l = sum_packed(p1[0], p1[1], st1.l);
+            st2.l = sum_packed(p2[0], p2[1], st2.l);
         }
+        transpose_write(t + 1);
         // The loads of this iteration and the previous one (K(t + 2), V(t + 3), K(t + 3), V(t + 4)) may stay in
         // flight past the barrier; everything older, in particular K(t + 1) and V(t + 2), has landed, and the
         // transposed V(t + 1) is written.
@@ -378,8 +409,8 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
     // Epilogue: lane owns query row q0w + l32 and channels cb*32 + 8*(i/4) + 4h + i%4.
-    l1 = pair_sum(l1);
-    l2 = pair_sum(l2);
+    const float l1 = pair_sum(st1.l);
+    const float l2 = pair_sum(st2.l);
     const float inv1 = 1.f / l1;
     const float inv2 = ep.lambda / l2;
     float ss = 0.f;
