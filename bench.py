@@ -8,7 +8,7 @@ events recorded on the stream it is launched on.  Prints ONE JSON line.
   value     prefill TFLOP/s, counting 12*d FLOP per unmasked (query, key) pair (two Q.K^T products of width d and
             two P.V products of width 2d), i.e. B*H*N*(N+1)/2 pairs
   roofline  the prefill kernel against the bf16 dense MFMA peak; decode carries its own against HBM bandwidth
-  cpu_baseline  the double-precision CPU oracle on a bounded row sample of the same prefill workload
+  cpu_baseline  the double-precision CPU oracle on the same prefill workload (all rows by default)
 """
 from __future__ import annotations
 
@@ -97,9 +97,10 @@ def cpu_baseline(inp_bits, lam, layer, N, target_rows):
     oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam, layer, True, rows=rows, threads=threads)
     dt = time.perf_counter() - t0
     return {"value": round(pairs * 12 * 64 / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows.size} of {total} query rows (every {stride}th row, {pairs} unmasked pairs) of the "
-                      f"B4 H12 N4096 causal prefill, double precision, {dt:.2f} s on {threads} threads of "
-                      f"'{cpu_model()}'",
+            "sample": (f"all {total} query rows" if stride == 1 else
+                       f"{rows.size} of {total} query rows (every {stride}th row)") +
+                      f" ({pairs} unmasked pairs) of the B4 H12 N4096 causal prefill, double precision, {dt:.2f} s on "
+                      f"{threads} threads of '{cpu_model()}'",
             "seconds": round(dt, 3)}
 
 
@@ -109,7 +110,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
-    ap.add_argument("--cpu-rows", type=int, default=65536, help="oracle row sample size for cpu_baseline")
+    ap.add_argument("--cpu-rows", type=int, default=4 * 12 * 4096,
+                    help="oracle row sample size for cpu_baseline (default: every row of the prefill workload)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()

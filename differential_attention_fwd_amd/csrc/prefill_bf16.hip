@@ -6,21 +6,26 @@
 // normalisation and the (1 - lambda_init) scale.
 //
 // Design (one pass over K1/K2/V, nothing N x N ever materialised):
-//   * A workgroup of 4 waves owns 128 query rows of one (batch, head); each wave owns 32 rows.  Key/value tiles of
-//     32 keys (K1 4 KiB, K2 4 KiB, V 8 KiB) are double-buffered through LDS.  K rows go straight from global
-//     memory to LDS (global_load_lds_dwordx4, no registers); V goes through registers and is stored TRANSPOSED
-//     (channel-major) so that every MFMA operand is fetched with 128-bit LDS reads.
+//   * A workgroup of 4 waves (one per SIMD) owns 128 query rows of one (batch, head); each wave owns 32 rows.  Two
+//     workgroups share a CU, so each SIMD runs two independent waves and the matrix cores of one overlap the
+//     softmax of the other.  Key tiles are 32 keys.
+//   * Loads go straight from global memory to LDS (buffer_load ... lds, no registers) through 4-slot rings: the
+//     K1 and K2 tiles three tiles ahead, the raw V tile four ahead.  Every step transposes the next raw V tile
+//     LDS-to-LDS (ds_read_b64_tr_b16, then 64-bit writes after the step's own work) into a channel-major V^T tile,
+//     double-buffered, so that every MFMA operand is one 128-bit LDS read.  Ring slots are separate __shared__
+//     arrays and the loop is unrolled by four, so the compiler can tell reads of one slot from loads still landing
+//     in another.  One workgroup barrier per tile.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held in
 //     registers).  In the accumulator layout every lane owns ONE query row (lane % 32) and 16 of the 32 keys, so
 //     row statistics need only the lane pair (l, l ^ 32), exchanged with v_permlane32_swap.
 //   * P^T stays in registers and feeds O^T = V^T P^T directly as the MFMA B operand.  The k-order of that product
 //     is the accumulator's key order; the transposed V tile stores keys in that order, so the A operand of each
-//     MFMA is one contiguous 16-byte read.  O^T's layout gives each lane one query row again, so the
-//     online-softmax rescale of O is lane-local.
+//     MFMA is one contiguous 16-byte read, shared by the two maps.  O^T's layout gives each lane one query row
+//     again, so the online-softmax rescale of O is lane-local.
 //   * Two online softmaxes run side by side (running max and sum per map, two O accumulators).  The running max
 //     only moves when a row's new maximum exceeds it by more than 2^8 (wave-uniform decision), so the O rescale
-//     is rare; exponents use exp2 with log2(e)/sqrt(d) folded into one FMA.  Map 2's exponentials are issued
-//     between map 1's value MFMAs so the VALU and the matrix cores of a wave overlap.
+//     is rare; exponents use exp2 with log2(e)/sqrt(d) folded into one FMA; row sums add the bf16-rounded
+//     probabilities pairwise with v_dot2_f32_bf16.  Map 2's exponentials are issued between map 1's value MFMAs.
 //   * Epilogue: O1/l1 - lambda O2/l2, RMS over the 128 channels (pair-reduced), scale, bf16 round-to-nearest-even.
 //   * Causal: row tiles are launched heaviest first; tiles wholly above a wave's rows are skipped by that wave,
 //     and only diagonal or ragged-tail tiles pay for masking.
