@@ -18,8 +18,8 @@ DIFFATTN_F32 = 1
 STATUS = {0: "DIFFATTN_OK", -1: "DIFFATTN_ERR_NULL", -2: "DIFFATTN_ERR_SHAPE", -3: "DIFFATTN_ERR_UNSUPPORTED",
           -4: "DIFFATTN_ERR_ALIGN", -5: "DIFFATTN_ERR_LAYER", -6: "DIFFATTN_ERR_LAMBDA",
           -7: "DIFFATTN_ERR_WORKSPACE", -8: "DIFFATTN_ERR_ALIAS", -9: "DIFFATTN_ERR_HIP"}
-EXPORTS = ["diffattn_fwd", "diffattn_decode", "diffattn_decode_workspace_bytes", "diffattn_lambda_init",
-           "diffattn_status_str", "diffattn_abi_version"]
+EXPORTS = ["diffattn_fwd", "diffattn_fwd_heads", "diffattn_decode", "diffattn_decode_heads",
+           "diffattn_decode_workspace_bytes", "diffattn_lambda_init", "diffattn_status_str", "diffattn_abi_version"]
 
 _lib = None
 
@@ -44,6 +44,11 @@ def lib() -> ctypes.CDLL:
     L.diffattn_decode.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, c_int, c_int, P,
                                   ctypes.c_size_t, P]
     L.diffattn_decode.restype = c_int
+    L.diffattn_fwd_heads.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, P, c_int, c_int, P]
+    L.diffattn_fwd_heads.restype = c_int
+    L.diffattn_decode_heads.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, P, c_int, c_int, P,
+                                        ctypes.c_size_t, P]
+    L.diffattn_decode_heads.restype = c_int
     L.diffattn_decode_workspace_bytes.argtypes = [i64, i64, i64, c_int]
     L.diffattn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.diffattn_lambda_init.argtypes = [c_int]
@@ -98,8 +103,20 @@ def _check_tensors(ts):
             raise ValueError("all tensors must be contiguous")
 
 
-def diffattn_fwd(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool, out=None, stream=None):
-    """Prefill: q1,k1,q2,k2 [B][H][N][d], v [B][H][N][2d] -> out [B][H][N][2d] (same dtype), on `stream`."""
+def _lambda_heads(lam, H, device):
+    """A per-head lambda tensor (H fp32 values on the GPU), or None when lam is a number."""
+    import torch
+    if not isinstance(lam, torch.Tensor):
+        return None
+    if lam.dtype != torch.float32 or lam.device != device or tuple(lam.shape) != (H,) or not lam.is_contiguous():
+        raise ValueError(f"per-head lambda must be a contiguous float32 tensor of shape ({H},) on {device}")
+    return lam
+
+
+def diffattn_fwd(q1, k1, q2, k2, v, lam, layer: int, causal: bool, out=None, stream=None):
+    """Prefill: q1,k1,q2,k2 [B][H][N][d], v [B][H][N][2d] -> out [B][H][N][2d] (same dtype), on `stream`.
+
+    lam: a number, or a float32 GPU tensor of shape (H,) holding one lambda per head (diffattn_fwd_heads)."""
     import torch
     _check_tensors((q1, k1, q2, k2, v))
     B, H, N, d = q1.shape
@@ -109,17 +126,24 @@ def diffattn_fwd(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool, out=No
     for t, shp in ((k1, q1.shape), (q2, q1.shape), (k2, q1.shape), (v, (B, H, N, 2 * d)), (out, (B, H, N, 2 * d))):
         if tuple(t.shape) != tuple(shp) or t.dtype != q1.dtype:
             raise ValueError(f"shape/dtype mismatch: {tuple(t.shape)} {t.dtype}, expected {tuple(shp)} {q1.dtype}")
-    st = lib().diffattn_fwd(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
-                            out.data_ptr(), B, H, N, d, _dtype_code(q1), float(lam), int(layer), int(bool(causal)),
-                            _stream_handle(stream, q1.device))
+    lh = _lambda_heads(lam, H, q1.device)
+    args = (q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
+            _dtype_code(q1))
+    tail = (int(layer), int(bool(causal)), _stream_handle(stream, q1.device))
+    if lh is None:
+        st, name = lib().diffattn_fwd(*args, float(lam), *tail), "diffattn_fwd"
+    else:
+        st, name = lib().diffattn_fwd_heads(*args, lh.data_ptr(), *tail), "diffattn_fwd_heads"
     if st != 0:
-        raise DiffAttnError(st, "diffattn_fwd")
+        raise DiffAttnError(st, name)
     return out
 
 
-def diffattn_decode(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool = True, out=None, workspace=None,
+def diffattn_decode(q1, k1, q2, k2, v, lam, layer: int, causal: bool = True, out=None, workspace=None,
                     stream=None):
-    """Decode: q1,q2 [B][H][d]; k1,k2 [B][H][L][d]; v [B][H][L][2d] -> out [B][H][2d], on `stream`."""
+    """Decode: q1,q2 [B][H][d]; k1,k2 [B][H][L][d]; v [B][H][L][2d] -> out [B][H][2d], on `stream`.
+
+    lam: a number, or a float32 GPU tensor of shape (H,) holding one lambda per head (diffattn_decode_heads)."""
     import torch
     _check_tensors((q1, k1, q2, k2, v))
     B, H, d = q1.shape
@@ -135,9 +159,14 @@ def diffattn_decode(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool = Tr
         workspace = torch.empty(need, dtype=torch.uint8, device=q1.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().diffattn_decode(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
-                               out.data_ptr(), B, H, L, d, _dtype_code(q1), float(lam), int(layer),
-                               int(bool(causal)), ws_ptr, ws_bytes, _stream_handle(stream, q1.device))
+    lh = _lambda_heads(lam, H, q1.device)
+    args = (q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, d,
+            _dtype_code(q1))
+    tail = (int(layer), int(bool(causal)), ws_ptr, ws_bytes, _stream_handle(stream, q1.device))
+    if lh is None:
+        st, name = lib().diffattn_decode(*args, float(lam), *tail), "diffattn_decode"
+    else:
+        st, name = lib().diffattn_decode_heads(*args, lh.data_ptr(), *tail), "diffattn_decode_heads"
     if st != 0:
-        raise DiffAttnError(st, "diffattn_decode")
+        raise DiffAttnError(st, name)
     return out

@@ -55,6 +55,7 @@ __global__ __launch_bounds__(THREADS) void attn_f32_kernel(const float* __restri
     const float* kb = k2 + bh * Nk * d;
     const float* vv = v + bh * Nk * dv;
     const float root_d = sqrtf((float)d);
+    const float lam = lambda_of(ep, (int)bh);
 
     float mx1 = -INFINITY, mx2 = -INFINITY;
     for (int64_t j = tid; j < nvis; j += THREADS) {
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(THREADS) void attn_f32_kernel(const float* __restri
         if (j < nvis) {
             const float a = expf(dotf(qa, ka + j * d, d) / root_d - m1) / s1;
             const float b = expf(dotf(qb, kb + j * d, d) / root_d - m2) / s2;
-            w[tid] = a - ep.lambda * b;
+            w[tid] = a - lam * b;
         }
         __syncthreads();
         if (tid < dv) {

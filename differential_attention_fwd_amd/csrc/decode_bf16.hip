@@ -211,7 +211,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
         o2a += w2 * p[4 + DV + 2 * lane];
         o2b += w2 * p[4 + DV + 2 * lane + 1];
     }
-    const float inv1 = 1.f / L1, inv2 = ep.lambda / L2;
+    const float inv1 = 1.f / L1, inv2 = lambda_of(ep, bh) / L2;
     float ya = o1a * inv1 - o2a * inv2;
     float yb = o1b * inv1 - o2b * inv2;
     if (ep.normalise) {

@@ -43,6 +43,17 @@ int make_epilogue(float lambda, int layer, Epilogue* ep) {
     ep->lambda = lambda;
     ep->normalise = layer >= 1 ? 1 : 0;
     ep->out_scale = layer >= 1 ? (float)(1.0 - diffattn_lambda_init(layer)) : 1.0f;
+    ep->lambda_heads = nullptr;
+    ep->heads = 1;
+    return DIFFATTN_OK;
+}
+
+// Per-head lambda: a device array of H floats, 4-byte aligned, that the call must not write.
+int check_lambda_heads(const float* lambda_heads, int64_t H, Span out) {
+    if (!lambda_heads) return DIFFATTN_ERR_NULL;
+    if (((uintptr_t)lambda_heads & 3u) != 0) return DIFFATTN_ERR_ALIGN;
+    const Span l{(uintptr_t)lambda_heads, (uintptr_t)lambda_heads + (size_t)H * sizeof(float)};
+    if (overlaps(l, out)) return DIFFATTN_ERR_ALIAS;
     return DIFFATTN_OK;
 }
 
@@ -75,13 +86,18 @@ const char* diffattn_status_str(int status) {
 
 int diffattn_abi_version(void) { return ABI_VERSION; }
 
-int diffattn_fwd(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out, int64_t B,
-                 int64_t H, int64_t N, int d, int dtype, float lambda, int layer, int causal, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out, int64_t B,
+             int64_t H, int64_t N, int d, int dtype, float lambda, const float* lambda_heads, bool per_head, int layer,
+             int causal, void* stream) {
     if (B < 0 || H < 0 || N < 0) return DIFFATTN_ERR_SHAPE;
     int st = check_dtype_d(dtype, d);
     if (st) return st;
     Epilogue ep;
-    st = make_epilogue(lambda, layer, &ep);
+    st = make_epilogue(per_head ? 0.0f : lambda, layer, &ep);
     if (st) return st;
     if (N > DIFFATTN_MAX_LEN) return DIFFATTN_ERR_SHAPE;
     int64_t BH, rows, qk_elems, v_elems;
@@ -100,6 +116,12 @@ int diffattn_fwd(const void* q1, const void* k1, const void* q2, const void* k2,
                          {(uintptr_t)v, (uintptr_t)v + v_bytes}};
     for (const Span& s : ins)
         if (overlaps(o, s)) return DIFFATTN_ERR_ALIAS;
+    if (per_head) {
+        st = check_lambda_heads(lambda_heads, H, o);
+        if (st) return st;
+        ep.lambda_heads = lambda_heads;
+        ep.heads = (int)H;
+    }
 
     hipStream_t s = (hipStream_t)stream;
     if (dtype == DIFFATTN_BF16)
@@ -110,6 +132,21 @@ int diffattn_fwd(const void* q1, const void* k1, const void* q2, const void* k2,
                                                 (const float*)v, (float*)out, BH, N, N, d, causal, ep, s));
 }
 
+}  // namespace
+
+extern "C" {
+
+int diffattn_fwd(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out, int64_t B,
+                 int64_t H, int64_t N, int d, int dtype, float lambda, int layer, int causal, void* stream) {
+    return fwd_impl(q1, k1, q2, k2, v, out, B, H, N, d, dtype, lambda, nullptr, false, layer, causal, stream);
+}
+
+int diffattn_fwd_heads(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
+                       int64_t B, int64_t H, int64_t N, int d, int dtype, const float* lambda_heads, int layer,
+                       int causal, void* stream) {
+    return fwd_impl(q1, k1, q2, k2, v, out, B, H, N, d, dtype, 0.0f, lambda_heads, true, layer, causal, stream);
+}
+
 size_t diffattn_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
     int64_t BH;
     if (B < 0 || H < 0 || L <= 0 || L > DIFFATTN_MAX_LEN || d != 64 || !mul_ok(B, H, &BH) || BH > INT32_MAX)
@@ -117,16 +154,19 @@ size_t diffattn_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
     return diffattn::decode_bf16_workspace_bytes(BH, L);
 }
 
-int diffattn_decode(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
-                    int64_t B, int64_t H, int64_t L, int d, int dtype, float lambda, int layer, int causal,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-    (void)causal;  // the single query is the last position: every cached key is visible either way
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out, int64_t B,
+                int64_t H, int64_t L, int d, int dtype, float lambda, const float* lambda_heads, bool per_head,
+                int layer, void* workspace, size_t workspace_bytes, void* stream) {
     if (B < 0 || H < 0 || L < 0) return DIFFATTN_ERR_SHAPE;
     if (L == 0 || L > DIFFATTN_MAX_LEN) return DIFFATTN_ERR_SHAPE;
     int st = check_dtype_d(dtype, d);
     if (st) return st;
     Epilogue ep;
-    st = make_epilogue(lambda, layer, &ep);
+    st = make_epilogue(per_head ? 0.0f : lambda, layer, &ep);
     if (st) return st;
     int64_t BH, q_elems, kv_rows, k_elems, v_elems;
     if (!mul_ok(B, H, &BH) || BH > INT32_MAX || !mul_ok(BH, d, &q_elems) || !mul_ok(BH, L, &kv_rows) ||
@@ -145,6 +185,12 @@ int diffattn_decode(const void* q1, const void* k1, const void* q2, const void* 
                          {(uintptr_t)v, (uintptr_t)v + (size_t)v_elems * eb}};
     for (const Span& s : ins)
         if (overlaps(o, s)) return DIFFATTN_ERR_ALIAS;
+    if (per_head) {
+        st = check_lambda_heads(lambda_heads, H, o);
+        if (st) return st;
+        ep.lambda_heads = lambda_heads;
+        ep.heads = (int)H;
+    }
 
     hipStream_t s = (hipStream_t)stream;
     if (dtype == DIFFATTN_F32)  // exact fp32 path: one query row per head at the end of the cache
@@ -159,9 +205,31 @@ int diffattn_decode(const void* q1, const void* k1, const void* q2, const void* 
     if (overlaps(w, o)) return DIFFATTN_ERR_ALIAS;
     for (const Span& sp : ins)
         if (overlaps(w, sp)) return DIFFATTN_ERR_ALIAS;
+    if (per_head && overlaps(w, Span{(uintptr_t)lambda_heads, (uintptr_t)lambda_heads + (size_t)H * sizeof(float)}))
+        return DIFFATTN_ERR_ALIAS;
     return hip_status(diffattn::launch_decode_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
                                                        (const uint16_t*)k2, (const uint16_t*)v, (uint16_t*)out, BH, L,
                                                        ep, workspace, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int diffattn_decode(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
+                    int64_t B, int64_t H, int64_t L, int d, int dtype, float lambda, int layer, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    (void)causal;  // the single query is the last position: every cached key is visible either way
+    return decode_impl(q1, k1, q2, k2, v, out, B, H, L, d, dtype, lambda, nullptr, false, layer, workspace,
+                       workspace_bytes, stream);
+}
+
+int diffattn_decode_heads(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
+                          int64_t B, int64_t H, int64_t L, int d, int dtype, const float* lambda_heads, int layer,
+                          int causal, void* workspace, size_t workspace_bytes, void* stream) {
+    (void)causal;
+    return decode_impl(q1, k1, q2, k2, v, out, B, H, L, d, dtype, 0.0f, lambda_heads, true, layer, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -9,10 +9,17 @@ namespace diffattn {
 
 // Per-call epilogue parameters: raw output (layer 0) or RMS-normalised and scaled by (1 - lambda_init).
 struct Epilogue {
-    float lambda;      // weight of the second softmax map
-    int normalise;     // 0: raw (map1 - lambda map2) V; 1: RMS norm (eps 1e-5, no affine) then * out_scale
-    float out_scale;   // 1 - lambda_init(layer) when normalise
+    float lambda;                // weight of the second softmax map (when lambda_heads is null)
+    int normalise;               // 0: raw (map1 - lambda map2) V; 1: RMS norm (eps 1e-5, no affine) then * out_scale
+    float out_scale;             // 1 - lambda_init(layer) when normalise
+    const float* lambda_heads;   // optional device array: lambda of head h is lambda_heads[h] (overrides lambda)
+    int heads;                   // H, to find a (batch, head) unit's head: h = bh % heads
 };
+
+// The lambda of (batch, head) unit bh.
+__device__ __forceinline__ float lambda_of(const Epilogue& ep, int bh) {
+    return ep.lambda_heads ? ep.lambda_heads[bh % ep.heads] : ep.lambda;
+}
 
 // bf16 prefill, d = 64, 2d = 128: fused one-pass kernel (two online softmaxes, two MFMA accumulators).
 hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,

@@ -63,6 +63,7 @@ constexpr int K_SLOT_BYTES = 2 * K_TILE_BYTES;
 // slot from a direct load still landing in another and does not drain the prefetches before every LDS read.
 template <int V> struct Slot { static constexpr int value = V; };
 template <int S, class T> __device__ __forceinline__ T* pick4(T* a, T* b, T* c, T* d) {
+    static_assert(RING == 4, "one array per ring slot");
     if constexpr (S % 4 == 0) return a;
     else if constexpr (S % 4 == 1) return b;
     else if constexpr (S % 4 == 2) return c;
@@ -417,7 +418,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     const float l1 = pair_sum(st1.l);
     const float l2 = pair_sum(st2.l);
     const float inv1 = 1.f / l1;
-    const float inv2 = ep.lambda / l2;
+    const float inv2 = lambda_of(ep, bh) / l2;
     float ss = 0.f;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)

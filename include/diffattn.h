@@ -27,7 +27,8 @@
  *         decode:  q1, q2 [B][H][d];  k1, k2 [B][H][L][d];  v [B][H][L][2d];  out [B][H][2d]
  *   - Element type `dtype`: DIFFATTN_BF16 (inputs and output bf16, fp32 accumulation) or DIFFATTN_F32 (fp32
  *     throughout).  Supported: bf16 with d = 64; fp32 with d = 8 or 64.  Anything else -> DIFFATTN_ERR_UNSUPPORTED.
- *   - Every pointer must be 16-byte aligned.  `out` (and the decode workspace) must not overlap any input.
+ *   - Every tensor pointer must be 16-byte aligned (the per-head lambda array: 4-byte).  `out` (and the decode
+ *     workspace) must not overlap any input.
  *   - Arguments are validated before any HIP call; on error nothing is launched and the status says why.
  *     Nothing is printed and nothing is thrown across the ABI.
  *   - Thread safety: no mutable global state; concurrent calls on different streams are independent.
@@ -86,6 +87,26 @@ size_t diffattn_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int d);
 int diffattn_decode(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
                     int64_t B, int64_t H, int64_t L, int d, int dtype, float lambda, int layer, int causal,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Per-head lambda variants.  The weight lambda of the second softmax map is learned per layer and may differ per
+ * head ([U], the paragraph after the worked example: lambda is a learnable scalar; [J] main features): these two
+ * entry points take it as an array instead of one float.  Every other argument, the layouts, the statuses and the
+ * stream semantics are those of diffattn_fwd and diffattn_decode.
+ *
+ *   lambda_heads  DEVICE pointer to H fp32 values, 4-byte aligned; head h of every batch entry uses lambda_heads[h].
+ *                 Read by the kernels on `stream`; the caller keeps it alive and unchanged until the call's work
+ *                 has finished, and it must not overlap `out` (or the decode workspace).  Its values are not
+ *                 inspected on the host: a non-finite entry yields non-finite outputs for that head.
+ *   Errors:       DIFFATTN_ERR_NULL if lambda_heads is NULL (and the call has work), DIFFATTN_ERR_ALIGN if it is
+ *                 not 4-byte aligned, DIFFATTN_ERR_ALIAS if it overlaps out or the workspace.
+ */
+int diffattn_fwd_heads(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
+                       int64_t B, int64_t H, int64_t N, int d, int dtype, const float *lambda_heads, int layer,
+                       int causal, void *stream);
+int diffattn_decode_heads(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
+                          int64_t B, int64_t H, int64_t L, int d, int dtype, const float *lambda_heads, int layer,
+                          int causal, void *workspace, size_t workspace_bytes, void *stream);
 
 /* lambda_init(layer) = 0.8 - 0.6 exp(-0.3 (layer - 1)) in double, for layer >= 1 ([U]); NaN for layer < 1. */
 double diffattn_lambda_init(int layer);

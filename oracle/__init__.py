@@ -74,11 +74,12 @@ def _f32(x) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(x), dtype=np.float32)
 
 
-def diffattn(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool, rows=None, want_diff: bool = False,
+def diffattn(q1, k1, q2, k2, v, lam, layer: int, causal: bool, rows=None, want_diff: bool = False,
              threads: int = 0, mutant: int = 0):
     """Evaluate the definition for selected query rows.
 
     q1, q2: [B][H][Nq][d]; k1, k2: [B][H][Nk][d]; v: [B][H][Nk][2d]  (float32 values; bf16 inputs widened).
+    lam: one float, or an array of H floats (one lambda per head).
     rows: None (all B*H*Nq rows, in [B][H][Nq] order) or indices into the flattened query rows.
     Returns out as float64 [nrows][2d] (reshaped to [B][H][Nq][2d] when rows is None), and with want_diff
     also the difference-map rows [nrows][Nk] (masked keys hold 0).
@@ -88,6 +89,11 @@ def diffattn(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool, rows=None,
     Nk = k1.shape[2]
     assert q2.shape == q1.shape and k1.shape == (B, H, Nk, d) and k2.shape == k1.shape
     assert v.shape == (B, H, Nk, 2 * d)
+    if np.ndim(lam) == 1:
+        # One lambda per head: the same definition, evaluated head by head with that head's lambda.
+        lam = np.asarray(lam, dtype=np.float64)
+        assert lam.shape == (H,)
+        return _per_head(q1, k1, q2, k2, v, lam, layer, causal, rows, want_diff, threads, mutant)
     if rows is None:
         rows_arr = None
         nrows = B * H * Nq
@@ -110,7 +116,32 @@ def diffattn(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool, rows=None,
     return (out, diff) if want_diff else out
 
 
-def decode(q1, k1, q2, k2, v, lam: float, layer: int, rows=None, threads: int = 0, mutant: int = 0):
+def _per_head(q1, k1, q2, k2, v, lam, layer, causal, rows, want_diff, threads, mutant):
+    B, H, Nq, d = q1.shape
+    Nk = k1.shape[2]
+    flat = np.arange(B * H * Nq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64).ravel()
+    out = np.zeros((flat.size, 2 * d), dtype=np.float64)
+    diff = np.zeros((flat.size, Nk), dtype=np.float64) if want_diff else None
+    b, h, i = flat // (H * Nq), (flat // Nq) % H, flat % Nq
+    for hh in range(H):
+        sel = np.nonzero(h == hh)[0]
+        if sel.size == 0:
+            continue
+        sl = (slice(None), slice(hh, hh + 1))
+        res = diffattn(q1[sl], k1[sl], q2[sl], k2[sl], v[sl], float(lam[hh]), layer, causal,
+                       rows=b[sel] * Nq + i[sel], want_diff=want_diff, threads=threads, mutant=mutant)
+        if want_diff:
+            out[sel], diff[sel] = res
+        else:
+            out[sel] = res
+    if rows is None:
+        out = out.reshape(B, H, Nq, 2 * d)
+        if diff is not None:
+            diff = diff.reshape(B, H, Nq, Nk)
+    return (out, diff) if want_diff else out
+
+
+def decode(q1, k1, q2, k2, v, lam, layer: int, rows=None, threads: int = 0, mutant: int = 0):
     """Single-token decode: q1, q2 [B][H][d] against caches k [B][H][L][d], v [B][H][L][2d]; out [B][H][2d]."""
     q1 = _f32(q1)
     q2 = _f32(q2)

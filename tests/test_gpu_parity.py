@@ -281,3 +281,69 @@ def test_decode_matches_prefill_last_row():
     dinp = {"q1": inp["q1"][:, :, -1], "q2": inp["q2"][:, :, -1], "k1": inp["k1"], "k2": inp["k2"], "v": inp["v"]}
     dec = run_decode_bf16(dinp, 0.8, 1)
     assert np.abs(pre - dec).max() <= 2e-2
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# One lambda per head (diffattn_fwd_heads / diffattn_decode_heads)
+# ---------------------------------------------------------------------------------------------------------------
+
+LAM_HEADS = np.array([0.05, 0.5, 0.95], dtype=np.float32)
+
+
+def dev_lam(lam):
+    return dev_f32(np.asarray(lam, dtype=np.float32))
+
+
+@pytest.mark.parametrize("N,causal,layer", [(300, True, 2), (129, False, 0)])
+def test_prefill_bf16_lambda_per_head(N, causal, layer):
+    torch = torch_mod()
+    inp = di.prefill_bf16(2, 3, N, 64, seed=400 + N)
+    say(f"case: prefill bf16 per-head lambda B2 H3 N{N} causal={causal} layer={layer}")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    out = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], dev_lam(LAM_HEADS), layer, causal)
+    torch.cuda.synchronize()
+    f = widen(inp)
+    ref = oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], LAM_HEADS.astype(np.float64), layer, causal)
+    check_bf16(host_bf16(out), ref, f"prefill per-head N{N}")
+
+
+def test_f32_lambda_per_head():
+    torch = torch_mod()
+    inp = di.prefill_f32(2, 3, 37, 8, seed=410)
+    say("case: fp32 per-head lambda B2 H3 N37 d8")
+    dev = {k: dev_f32(v) for k, v in inp.items()}
+    out = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], dev_lam(LAM_HEADS), 1, True)
+    torch.cuda.synchronize()
+    ref = oracle.diffattn(inp["q1"], inp["k1"], inp["q2"], inp["k2"], inp["v"], LAM_HEADS.astype(np.float64), 1, True)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - ref).max()
+    say(f"fp32 per-head: max-abs {err:.3e}")
+    assert err <= F32_TOL
+
+
+def test_decode_bf16_lambda_per_head():
+    torch = torch_mod()
+    inp = di.decode_bf16(2, 3, 1500, 64, seed=420)
+    say("case: decode bf16 per-head lambda B2 H3 L1500")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    out = da.diffattn_decode(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], dev_lam(LAM_HEADS), 1)
+    torch.cuda.synchronize()
+    f = widen(inp)
+    ref = oracle.decode(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], LAM_HEADS.astype(np.float64), 1)
+    check_bf16(host_bf16(out), ref, "decode per-head L1500")
+
+
+def test_uniform_lambda_heads_equal_scalar_lambda():
+    """A per-head array holding one value gives bit-identical output to the scalar entry point."""
+    torch = torch_mod()
+    inp = di.prefill_bf16(1, 3, 200, 64, seed=430)
+    say("case: uniform per-head lambda == scalar lambda (prefill N200, decode L200)")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    lam = float(np.float32(0.625))
+    a = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], lam, 3, True)
+    b = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], dev_lam([lam] * 3), 3, True)
+    q1, q2 = dev["q1"][:, :, -1].contiguous(), dev["q2"][:, :, -1].contiguous()
+    c = da.diffattn_decode(q1, dev["k1"], q2, dev["k2"], dev["v"], lam, 3)
+    e = da.diffattn_decode(q1, dev["k1"], q2, dev["k2"], dev["v"], dev_lam([lam] * 3), 3)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(c.view(torch.int16), e.view(torch.int16))
