@@ -57,6 +57,9 @@ def _load(mutant: int = 0):
     lib.oracle_diffattn.argtypes = [P, P, P, P, P, i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_int,
                                     ctypes.c_int, P, i64, P, P, ctypes.c_int]
     lib.oracle_diffattn.restype = ctypes.c_int
+    lib.oracle_diffattn_bwd.argtypes = [P, P, P, P, P, P, i64, i64, i64, i64, P, ctypes.c_int, ctypes.c_int,
+                                        P, P, P, P, P, P, ctypes.c_int]
+    lib.oracle_diffattn_bwd.restype = ctypes.c_int
     _libs[mutant] = lib
     return lib
 
@@ -139,6 +142,31 @@ def _per_head(q1, k1, q2, k2, v, lam, layer, causal, rows, want_diff, threads, m
         if diff is not None:
             diff = diff.reshape(B, H, Nq, Nk)
     return (out, diff) if want_diff else out
+
+
+def diffattn_bwd(q1, k1, q2, k2, v, dy, lam, layer: int, causal: bool, threads: int = 0, mutant: int = 0):
+    """Gradients of a loss with respect to the inputs of the square (Nq = Nk) forward, given dy = dLoss/dout.
+
+    q1, k1, q2, k2: [B][H][N][d]; v, dy: [B][H][N][2d] (float32 values).  lam: one float or H floats.
+    Returns a dict of float64 arrays: dq1, dk1, dq2, dk2 [B][H][N][d], dv [B][H][N][2d], dlambda [H] (summed over
+    the batch; for a scalar lambda shared by all heads its gradient is dlambda.sum()).
+    """
+    q1, k1, q2, k2, v, dy = (_f32(t) for t in (q1, k1, q2, k2, v, dy))
+    B, H, N, d = q1.shape
+    assert k1.shape == q1.shape and q2.shape == q1.shape and k2.shape == q1.shape
+    assert v.shape == (B, H, N, 2 * d) and dy.shape == v.shape
+    lh = np.ascontiguousarray(np.broadcast_to(np.asarray(lam, dtype=np.float64), (H,)))
+    g = {k: np.zeros((B, H, N, d), dtype=np.float64) for k in ("dq1", "dk1", "dq2", "dk2")}
+    g["dv"] = np.zeros((B, H, N, 2 * d), dtype=np.float64)
+    g["dlambda"] = np.zeros(H, dtype=np.float64)
+    rc = _load(mutant).oracle_diffattn_bwd(
+        q1.ctypes.data, k1.ctypes.data, q2.ctypes.data, k2.ctypes.data, v.ctypes.data, dy.ctypes.data,
+        B, H, N, d, lh.ctypes.data, int(layer), int(bool(causal)),
+        g["dq1"].ctypes.data, g["dk1"].ctypes.data, g["dq2"].ctypes.data, g["dk2"].ctypes.data, g["dv"].ctypes.data,
+        g["dlambda"].ctypes.data, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_diffattn_bwd rejected its arguments (rc={rc})")
+    return g
 
 
 def decode(q1, k1, q2, k2, v, lam, layer: int, rows=None, threads: int = 0, mutant: int = 0):
