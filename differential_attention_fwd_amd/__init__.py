@@ -19,7 +19,9 @@ STATUS = {0: "DIFFATTN_OK", -1: "DIFFATTN_ERR_NULL", -2: "DIFFATTN_ERR_SHAPE", -
           -4: "DIFFATTN_ERR_ALIGN", -5: "DIFFATTN_ERR_LAYER", -6: "DIFFATTN_ERR_LAMBDA",
           -7: "DIFFATTN_ERR_WORKSPACE", -8: "DIFFATTN_ERR_ALIAS", -9: "DIFFATTN_ERR_HIP"}
 EXPORTS = ["diffattn_fwd", "diffattn_fwd_heads", "diffattn_decode", "diffattn_decode_heads",
-           "diffattn_decode_workspace_bytes", "diffattn_lambda_init", "diffattn_status_str", "diffattn_abi_version"]
+           "diffattn_decode_workspace_bytes", "diffattn_train_saved_bytes", "diffattn_fwd_train",
+           "diffattn_bwd_workspace_bytes", "diffattn_bwd", "diffattn_lambda_init", "diffattn_status_str",
+           "diffattn_abi_version"]
 
 _lib = None
 
@@ -49,6 +51,16 @@ def lib() -> ctypes.CDLL:
     L.diffattn_decode_heads.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, P, c_int, c_int, P,
                                         ctypes.c_size_t, P]
     L.diffattn_decode_heads.restype = c_int
+    L.diffattn_train_saved_bytes.argtypes = [i64, i64, i64, c_int]
+    L.diffattn_train_saved_bytes.restype = ctypes.c_size_t
+    L.diffattn_bwd_workspace_bytes.argtypes = [i64, i64, i64, c_int]
+    L.diffattn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.diffattn_fwd_train.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, P, c_int, c_int, P,
+                                     ctypes.c_size_t, P]
+    L.diffattn_fwd_train.restype = c_int
+    L.diffattn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, P, c_int,
+                               c_int, P, ctypes.c_size_t, P]
+    L.diffattn_bwd.restype = c_int
     L.diffattn_decode_workspace_bytes.argtypes = [i64, i64, i64, c_int]
     L.diffattn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.diffattn_lambda_init.argtypes = [c_int]
@@ -170,3 +182,67 @@ def diffattn_decode(q1, k1, q2, k2, v, lam, layer: int, causal: bool = True, out
     if st != 0:
         raise DiffAttnError(st, name)
     return out
+
+
+def diffattn_train_saved_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().diffattn_train_saved_bytes(int(B), int(H), int(N), int(d)))
+
+
+def diffattn_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().diffattn_bwd_workspace_bytes(int(B), int(H), int(N), int(d)))
+
+
+def _lambda_args(lam, H, device):
+    lh = _lambda_heads(lam, H, device)
+    return (0.0, lh.data_ptr()) if lh is not None else (float(lam), None)
+
+
+def diffattn_fwd_train(q1, k1, q2, k2, v, lam, layer: int, causal: bool, out=None, saved=None, stream=None):
+    """Training forward (bf16, d = 64): returns (out, saved); `saved` feeds diffattn_bwd."""
+    import torch
+    _check_tensors((q1, k1, q2, k2, v))
+    B, H, N, d = q1.shape
+    if out is None:
+        out = torch.empty((B, H, N, 2 * d), dtype=q1.dtype, device=q1.device)
+    if saved is None:
+        saved = torch.empty(max(diffattn_train_saved_bytes(B, H, N, d), 16), dtype=torch.uint8, device=q1.device)
+    _check_tensors((out, saved))
+    for t, shp in ((k1, q1.shape), (q2, q1.shape), (k2, q1.shape), (v, (B, H, N, 2 * d)), (out, (B, H, N, 2 * d))):
+        if tuple(t.shape) != tuple(shp) or t.dtype != q1.dtype:
+            raise ValueError(f"shape/dtype mismatch: {tuple(t.shape)} {t.dtype}, expected {tuple(shp)} {q1.dtype}")
+    lam_f, lam_p = _lambda_args(lam, H, q1.device)
+    st = lib().diffattn_fwd_train(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
+                                  out.data_ptr(), B, H, N, d, _dtype_code(q1), lam_f, lam_p, int(layer),
+                                  int(bool(causal)), saved.data_ptr(), saved.numel() * saved.element_size(),
+                                  _stream_handle(stream, q1.device))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_fwd_train")
+    return out, saved
+
+
+def diffattn_bwd(q1, k1, q2, k2, v, dy, saved, lam, layer: int, causal: bool, grads=None, workspace=None,
+                 stream=None):
+    """Backward (bf16, d = 64): returns a dict dq1, dk1, dq2, dk2, dv (bf16, shapes of the inputs) and dlambda
+    (float32, one per head, summed over the batch)."""
+    import torch
+    _check_tensors((q1, k1, q2, k2, v, dy, saved))
+    B, H, N, d = q1.shape
+    if grads is None:
+        grads = {k: torch.empty_like(t) for k, t in (("dq1", q1), ("dk1", k1), ("dq2", q2), ("dk2", k2), ("dv", v))}
+        grads["dlambda"] = torch.empty(H, dtype=torch.float32, device=q1.device)
+    _check_tensors(tuple(grads.values()))
+    need = diffattn_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q1.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lam_f, lam_p = _lambda_args(lam, H, q1.device)
+    g = grads
+    st = lib().diffattn_bwd(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(), dy.data_ptr(),
+                            saved.data_ptr(), g["dq1"].data_ptr(), g["dk1"].data_ptr(), g["dq2"].data_ptr(),
+                            g["dk2"].data_ptr(), g["dv"].data_ptr(), g["dlambda"].data_ptr(), B, H, N, d,
+                            _dtype_code(q1), lam_f, lam_p, int(layer), int(bool(causal)), ws_ptr, ws_bytes,
+                            _stream_handle(stream, q1.device))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_bwd")
+    return grads

@@ -15,11 +15,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdiffattn.so")
-SOURCES = ["diffattn_api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "attn_f32.hip"]
+SOURCES = ["diffattn_api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "attn_f32.hip", "backward_bf16.hip"]
 # Per-source extra flags.  The prefill kernel never produces a NaN (see its header), and without NaN semantics
 # v_max3 needs no quieting of MFMA results.
 EXTRA = {"prefill_bf16.hip": ["-fno-honor-nans"]}
-HEADERS = ["launch.h"]
+HEADERS = ["launch.h", "tiles.h"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

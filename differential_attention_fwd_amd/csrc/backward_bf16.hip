@@ -1,0 +1,496 @@
+// Backward pass of differential attention for gfx950 (bf16 inputs and gradients, fp32 accumulation, d = 64,
+// 2d = 128).
+//
+// The forward it differentiates (Ultralytics glossary "Differential Transformer", section on how differential
+// attention works: worked example and the paragraph after it): per head and query row i, a = softmax(q1 K1^T /
+// sqrt(d)), b = softmax(q2 K2^T / sqrt(d)), o = (a - lambda b) V, then for layer >= 1 the RMS normalisation and
+// the (1 - lambda_init) scale.  The pages give no backward pass; these kernels apply the chain rule:
+//   dO  = g r dy - g r^3 o (dy . o) / 2d        (normalised layers; g = 1 - lambda_init, r = (mean o^2 + eps)^-1/2)
+//   E1  = dO . o1,  E2 = dO . o2                 (o1 = a V, o2 = b V, saved by the training forward)
+//   dp  = dO . v_j
+//   ds1 = a (dp - E1),   ds2 = -lambda b (dp - E2)
+//   dV  = sum_i (a - lambda b)_ij dO_i,   dQ1 = ds1 K1 / sqrt(d),   dK1 = ds1^T Q1 / sqrt(d)   (same for map 2)
+//   dlambda = -sum_i dO_i . o2_i                  (per head, summed over the batch)
+// with a and b recomputed from the scores and the per-row log-sum-exps saved by the forward.
+//
+// Kernels (all launched on one stream, in order):
+//   1. bwd_pre:      per row, dO (bf16) and (lse1, lse2, E1, E2), and the row's share of dlambda.
+//   2. bwd_dq:       per 128-row query block (4 waves x 32 rows), loop over key tiles up to the diagonal:
+//                    S^T = K Q^T and dP^T = V dO^T on MFMA, ds in registers, dQ^T += K^T ds^T with K^T tiles
+//                    transposed in LDS.  Same register plan as the forward (two waves per SIMD).
+//   3. bwd_dkdv:     per 128-key block (4 waves x 32 keys), loop over query tiles from the diagonal: S = Q K^T and
+//                    dP = dO V^T with the wave's K and V rows held in registers, then dV^T += dO^T W and
+//                    dK^T += Q^T ds from transposed Q and dO tiles.  Its 128 accumulator registers plus the score
+//                    tiles need one wave per SIMD (the accumulators live in AGPRs).
+//   4. bwd_dlambda:  per head, a fixed-order sum of the rows' dlambda shares (deterministic).
+// Tiles move global -> registers -> LDS (one tile ahead), are transposed in LDS with ds_read_b64_tr_b16, and
+// three workgroup barriers separate loading, transposing and computing.
+#include "launch.h"
+#include "tiles.h"
+
+namespace diffattn {
+namespace {
+
+constexpr int D = 64;
+constexpr int DV = 128;
+constexpr int TILE = 32;          // keys (dq) or queries (dkdv) per tile
+constexpr int WAVES = 4;
+constexpr int THREADS = 64 * WAVES;
+constexpr int BLOCK = TILE * WAVES;   // rows (dq) or keys (dkdv) per workgroup
+constexpr int STAT_FLOATS = 4;    // per row in the workspace: lse1, lse2, E1, E2
+
+// ---------------------------------------------------------------------------------------------------------------
+// Tile staging: a 32-row tile of width W (64 or 128 bf16) is read from global memory into registers (16 bytes per
+// chunk, rows at or beyond N read as zero), then written to LDS row-major with the forward's swizzles (k_off for
+// W = 64, vr_off for W = 128), then transposed into a [W][32] tile (vt_off, rows in key_pos order).
+// ---------------------------------------------------------------------------------------------------------------
+template <int W>
+__device__ __forceinline__ int row_off(int row, int chunk) {
+    if constexpr (W == 64) return k_off(row, chunk);
+    else return vr_off(row, chunk);
+}
+
+// Chunks of one tile per thread.
+template <int W> constexpr int chunks_per_thread() { return TILE * W * 2 / 16 / THREADS; }   // 1 (W=64), 2 (W=128)
+
+template <int W>
+__device__ __forceinline__ void load_tile(const uint16_t* head, int row0, int N, int tid, u32x4 (&r)[chunks_per_thread<W>()]) {
+    constexpr int CPR = W / 8;   // chunks per row
+#pragma unroll
+    for (int k = 0; k < chunks_per_thread<W>(); ++k) {
+        const int u = tid + THREADS * k;
+        const int row = u / CPR, chunk = u % CPR;
+        const int g = row0 + row;
+        r[k] = g < N ? *(const u32x4*)(head + (size_t)g * W + chunk * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int W>
+__device__ __forceinline__ void store_tile(unsigned char* lds, int tid, const u32x4 (&r)[chunks_per_thread<W>()]) {
+    constexpr int CPR = W / 8;
+#pragma unroll
+    for (int k = 0; k < chunks_per_thread<W>(); ++k) {
+        const int u = tid + THREADS * k;
+        *(u32x4*)(lds + row_off<W>(u / CPR, u % CPR)) = r[k];
+    }
+}
+
+// Row-major [32][W] tile -> [W][32] tile.  A 16-lane group transposes a block of 4 rows x 16 channels with one
+// ds_read_b64_tr_b16 (lane 4 jj + q supplies row jj, channels 4 q .. 4 q + 3; lane i receives channel i for the
+// 4 rows) and one 64-bit write.  Block b of group g: channel group (g + 16 b) % (W / 16), row block
+// (g + 16 b) / (W / 16).
+template <int W>
+__device__ __forceinline__ void transpose_tile(const unsigned char* src, unsigned char* dst, int tid) {
+    constexpr int CG = W / 16;
+    constexpr int PER = 8 * CG / 16;   // blocks per 16-lane group: 2 (W=64) or 4 (W=128)
+    const int grp = tid >> 4, gl = tid & 15;
+    s16x4 x[PER];
+#pragma unroll
+    for (int b = 0; b < PER; ++b) {
+        const int blk = grp + 16 * b, cg = blk % CG, kb = blk / CG;
+        const int row = 4 * kb + (gl >> 2), ch0 = 16 * cg + 4 * (gl & 3);
+        x[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + row_off<W>(row, ch0 >> 3) + (ch0 & 7) * 2));
+    }
+#pragma unroll
+    for (int b = 0; b < PER; ++b) {
+        const int blk = grp + 16 * b, cg = blk % CG, kb = blk / CG;
+        const int pos = key_pos(4 * kb);
+        *(s16x4*)(dst + vt_off(16 * cg + gl, pos >> 3) + (pos & 7) * 2) = x[b];
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+__device__ __forceinline__ unsigned pack_bf16_bits(float a, float b) { return pack2(a, b); }
+
+// ---------------------------------------------------------------------------------------------------------------
+// 1. Preprocess: one wave per row; lane holds channels 2 lane, 2 lane + 1.
+// ---------------------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(THREADS) void bwd_pre_kernel(const uint16_t* __restrict__ dy, const float* __restrict__ saved,
+                                                          uint16_t* __restrict__ dO, float* __restrict__ stats,
+                                                          float* __restrict__ dl_rows, int64_t rows, int N, Epilogue ep) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int bh = (int)(row / N);
+    const float lam = lambda_of(ep, bh);
+    const float* srow = saved + row * SAVED_FLOATS;
+    const unsigned dyb = *(const unsigned*)(dy + row * DV + 2 * lane);
+    const float dy0 = __uint_as_float(dyb << 16), dy1 = __uint_as_float(dyb & 0xffff0000u);
+    const f32x2 o1 = *(const f32x2*)(srow + SAVED_O1 + 2 * lane);
+    const f32x2 o2 = *(const f32x2*)(srow + SAVED_O2 + 2 * lane);
+    const float oc0 = o1[0] - lam * o2[0], oc1 = o1[1] - lam * o2[1];
+    float d0 = dy0, d1 = dy1;
+    if (ep.normalise) {
+        const float rr = srow[2];
+        const float dyo = wave_sum(dy0 * oc0 + dy1 * oc1);
+        const float g = ep.out_scale;
+        const float k = g * rr * rr * rr * dyo * (1.f / DV);
+        d0 = g * rr * dy0 - k * oc0;
+        d1 = g * rr * dy1 - k * oc1;
+    }
+    // dO is used in bf16 by the matrix products; E1 and E2 use the same rounded values.
+    const unsigned db = pack_bf16_bits(d0, d1);
+    *(unsigned*)(dO + row * DV + 2 * lane) = db;
+    const float r0 = __uint_as_float(db << 16), r1 = __uint_as_float(db & 0xffff0000u);
+    const float e1 = wave_sum(r0 * o1[0] + r1 * o1[1]);
+    const float e2 = wave_sum(r0 * o2[0] + r1 * o2[1]);
+    // dlambda is a sum over rows with much cancellation: it uses the unrounded dO.
+    const float dl = wave_sum(d0 * o2[0] + d1 * o2[1]);
+    if (lane == 0) {
+        *(f32x4*)(stats + row * STAT_FLOATS) = f32x4{srow[0], srow[1], e1, e2};
+        dl_rows[row] = -dl;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------------------------
+// 2. dQ: per 128-row query block; lane owns query row q0w + l32 (as in the forward).
+// ---------------------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1,
+                   const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
+                   const uint16_t* __restrict__ gv, const uint16_t* __restrict__ gdo,
+                   const float* __restrict__ stats, uint16_t* __restrict__ dq1, uint16_t* __restrict__ dq2,
+                   int BH, int N, int n_blocks, int causal, Epilogue ep) {
+    __shared__ __attribute__((aligned(16))) unsigned char k1s[TILE * D * 2], k2s[TILE * D * 2], vs[TILE * DV * 2];
+    __shared__ __attribute__((aligned(16))) unsigned char k1t[TILE * D * 2], k2t[TILE * D * 2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const int bid = blockIdx.x;
+    const int qb = causal ? (n_blocks - 1 - bid / BH) : bid / BH;   // heaviest query blocks first
+    const int bh = bid % BH;
+    const int q0 = qb * BLOCK, q0w = q0 + TILE * wave;
+    const size_t hqk = (size_t)bh * N * D, hv = (size_t)bh * N * DV;
+    const int q = q0w + l32, qc = min(q, N - 1);
+
+    bf16x8 qa[4], qbf[4], dob[8];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+        qa[kc] = *(const bf16x8*)(gq1 + hqk + (size_t)qc * D + 16 * kc + 8 * h);
+        qbf[kc] = *(const bf16x8*)(gq2 + hqk + (size_t)qc * D + 16 * kc + 8 * h);
+    }
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) dob[kc] = *(const bf16x8*)(gdo + hv + (size_t)qc * DV + 16 * kc + 8 * h);
+    const f32x4 st = *(const f32x4*)(stats + ((size_t)bh * N + qc) * STAT_FLOATS);
+    const float lse1 = st[0], lse2 = st[1], e1 = st[2], e2 = st[3];
+    const float c = LOG2E * 0.125f;
+
+    f32x16 acc1[2], acc2[2];   // dQ^T blocks: d = 32 mb + 8 (i / 4) + 4 h + i % 4, query = lane's row
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { acc1[mb][i] = 0.f; acc2[mb][i] = 0.f; }
+
+    const int q_last = min(N, q0 + BLOCK) - 1;
+    const int n_tiles = causal ? (q_last / TILE + 1) : (N + TILE - 1) / TILE;
+    const int t_last = causal ? min(n_tiles - 1, (q0w + TILE - 1) / TILE) : n_tiles - 1;
+    const int k_rd0 = k_off(l32, h);
+    const int t_rd0 = vt_off(l32, h), t_rd1 = vt_off(l32, 2 + h);
+
+    u32x4 rk1[1], rk2[1], rv[2];
+    load_tile<D>(gk1 + hqk, 0, N, tid, rk1);
+    load_tile<D>(gk2 + hqk, 0, N, tid, rk2);
+    load_tile<DV>(gv + hv, 0, N, tid, rv);
+    for (int t = 0; t < n_tiles; ++t) {
+        __syncthreads();
+        store_tile<D>(k1s, tid, rk1);
+        store_tile<D>(k2s, tid, rk2);
+        store_tile<DV>(vs, tid, rv);
+        __syncthreads();
+        transpose_tile<D>(k1s, k1t, tid);
+        transpose_tile<D>(k2s, k2t, tid);
+        if (t + 1 < n_tiles) {
+            load_tile<D>(gk1 + hqk, (t + 1) * TILE, N, tid, rk1);
+            load_tile<D>(gk2 + hqk, (t + 1) * TILE, N, tid, rk2);
+            load_tile<DV>(gv + hv, (t + 1) * TILE, N, tid, rv);
+        }
+        __syncthreads();
+        if (t > t_last) continue;
+        // S^T = K Q^T (both maps) and dP^T = V dO^T: lane holds query q, keys t*32 + 8 (i/4) + 4 h + i % 4.
+        f32x16 s1, s2, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { s1[i] = 0.f; s2[i] = 0.f; dp[i] = 0.f; }
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            s1 = mfma(*(const bf16x8*)(k1s + (k_rd0 ^ (32 * kc))), qa[kc], s1);
+            s2 = mfma(*(const bf16x8*)(k2s + (k_rd0 ^ (32 * kc))), qbf[kc], s2);
+        }
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) dp = mfma(*(const bf16x8*)(vs + vr_off(l32, 2 * kc + h)), dob[kc], dp);
+        const int kv0 = t * TILE;
+        float g1[16], g2[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = kv0 + 8 * (i >> 2) + 4 * h + (i & 3);
+            const bool vis = key < N && (!causal || key <= q);
+            const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -lse1));
+            const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -lse2));
+            g1[i] = vis ? a * (dp[i] - e1) : 0.f;
+            g2[i] = vis ? b * (dp[i] - e2) : 0.f;   // times -lambda at the end
+        }
+        bf16x8 p1[2], p2[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 a, b;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                a[k] = pack2(g1[8 * ks + 2 * k], g1[8 * ks + 2 * k + 1]);
+                b[k] = pack2(g2[8 * ks + 2 * k], g2[8 * ks + 2 * k + 1]);
+            }
+            p1[ks] = __builtin_bit_cast(bf16x8, a);
+            p2[ks] = __builtin_bit_cast(bf16x8, b);
+        }
+        // dQ^T += K^T ds^T: A = K^T rows d = 32 mb + l32, key chunk 2 ks + h.
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const int off = (ks ? t_rd1 : t_rd0) + 2048 * mb;
+                acc1[mb] = mfma(*(const bf16x8*)(k1t + off), p1[ks], acc1[mb]);
+                acc2[mb] = mfma(*(const bf16x8*)(k2t + off), p2[ks], acc2[mb]);
+            }
+    }
+    if (q >= N) return;
+    const float sc1 = 0.125f, sc2 = -lambda_of(ep, bh) * 0.125f;
+    uint16_t* r1 = dq1 + hqk + (size_t)q * D + 4 * h;
+    uint16_t* r2 = dq2 + hqk + (size_t)q * D + 4 * h;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            u32x2 w1, w2;
+            w1[0] = pack2(acc1[mb][4 * g4] * sc1, acc1[mb][4 * g4 + 1] * sc1);
+            w1[1] = pack2(acc1[mb][4 * g4 + 2] * sc1, acc1[mb][4 * g4 + 3] * sc1);
+            w2[0] = pack2(acc2[mb][4 * g4] * sc2, acc2[mb][4 * g4 + 1] * sc2);
+            w2[1] = pack2(acc2[mb][4 * g4 + 2] * sc2, acc2[mb][4 * g4 + 3] * sc2);
+            *(u32x2*)(r1 + 32 * mb + 8 * g4) = w1;
+            *(u32x2*)(r2 + 32 * mb + 8 * g4) = w2;
+        }
+}
+
+// ---------------------------------------------------------------------------------------------------------------
+// 3. dK, dV: per 128-key block; lane owns key k0w + l32 in every product.
+// ---------------------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1,
+                     const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
+                     const uint16_t* __restrict__ gv, const uint16_t* __restrict__ gdo,
+                     const float* __restrict__ stats, uint16_t* __restrict__ dk1, uint16_t* __restrict__ dk2,
+                     uint16_t* __restrict__ dv, int BH, int N, int n_blocks, int causal, Epilogue ep) {
+    __shared__ __attribute__((aligned(16))) unsigned char q1s[TILE * D * 2], q2s[TILE * D * 2], dos[TILE * DV * 2];
+    __shared__ __attribute__((aligned(16))) unsigned char q1t[TILE * D * 2], q2t[TILE * D * 2], dot[TILE * DV * 2];
+    __shared__ __attribute__((aligned(16))) float sts[STAT_FLOATS][TILE];   // lse1, lse2, E1, E2 per query
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const int bid = blockIdx.x;
+    const int kb = bid / BH;   // key blocks in order: the first ones see the most queries under the causal mask
+    const int bh = bid % BH;
+    const int k0 = kb * BLOCK, k0w = k0 + TILE * wave;
+    const size_t hqk = (size_t)bh * N * D, hv = (size_t)bh * N * DV;
+    const int key = k0w + l32, kc_row = min(key, N - 1);
+    (void)n_blocks;
+
+    bf16x8 kb1[4], kb2[4], vb[8];   // the wave's K and V rows as B operands (k = feature, n = key)
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+        kb1[kc] = *(const bf16x8*)(gk1 + hqk + (size_t)kc_row * D + 16 * kc + 8 * h);
+        kb2[kc] = *(const bf16x8*)(gk2 + hqk + (size_t)kc_row * D + 16 * kc + 8 * h);
+    }
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) vb[kc] = *(const bf16x8*)(gv + hv + (size_t)kc_row * DV + 16 * kc + 8 * h);
+    const float c = LOG2E * 0.125f;
+    const float lam = lambda_of(ep, bh);
+
+    f32x16 av[4], ak1[2], ak2[2];   // dV^T, dK1^T, dK2^T: feature 32 blk + 8 (i/4) + 4 h + i % 4, key = lane's key
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) av[cb][i] = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) { ak1[nb][i] = 0.f; ak2[nb][i] = 0.f; }
+    }
+
+    const int n_qt = (N + TILE - 1) / TILE;
+    const int u_first = causal ? k0 / TILE : 0;                  // workgroup's first query tile
+    const int u_wave = causal ? k0w / TILE : 0;                  // this wave's first query tile with visible queries
+    const int a_rd0 = k_off(l32, h);                            // Q tile A-operand read (row l32, chunk 2 kc + h)
+    const int t_rd0 = vt_off(l32, h), t_rd1 = vt_off(l32, 2 + h);
+
+    u32x4 rq1[1], rq2[1], rdo[2];
+    f32x4 rst = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto load_q = [&](int u) __attribute__((always_inline)) {
+        load_tile<D>(gq1 + hqk, u * TILE, N, tid, rq1);
+        load_tile<D>(gq2 + hqk, u * TILE, N, tid, rq2);
+        load_tile<DV>(gdo + hv, u * TILE, N, tid, rdo);
+        const int qr = u * TILE + tid;
+        if (tid < TILE && qr < N) rst = *(const f32x4*)(stats + ((size_t)bh * N + qr) * STAT_FLOATS);
+    };
+    if (u_first < n_qt) load_q(u_first);
+    for (int u = u_first; u < n_qt; ++u) {
+        __syncthreads();
+        store_tile<D>(q1s, tid, rq1);
+        store_tile<D>(q2s, tid, rq2);
+        store_tile<DV>(dos, tid, rdo);
+        if (tid < TILE) {
+#pragma unroll
+            for (int k = 0; k < STAT_FLOATS; ++k) sts[k][tid] = rst[k];
+        }
+        __syncthreads();
+        transpose_tile<D>(q1s, q1t, tid);
+        transpose_tile<D>(q2s, q2t, tid);
+        transpose_tile<DV>(dos, dot, tid);
+        if (u + 1 < n_qt) load_q(u + 1);
+        __syncthreads();
+        if (u < u_wave) continue;
+        // S = Q K^T and dP = dO V^T: lane holds key `key`, queries u*32 + 8 (i/4) + 4 h + i % 4.
+        f32x16 s1, s2, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { s1[i] = 0.f; s2[i] = 0.f; dp[i] = 0.f; }
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            s1 = mfma(*(const bf16x8*)(q1s + (a_rd0 ^ (32 * kc))), kb1[kc], s1);
+            s2 = mfma(*(const bf16x8*)(q2s + (a_rd0 ^ (32 * kc))), kb2[kc], s2);
+        }
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) dp = mfma(*(const bf16x8*)(dos + vr_off(l32, 2 * kc + h)), vb[kc], dp);
+        float w[16], g1[16], g2[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int qo = 8 * g + 4 * h;   // first of the 4 queries of element group g
+            const f32x4 L1 = *(const f32x4*)&sts[0][qo], L2 = *(const f32x4*)&sts[1][qo];
+            const f32x4 E1 = *(const f32x4*)&sts[2][qo], E2 = *(const f32x4*)&sts[3][qo];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * g + e;
+                const int qq = u * TILE + qo + e;
+                const bool vis = qq < N && (!causal || key <= qq);
+                const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -L1[e]));
+                const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -L2[e]));
+                w[i] = vis ? a - lam * b : 0.f;
+                g1[i] = vis ? a * (dp[i] - E1[e]) : 0.f;
+                g2[i] = vis ? b * (dp[i] - E2[e]) : 0.f;   // times -lambda at the end
+            }
+        }
+        bf16x8 pw[2], p1[2], p2[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 x, y, z;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x[k] = pack2(w[8 * ks + 2 * k], w[8 * ks + 2 * k + 1]);
+                y[k] = pack2(g1[8 * ks + 2 * k], g1[8 * ks + 2 * k + 1]);
+                z[k] = pack2(g2[8 * ks + 2 * k], g2[8 * ks + 2 * k + 1]);
+            }
+            pw[ks] = __builtin_bit_cast(bf16x8, x);
+            p1[ks] = __builtin_bit_cast(bf16x8, y);
+            p2[ks] = __builtin_bit_cast(bf16x8, z);
+        }
+        // dV^T += dO^T W, dK^T += Q^T ds: A = transposed tiles (feature rows 32 blk + l32, query chunk 2 ks + h).
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int tr = ks ? t_rd1 : t_rd0;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) av[cb] = mfma(*(const bf16x8*)(dot + tr + 2048 * cb), pw[ks], av[cb]);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                ak1[nb] = mfma(*(const bf16x8*)(q1t + tr + 2048 * nb), p1[ks], ak1[nb]);
+                ak2[nb] = mfma(*(const bf16x8*)(q2t + tr + 2048 * nb), p2[ks], ak2[nb]);
+            }
+        }
+    }
+    if (key >= N) return;
+    const float sc1 = 0.125f, sc2 = -lam * 0.125f;
+    uint16_t* r1 = dk1 + hqk + (size_t)key * D + 4 * h;
+    uint16_t* r2 = dk2 + hqk + (size_t)key * D + 4 * h;
+    uint16_t* rvv = dv + hv + (size_t)key * DV + 4 * h;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            u32x2 w1, w2;
+            w1[0] = pack2(ak1[nb][4 * g4] * sc1, ak1[nb][4 * g4 + 1] * sc1);
+            w1[1] = pack2(ak1[nb][4 * g4 + 2] * sc1, ak1[nb][4 * g4 + 3] * sc1);
+            w2[0] = pack2(ak2[nb][4 * g4] * sc2, ak2[nb][4 * g4 + 1] * sc2);
+            w2[1] = pack2(ak2[nb][4 * g4 + 2] * sc2, ak2[nb][4 * g4 + 3] * sc2);
+            *(u32x2*)(r1 + 32 * nb + 8 * g4) = w1;
+            *(u32x2*)(r2 + 32 * nb + 8 * g4) = w2;
+        }
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            u32x2 wv;
+            wv[0] = pack2(av[cb][4 * g4], av[cb][4 * g4 + 1]);
+            wv[1] = pack2(av[cb][4 * g4 + 2], av[cb][4 * g4 + 3]);
+            *(u32x2*)(rvv + 32 * cb + 8 * g4) = wv;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------------------------
+// 4. dlambda: one workgroup per head, fixed summation order.
+// ---------------------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(THREADS) void bwd_dlambda_kernel(const float* __restrict__ dl_rows, float* __restrict__ dlambda,
+                                                              int B, int H, int N) {
+    __shared__ float red[THREADS];
+    const int hh = blockIdx.x, tid = threadIdx.x;
+    float acc = 0.f;
+    for (int b = 0; b < B; ++b) {
+        const float* p = dl_rows + ((size_t)b * H + hh) * N;
+        for (int i = tid; i < N; i += THREADS) acc += p[i];
+    }
+    red[tid] = acc;
+    __syncthreads();
+    for (int s = THREADS / 2; s > 0; s >>= 1) {
+        if (tid < s) red[tid] += red[tid + s];
+        __syncthreads();
+    }
+    if (tid == 0) dlambda[hh] = red[0];
+}
+
+}  // namespace
+
+size_t bwd_bf16_workspace_bytes(int64_t BH, int64_t N) {
+    const size_t rows = (size_t)BH * (size_t)N;
+    // dO (bf16, 2d per row) | stats (4 floats per row) | dlambda shares (1 float per row), each 256-byte aligned
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    return up(rows * DV * 2) + up(rows * STAT_FLOATS * 4) + up(rows * 4);
+}
+
+hipError_t launch_bwd_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
+                               const uint16_t* v, const uint16_t* dy, const float* saved, uint16_t* dq1,
+                               uint16_t* dk1, uint16_t* dq2, uint16_t* dk2, uint16_t* dv, float* dlambda, int64_t B,
+                               int64_t H, int64_t N, int causal, Epilogue ep, void* workspace, hipStream_t stream) {
+    const int64_t BH = B * H, rows = BH * N;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    unsigned char* ws = (unsigned char*)workspace;
+    uint16_t* dO = (uint16_t*)ws;
+    float* stats = (float*)(ws + up((size_t)rows * DV * 2));
+    float* dl_rows = (float*)(ws + up((size_t)rows * DV * 2) + up((size_t)rows * STAT_FLOATS * 4));
+    const int64_t pre_blocks = (rows + WAVES - 1) / WAVES;
+    const int n_blocks = (int)((N + BLOCK - 1) / BLOCK);
+    const int64_t grid = (int64_t)n_blocks * BH;
+    if (pre_blocks > 0x7fffffff || grid > 0x7fffffff) return hipErrorInvalidValue;
+    if (rows == 0) {   // only dlambda (zeros)
+        hipLaunchKernelGGL(bwd_dlambda_kernel, dim3((unsigned)H), dim3(THREADS), 0, stream, dl_rows, dlambda, (int)B,
+                           (int)H, 0);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)pre_blocks), dim3(THREADS), 0, stream, dy, saved, dO, stats,
+                       dl_rows, rows, (int)N, ep);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)grid), dim3(THREADS), 0, stream, q1, k1, q2, k2, v, dO, stats,
+                       dq1, dq2, (int)BH, (int)N, n_blocks, causal ? 1 : 0, ep);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)grid), dim3(THREADS), 0, stream, q1, k1, q2, k2, v, dO, stats,
+                       dk1, dk2, dv, (int)BH, (int)N, n_blocks, causal ? 1 : 0, ep);
+    hipLaunchKernelGGL(bwd_dlambda_kernel, dim3((unsigned)H), dim3(THREADS), 0, stream, dl_rows, dlambda, (int)B,
+                       (int)H, (int)N);
+    return hipGetLastError();
+}
+
+}  // namespace diffattn

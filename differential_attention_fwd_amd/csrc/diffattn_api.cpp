@@ -127,7 +127,8 @@ int fwd_impl(const void* q1, const void* k1, const void* q2, const void* k2, con
     if (dtype == DIFFATTN_BF16)
         return hip_status(diffattn::launch_prefill_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1,
                                                             (const uint16_t*)q2, (const uint16_t*)k2,
-                                                            (const uint16_t*)v, (uint16_t*)out, BH, N, causal, ep, s));
+                                                            (const uint16_t*)v, (uint16_t*)out, BH, N, causal, ep, nullptr,
+                                                            s));
     return hip_status(diffattn::launch_attn_f32((const float*)q1, (const float*)k1, (const float*)q2, (const float*)k2,
                                                 (const float*)v, (float*)out, BH, N, N, d, causal, ep, s));
 }
@@ -230,6 +231,117 @@ int diffattn_decode_heads(const void* q1, const void* k1, const void* q2, const 
     (void)causal;
     return decode_impl(q1, k1, q2, k2, v, out, B, H, L, d, dtype, 0.0f, lambda_heads, true, layer, workspace,
                        workspace_bytes, stream);
+}
+
+
+size_t diffattn_train_saved_bytes(int64_t B, int64_t H, int64_t N, int d) {
+    int64_t BH, rows;
+    if (B < 0 || H < 0 || N < 0 || N > DIFFATTN_MAX_LEN || d != 64 || !mul_ok(B, H, &BH) || BH > INT32_MAX ||
+        !mul_ok(BH, N, &rows))
+        return 0;
+    return (size_t)rows * diffattn::SAVED_FLOATS * sizeof(float);
+}
+
+size_t diffattn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int d) {
+    int64_t BH, rows;
+    if (B < 0 || H < 0 || N < 0 || N > DIFFATTN_MAX_LEN || d != 64 || !mul_ok(B, H, &BH) || BH > INT32_MAX ||
+        !mul_ok(BH, N, &rows) || rows == 0)
+        return 0;
+    return diffattn::bwd_bf16_workspace_bytes(BH, N);
+}
+
+int diffattn_fwd_train(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
+                       int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda, const float* lambda_heads,
+                       int layer, int causal, void* saved, size_t saved_bytes, void* stream) {
+    if (B < 0 || H < 0 || N < 0 || N > DIFFATTN_MAX_LEN) return DIFFATTN_ERR_SHAPE;
+    if (dtype != DIFFATTN_BF16 || d != 64) return DIFFATTN_ERR_UNSUPPORTED;
+    Epilogue ep;
+    int st = make_epilogue(lambda_heads ? 0.0f : lambda, layer, &ep);
+    if (st) return st;
+    int64_t BH, rows;
+    if (!mul_ok(B, H, &BH) || BH > INT32_MAX || !mul_ok(BH, N, &rows)) return DIFFATTN_ERR_SHAPE;
+    if (rows == 0) return DIFFATTN_OK;
+    if (!q1 || !k1 || !q2 || !k2 || !v || !out || !saved) return DIFFATTN_ERR_NULL;
+    if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2) || !aligned16(v) || !aligned16(out) ||
+        !aligned16(saved))
+        return DIFFATTN_ERR_ALIGN;
+    const size_t need = diffattn_train_saved_bytes(B, H, N, d);
+    if (saved_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+    const size_t qk = (size_t)rows * 64 * 2, vb = (size_t)rows * 128 * 2;
+    const Span ins[5] = {{(uintptr_t)q1, (uintptr_t)q1 + qk}, {(uintptr_t)k1, (uintptr_t)k1 + qk},
+                         {(uintptr_t)q2, (uintptr_t)q2 + qk}, {(uintptr_t)k2, (uintptr_t)k2 + qk},
+                         {(uintptr_t)v, (uintptr_t)v + vb}};
+    const Span o{(uintptr_t)out, (uintptr_t)out + vb}, sv{(uintptr_t)saved, (uintptr_t)saved + need};
+    if (overlaps(o, sv)) return DIFFATTN_ERR_ALIAS;
+    for (const Span& sp : ins)
+        if (overlaps(o, sp) || overlaps(sv, sp)) return DIFFATTN_ERR_ALIAS;
+    if (lambda_heads) {
+        st = check_lambda_heads(lambda_heads, H, o);
+        if (st) return st;
+        if (overlaps(sv, Span{(uintptr_t)lambda_heads, (uintptr_t)lambda_heads + (size_t)H * sizeof(float)}))
+            return DIFFATTN_ERR_ALIAS;
+        ep.lambda_heads = lambda_heads;
+        ep.heads = (int)H;
+    }
+    return hip_status(diffattn::launch_prefill_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
+                                                        (const uint16_t*)k2, (const uint16_t*)v, (uint16_t*)out, BH,
+                                                        N, causal, ep, (float*)saved, (hipStream_t)stream));
+}
+
+int diffattn_bwd(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, const void* dy,
+                 const void* saved, void* dq1, void* dk1, void* dq2, void* dk2, void* dv, float* dlambda, int64_t B,
+                 int64_t H, int64_t N, int d, int dtype, float lambda, const float* lambda_heads, int layer,
+                 int causal, void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || H < 0 || N < 0 || N > DIFFATTN_MAX_LEN) return DIFFATTN_ERR_SHAPE;
+    if (dtype != DIFFATTN_BF16 || d != 64) return DIFFATTN_ERR_UNSUPPORTED;
+    Epilogue ep;
+    int st = make_epilogue(lambda_heads ? 0.0f : lambda, layer, &ep);
+    if (st) return st;
+    int64_t BH, rows;
+    if (!mul_ok(B, H, &BH) || BH > INT32_MAX || !mul_ok(BH, N, &rows)) return DIFFATTN_ERR_SHAPE;
+    if (BH == 0) return DIFFATTN_OK;
+    if (!dlambda) return DIFFATTN_ERR_NULL;
+    if (((uintptr_t)dlambda & 3u) != 0) return DIFFATTN_ERR_ALIGN;
+    if (rows == 0)   // no rows: dlambda is zero (written by a kernel, so the call stays capturable in a graph)
+        return hip_status(diffattn::launch_bwd_bf16_d64(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                         nullptr, nullptr, nullptr, nullptr, nullptr, dlambda, B, H, 0,
+                                                         causal, ep, nullptr, (hipStream_t)stream));
+    if (!q1 || !k1 || !q2 || !k2 || !v || !dy || !saved || !dq1 || !dk1 || !dq2 || !dk2 || !dv) return DIFFATTN_ERR_NULL;
+    const void* a16[] = {q1, k1, q2, k2, v, dy, saved, dq1, dk1, dq2, dk2, dv};
+    for (const void* p : a16)
+        if (!aligned16(p)) return DIFFATTN_ERR_ALIGN;
+    const size_t need = diffattn_bwd_workspace_bytes(B, H, N, d);
+    if (!workspace || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return DIFFATTN_ERR_ALIGN;
+    const size_t qk = (size_t)rows * 64 * 2, vb = (size_t)rows * 128 * 2;
+    const size_t sb = diffattn_train_saved_bytes(B, H, N, d);
+    const Span ins[7] = {{(uintptr_t)q1, (uintptr_t)q1 + qk}, {(uintptr_t)k1, (uintptr_t)k1 + qk},
+                         {(uintptr_t)q2, (uintptr_t)q2 + qk}, {(uintptr_t)k2, (uintptr_t)k2 + qk},
+                         {(uintptr_t)v, (uintptr_t)v + vb}, {(uintptr_t)dy, (uintptr_t)dy + vb},
+                         {(uintptr_t)saved, (uintptr_t)saved + sb}};
+    const Span outs[7] = {{(uintptr_t)dq1, (uintptr_t)dq1 + qk}, {(uintptr_t)dk1, (uintptr_t)dk1 + qk},
+                          {(uintptr_t)dq2, (uintptr_t)dq2 + qk}, {(uintptr_t)dk2, (uintptr_t)dk2 + qk},
+                          {(uintptr_t)dv, (uintptr_t)dv + vb},
+                          {(uintptr_t)dlambda, (uintptr_t)dlambda + (size_t)H * sizeof(float)},
+                          {(uintptr_t)workspace, (uintptr_t)workspace + need}};
+    for (int i = 0; i < 7; ++i) {
+        for (const Span& sp : ins)
+            if (overlaps(outs[i], sp)) return DIFFATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 7; ++j)
+            if (overlaps(outs[i], outs[j])) return DIFFATTN_ERR_ALIAS;
+    }
+    if (lambda_heads) {
+        if (((uintptr_t)lambda_heads & 3u) != 0) return DIFFATTN_ERR_ALIGN;
+        const Span l{(uintptr_t)lambda_heads, (uintptr_t)lambda_heads + (size_t)H * sizeof(float)};
+        for (const Span& sp : outs)
+            if (overlaps(l, sp)) return DIFFATTN_ERR_ALIAS;
+        ep.lambda_heads = lambda_heads;
+        ep.heads = (int)H;
+    }
+    return hip_status(diffattn::launch_bwd_bf16_d64(
+        (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2, (const uint16_t*)k2, (const uint16_t*)v,
+        (const uint16_t*)dy, (const float*)saved, (uint16_t*)dq1, (uint16_t*)dk1, (uint16_t*)dq2, (uint16_t*)dk2,
+        (uint16_t*)dv, dlambda, B, H, N, causal, ep, workspace, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -21,10 +21,28 @@ __device__ __forceinline__ float lambda_of(const Epilogue& ep, int bh) {
     return ep.lambda_heads ? ep.lambda_heads[bh % ep.heads] : ep.lambda;
 }
 
-// bf16 prefill, d = 64, 2d = 128: fused one-pass kernel (two online softmaxes, two MFMA accumulators).
+// Training statistics of one query row (d = 64), written by the forward for the backward pass, fp32:
+//   [0] lse1, [1] lse2: log-sum-exp of each map in log2 units of the scaled scores (p = 2^(s log2(e)/sqrt(d) - lse))
+//   [2] r = 1 / sqrt(mean(o^2) + 1e-5) of the combined row o (1 when the layer is not normalised), [3] unused
+//   [SAVED_O1 ..] o1 = map 1 times V (128 floats), [SAVED_O2 ..] o2 = map 2 times V (128 floats).
+constexpr int SAVED_O1 = 4;
+constexpr int SAVED_O2 = 4 + 128;
+constexpr int SAVED_FLOATS = 4 + 256;   // 1040 bytes per row
+
+// bf16 prefill, d = 64, 2d = 128: fused one-pass kernel (two online softmaxes, two MFMA accumulators).  With a
+// non-null `saved` ([BH][N][SAVED_FLOATS] fp32) it also writes each row's training statistics.
 hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
                                    const uint16_t* v, uint16_t* out, int64_t BH, int64_t N, int causal,
-                                   Epilogue ep, hipStream_t stream);
+                                   Epilogue ep, float* saved, hipStream_t stream);
+
+// bf16 backward, d = 64: preprocess, dQ, dK/dV and dlambda kernels (see backward_bf16.hip).  `saved` is the
+// training forward's [BH][N][SAVED_FLOATS]; `workspace` holds bwd_bf16_workspace_bytes(BH, N) bytes (256-byte
+// aligned); dlambda receives H floats (per head, summed over the batch).
+size_t bwd_bf16_workspace_bytes(int64_t BH, int64_t N);
+hipError_t launch_bwd_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
+                               const uint16_t* v, const uint16_t* dy, const float* saved, uint16_t* dq1,
+                               uint16_t* dk1, uint16_t* dq2, uint16_t* dk2, uint16_t* dv, float* dlambda, int64_t B,
+                               int64_t H, int64_t N, int causal, Epilogue ep, void* workspace, hipStream_t stream);
 
 // fp32 path (d = 8 or 64), general Nq <= Nk with end-aligned causal mask; exact three-pass softmax per row.
 hipError_t launch_attn_f32(const float* q1, const float* k1, const float* q2, const float* k2, const float* v,

@@ -33,19 +33,10 @@
 // This translation unit is compiled with -fno-honor-nans: no NaN can arise (inputs are finite, masked scores are
 // -inf, and every processed row has a visible key in its first tile), and it lets v_max3 run without quieting.
 #include "launch.h"
+#include "tiles.h"
 
 namespace diffattn {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = 64;
 constexpr int DV = 128;
@@ -70,42 +61,6 @@ template <int S, class T> __device__ __forceinline__ T* pick4(T* a, T* b, T* c, 
     else return d;
 }
 constexpr float RESCALE_THRESHOLD = 8.0f;       // log2 units: p never exceeds 2^8 between rescales
-constexpr float LOG2E = 1.4426950408889634f;
-
-// K tile: row r (key) of 128 bytes = 8 chunks of 16 bytes; chunk c lives at position c ^ ((r >> 1) & 7).  A wave's
-// 16-lane read group (16 rows, one chunk) and the contiguous direct loads both touch 16 distinct bank quads.
-__device__ __forceinline__ int k_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
-
-// Transposed V tile: 128 channel rows of 64 bytes (32 keys).  Keys are stored in the accumulator's key order:
-// key 16s + 8a + 4h + j sits at position 16s + 8h + 4a + j (bits 2 and 3 swapped).  Channel c occupies physical
-// row (c & ~3) | ((c & 3) ^ ((c >> 4) & 1)) and its 16-byte chunk q sits at q ^ ((c >> 2) & 3): the 16
-// consecutive channels of a 128-bit read group hit 16 distinct bank quads, and a transposing write group
-// (4 key groups x 8 channel groups) at most 2-way shares one.  The swizzle uses only channel bits 0..4, so the
-// four 32-channel blocks of a read differ by a constant offset.
-__device__ __forceinline__ int vt_off(int c, int chunk) {
-    const int prow = (c & ~3) | ((c & 3) ^ ((c >> 4) & 1));
-    return prow * 64 + ((chunk ^ ((c >> 2) & 3)) << 4);
-}
-__device__ __forceinline__ int key_pos(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
-
-// Raw V tile as loaded: row r (key) of 256 bytes = 16 chunks of 16 bytes; chunk c lives at c ^ (2 (r & 3)), so the
-// 4 rows x 32 bytes read by each 16-lane group of a transposing read hit 8 distinct bank quads.
-__device__ __forceinline__ int vr_off(int row, int chunk) { return row * 256 + ((chunk ^ ((row & 3) << 1)) << 4); }
-
-// Combine a per-lane value with the value of lane (l ^ 32).
-__device__ __forceinline__ float pair_max(float x) {
-    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-__device__ __forceinline__ unsigned pack2(float a, float b) {
-    const f32x2 v = {a, b};
-    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
-}
 
 __device__ __forceinline__ float max16(const f32x16& s) {
     const float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
@@ -169,29 +124,13 @@ __device__ __forceinline__ float sum_packed(const bf16x8& lo, const bf16x8& hi, 
     return l + (t0 + t1);
 }
 
-__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8): wait until at most `vm` vector
-// memory operations of this wave are outstanding and all LDS operations are done.
-constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14); }
-
-// Workgroup barrier without the memory-model fence of __syncthreads (which would drain every outstanding load,
-// including prefetches meant to stay in flight).  Callers first wait for their own LDS traffic with s_waitcnt;
-// LDS is coherent inside the workgroup.  The empty asm statements keep the compiler from moving memory
-// accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
+// SAVE: also write each row's training statistics (SAVED_* in launch.h) for the backward pass.
+template <bool SAVE>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1,
                              const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
                              const uint16_t* __restrict__ gv, uint16_t* __restrict__ gout, int BH, int N,
-                             int n_row_tiles, int causal, Epilogue ep) {
+                             int n_row_tiles, int causal, Epilogue ep, float* __restrict__ saved) {
     __shared__ __attribute__((aligned(16))) unsigned char kr0[K_SLOT_BYTES], kr1[K_SLOT_BYTES], kr2[K_SLOT_BYTES],
         kr3[K_SLOT_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char vr0[V_TILE_BYTES], vr1[V_TILE_BYTES], vr2[V_TILE_BYTES],
@@ -419,21 +358,52 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     const float l2 = pair_sum(st2.l);
     const float inv1 = 1.f / l1;
     const float inv2 = lambda_of(ep, bh) / l2;
+    const int q = q0w + l32;
+    float* srow = nullptr;
+    if constexpr (SAVE) {
+        // The two maps' normalised outputs, O1 / l1 and O2 / l2, before they are combined.
+        if (q < N) {
+            srow = saved + ((size_t)bh * N + q) * SAVED_FLOATS;
+            const float r2 = 1.f / l2;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int ch = cb * 32 + 8 * g4 + 4 * h;
+                    f32x4 a, b;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        a[e] = o1[cb][4 * g4 + e] * inv1;
+                        b[e] = o2[cb][4 * g4 + e] * r2;
+                    }
+                    *(f32x4*)(srow + SAVED_O1 + ch) = a;
+                    *(f32x4*)(srow + SAVED_O2 + ch) = b;
+                }
+        }
+    }
     float ss = 0.f;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float o = o1[cb][i] * inv1 - o2[cb][i] * inv2;
+            // One explicit fused multiply-add over a rounded product: the training variant, which also stores
+            // o1 * inv1, then produces the same output bits (contraction could otherwise fuse either product).
+            const float t2 = o2[cb][i] * inv2;
+            const float o = __builtin_fmaf(o1[cb][i], inv1, -t2);
             o1[cb][i] = o;
             ss += o * o;
         }
-    float r = 1.f;
+    float rr = 1.f;   // 1 / sqrt(mean(o^2) + eps) when normalising
     if (ep.normalise) {
         ss = pair_sum(ss);
-        r = __builtin_amdgcn_rsqf(ss * (1.f / DV) + 1e-5f) * ep.out_scale;
+        rr = __builtin_amdgcn_rsqf(ss * (1.f / DV) + 1e-5f);
     }
-    const int q = q0w + l32;
+    const float r = ep.normalise ? rr * ep.out_scale : 1.f;
+    if constexpr (SAVE) {
+        // Log-sum-exp of each map in log2 units of the scaled scores: p = 2^(s * log2(e) / sqrt(d) - lse).
+        if (q < N && h == 0)
+            *(f32x4*)srow = f32x4{st1.ml + __builtin_amdgcn_logf(l1), st2.ml + __builtin_amdgcn_logf(l2), rr, 0.f};
+    }
     if (q < N) {
         uint16_t* orow = gout + head_v + (size_t)q * DV + 4 * h;
 #pragma unroll
@@ -452,12 +422,16 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
 
 hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
                                    const uint16_t* v, uint16_t* out, int64_t BH, int64_t N, int causal,
-                                   Epilogue ep, hipStream_t stream) {
+                                   Epilogue ep, float* saved, hipStream_t stream) {
     const int n_row_tiles = (int)((N + BM - 1) / BM);
     const int64_t blocks = (int64_t)n_row_tiles * BH;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(prefill_bf16_d64_kernel, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1, q2, k2, v,
-                       out, (int)BH, (int)N, n_row_tiles, causal ? 1 : 0, ep);
+    if (saved)
+        hipLaunchKernelGGL(prefill_bf16_d64_kernel<true>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1,
+                           q2, k2, v, out, (int)BH, (int)N, n_row_tiles, causal ? 1 : 0, ep, saved);
+    else
+        hipLaunchKernelGGL(prefill_bf16_d64_kernel<false>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1,
+                           q2, k2, v, out, (int)BH, (int)N, n_row_tiles, causal ? 1 : 0, ep, saved);
     return hipGetLastError();
 }
 

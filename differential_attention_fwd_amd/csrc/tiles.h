@@ -1,0 +1,82 @@
+// Tile layouts and small wave-level helpers shared by the bf16 kernels for gfx950 (forward and backward).
+//
+// MFMA v_mfma_f32_32x32x16_bf16 operand layouts (lane l, h = l / 32, r = l % 32):
+//   A (32 x 16): lane holds A[m = r][k = 8 h + j], j = 0..7      B (16 x 32): lane holds B[k = 8 h + j][n = r]
+//   D (32 x 32): lane holds D[m = 8 (i / 4) + 4 h + i % 4][n = r], i = 0..15
+// A row-major tile feeds A operands with one 16-byte read per lane; a k-dimension that runs along the tile's rows
+// (keys or queries) needs the tile transposed ("T" tiles below).  When such a product consumes an accumulator of
+// another product as its B operand, the k order is the accumulator's row order: position 8 h + j of a 16-slot
+// k step holds row 8 (j / 4) + 4 h + j % 4, i.e. bits 2 and 3 of the row index swapped (key_pos).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace diffattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+// K tile: row r (key) of 128 bytes = 8 chunks of 16 bytes; chunk c lives at position c ^ ((r >> 1) & 7).  A wave's
+// 16-lane read group (16 rows, one chunk) and the contiguous direct loads both touch 16 distinct bank quads.
+__device__ __forceinline__ int k_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+// Transposed tile (V^T, and any [32 rows][W] tile transposed): W channel rows of 64 bytes (32 keys or queries).  Keys are stored in the accumulator's key order:
+// key 16s + 8a + 4h + j sits at position 16s + 8h + 4a + j (bits 2 and 3 swapped).  Channel c occupies physical
+// row (c & ~3) | ((c & 3) ^ ((c >> 4) & 1)) and its 16-byte chunk q sits at q ^ ((c >> 2) & 3): the 16
+// consecutive channels of a 128-bit read group hit 16 distinct bank quads, and a transposing write group
+// (4 key groups x 8 channel groups) at most 2-way shares one.  The swizzle uses only channel bits 0..4, so the
+// four 32-channel blocks of a read differ by a constant offset.
+__device__ __forceinline__ int vt_off(int c, int chunk) {
+    const int prow = (c & ~3) | ((c & 3) ^ ((c >> 4) & 1));
+    return prow * 64 + ((chunk ^ ((c >> 2) & 3)) << 4);
+}
+__device__ __forceinline__ int key_pos(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
+
+// Raw V tile as loaded: row r (key) of 256 bytes = 16 chunks of 16 bytes; chunk c lives at c ^ (2 (r & 3)), so the
+// 4 rows x 32 bytes read by each 16-lane group of a transposing read hit 8 distinct bank quads.
+__device__ __forceinline__ int vr_off(int row, int chunk) { return row * 256 + ((chunk ^ ((row & 3) << 1)) << 4); }
+
+// Combine a per-lane value with the value of lane (l ^ 32).
+__device__ __forceinline__ float pair_max(float x) {
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8): wait until at most `vm` vector
+// memory operations of this wave are outstanding and all LDS operations are done.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14); }
+
+// Workgroup barrier without the memory-model fence of __syncthreads (which would drain every outstanding load,
+// including prefetches meant to stay in flight).  Callers first wait for their own LDS traffic with s_waitcnt;
+// LDS is coherent inside the workgroup.  The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+}  // namespace diffattn

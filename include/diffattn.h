@@ -108,6 +108,37 @@ int diffattn_decode_heads(const void *q1, const void *k1, const void *q2, const 
                           int64_t B, int64_t H, int64_t L, int d, int dtype, const float *lambda_heads, int layer,
                           int causal, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Training: a forward that keeps what the backward pass needs, and the backward pass.  The pages describe no
+ * backward; it is the chain rule of the forward above (normalisation, the lambda-weighted difference, both
+ * softmaxes, the scaled scores), so gradients are those of the exact forward definition.  bf16 with d = 64 only
+ * (anything else -> DIFFATTN_ERR_UNSUPPORTED); causal or not; lambda scalar, or per head when lambda_heads is
+ * non-NULL (a device array of H floats, as for diffattn_fwd_heads; then `lambda` is ignored).
+ *
+ * diffattn_train_saved_bytes: size of `saved` for diffattn_fwd_train, B*H*N*1040 bytes (0 if unsupported).
+ * diffattn_fwd_train: same output as diffattn_fwd (bit-identical), and writes `saved` (device, 16-byte aligned,
+ *   >= diffattn_train_saved_bytes, overlapping nothing else): per query row the two maps' log-sum-exps, the row's
+ *   RMS factor and the two maps' outputs before they are combined (fp32; layout private to the library).
+ * diffattn_bwd_workspace_bytes: scratch size for diffattn_bwd (0 for an empty problem or unsupported d).
+ * diffattn_bwd: given dy = dLoss/dout ([B][H][N][2d] bf16) and the `saved` of the forward call with the same
+ *   inputs, lambda, layer and causal flag, writes dq1, dk1, dq2, dk2 ([B][H][N][d] bf16), dv ([B][H][N][2d] bf16)
+ *   and dlambda (device, H floats, 4-byte aligned: dLoss/dlambda of each head, summed over the batch; for one
+ *   lambda shared by all heads, sum the H values).  All gradients are overwritten, not accumulated.
+ *   workspace: device, 256-byte aligned, >= diffattn_bwd_workspace_bytes (contents on entry ignored).
+ *   Outputs, dlambda and workspace must not overlap each other or any input.  N == 0 writes zeros to dlambda;
+ *   B*H == 0 is a no-op.  Errors as for diffattn_fwd, plus DIFFATTN_ERR_WORKSPACE for a missing or small
+ *   workspace / saved buffer.
+ */
+size_t diffattn_train_saved_bytes(int64_t B, int64_t H, int64_t N, int d);
+int diffattn_fwd_train(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
+                       int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda, const float *lambda_heads,
+                       int layer, int causal, void *saved, size_t saved_bytes, void *stream);
+size_t diffattn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int d);
+int diffattn_bwd(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, const void *dy,
+                 const void *saved, void *dq1, void *dk1, void *dq2, void *dk2, void *dv, float *dlambda, int64_t B,
+                 int64_t H, int64_t N, int d, int dtype, float lambda, const float *lambda_heads, int layer,
+                 int causal, void *workspace, size_t workspace_bytes, void *stream);
+
 /* lambda_init(layer) = 0.8 - 0.6 exp(-0.3 (layer - 1)) in double, for layer >= 1 ([U]); NaN for layer < 1. */
 double diffattn_lambda_init(int layer);
 

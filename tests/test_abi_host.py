@@ -160,3 +160,49 @@ def test_decode_heads_validation(lib, case, expect):
 def test_lambda_heads_4_byte_alignment_is_enough(lib):
     # A per-head lambda array only needs 4-byte alignment; this call still fails, but later (on the output alias).
     assert fwd_heads(lib, lh=A[7] + 4, out=A[7]) == E_ALIAS
+
+
+def fwd_train(lib, saved=A[6], saved_bytes=None, out=A[5], B=1, H=2, N=64, d=64, dtype=BF16, lam=0.5, lh=None,
+              layer=1):
+    if saved_bytes is None:
+        saved_bytes = lib.diffattn_train_saved_bytes(B, H, N, d)
+    return lib.diffattn_fwd_train(A[0], A[1], A[2], A[3], A[4], out, B, H, N, d, dtype, lam, lh, layer, 1, saved,
+                                  saved_bytes, None)
+
+
+G = [0x80000000 + 0x10000000 * i for i in range(8)]   # more fake, widely separated device addresses
+
+
+def bwd(lib, dq1=G[0], dlam=G[5], ws=G[6], ws_bytes=None, saved=A[6], B=1, H=2, N=64, d=64, dtype=BF16, lam=0.5,
+        lh=None, layer=1):
+    if ws_bytes is None:
+        ws_bytes = lib.diffattn_bwd_workspace_bytes(B, H, N, d)
+    return lib.diffattn_bwd(A[0], A[1], A[2], A[3], A[4], A[7], saved, dq1, G[1], G[2], G[3], G[4], dlam, B, H, N,
+                            d, dtype, lam, lh, layer, 1, ws, ws_bytes, None)
+
+
+def test_train_sizes(lib):
+    assert lib.diffattn_train_saved_bytes(2, 3, 100, 64) == 2 * 3 * 100 * 1040
+    assert lib.diffattn_train_saved_bytes(2, 3, 100, 8) == 0
+    n = lib.diffattn_bwd_workspace_bytes(2, 3, 100, 64)
+    assert n >= 2 * 3 * 100 * (256 + 16 + 4) and n % 256 == 0
+    assert lib.diffattn_bwd_workspace_bytes(2, 3, 0, 64) == 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(saved=None), E_NULL), (dict(saved_bytes=64), E_WS), (dict(saved=A[6] + 8), E_ALIGN),
+    (dict(saved=A[4]), E_ALIAS), (dict(saved=A[5] + 64), E_ALIAS), (dict(dtype=F32), E_UNSUP), (dict(d=8), E_UNSUP),
+    (dict(N=0), OK), (dict(lam=float("nan")), E_LAMBDA), (dict(layer=-1), E_LAYER), (dict(lh=A[7] + 2), E_ALIGN),
+])
+def test_fwd_train_validation(lib, case, expect):
+    assert fwd_train(lib, **case) == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(dq1=None), E_NULL), (dict(dlam=None), E_NULL), (dict(ws=None), E_WS), (dict(ws_bytes=256), E_WS),
+    (dict(ws=G[6] + 16), E_ALIGN), (dict(dlam=G[5] + 2), E_ALIGN), (dict(dq1=A[0]), E_ALIAS),
+    (dict(dq1=G[1] - 64), E_ALIAS), (dict(dlam=G[6] + 256), E_ALIAS), (dict(ws=A[6] + 1024), E_ALIAS),
+    (dict(dtype=F32), E_UNSUP), (dict(B=0), OK), (dict(lh=G[0] + 4), E_ALIAS),
+])
+def test_bwd_validation(lib, case, expect):
+    assert bwd(lib, **case) == expect

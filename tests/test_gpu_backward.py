@@ -1,0 +1,112 @@
+"""GPU parity of the training forward and the backward pass against the CPU oracles.
+
+The backward oracle is the chain rule of the forward definition in double precision, pinned by finite differences
+of the forward oracle (tests/test_oracle_bwd.py).  The GPU path computes in bf16 with fp32 accumulation: probabilities
+and ds are rounded to bf16 before the matrix products (relative error 2^-9 each), dO is rounded to bf16, and the
+gradients are stored as bf16 (2^-9).  Over the key or query sums these errors partly cancel, so each gradient tensor
+is checked relative to its own scale: max |got - ref| <= 2.5e-2 max |ref| and mean |got - ref| <= 4e-3 max |ref|;
+dlambda within 2e-2 of the largest head's |dlambda|: it is a sum over rows of terms of both signs, each
+carrying the forward's bf16-probability error (2^-9 relative) in o2, and the cancellation enlarges the relative
+error of the total.  The scale has an absolute floor of 1e-2: with a
+single key per row the exact dq is zero and the GPU returns rounding residue.
+"""
+import numpy as np
+import pytest
+
+import diffattn_inputs as di
+import differential_attention_fwd_amd as da
+import oracle
+
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("gpu")]
+
+REL_MAX, REL_MEAN, REL_DLAMBDA = 2.5e-2, 4e-3, 2e-2
+SCALE_FLOOR = 1e-2   # absolute floor of a gradient's scale (one key per row makes dq exactly zero)
+
+
+def torch_mod():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return torch
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def dev_bf16(bits):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def host(t):
+    torch = torch_mod()
+    return di.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+
+
+def run_case(B, H, N, causal, layer, lam, seed):
+    torch = torch_mod()
+    inp = di.prefill_bf16(B, H, N, 64, seed=seed)
+    dy_bits = di.output_grad_bf16(B, H, N, 64, seed=seed)
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    dy = dev_bf16(dy_bits)
+    lam_dev = torch.tensor(np.asarray(lam, dtype=np.float32), device="cuda:0") if np.ndim(lam) else lam
+    out, saved = da.diffattn_fwd_train(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], lam_dev, layer, causal)
+    g = da.diffattn_bwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], dy, saved, lam_dev, layer, causal)
+    torch.cuda.synchronize()
+    f = {k: di.bf16_bits_to_f32(v) for k, v in inp.items()}
+    ref = oracle.diffattn_bwd(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], di.bf16_bits_to_f32(dy_bits),
+                              np.asarray(lam, dtype=np.float32).astype(np.float64), layer, causal)
+    return out, g, ref, dev
+
+
+def check_grads(g, ref, what):
+    for k in ("dq1", "dk1", "dq2", "dk2", "dv"):
+        got = host(g[k])
+        r = ref[k]
+        scale = max(np.abs(r).max(), SCALE_FLOOR)
+        err = np.abs(got - r)
+        say(f"{what} {k}: max-abs {err.max():.3e} mean-abs {err.mean():.3e} (scale {scale:.3e}, "
+            f"rel max {err.max() / scale:.2e}, rel mean {err.mean() / scale:.2e})")
+        assert np.isfinite(got).all(), k
+        assert err.max() <= REL_MAX * scale, f"{what} {k}: max-abs {err.max():.3e} vs scale {scale:.3e}"
+        assert err.mean() <= REL_MEAN * scale, f"{what} {k}: mean-abs {err.mean():.3e} vs scale {scale:.3e}"
+    dl = g["dlambda"].cpu().numpy().astype(np.float64)
+    rel = np.abs(dl - ref["dlambda"]).max() / max(np.abs(ref["dlambda"]).max(), 1e-30)
+    say(f"{what} dlambda: got {dl} ref {ref['dlambda']} rel {rel:.2e}")
+    assert rel <= REL_DLAMBDA
+
+
+def test_training_forward_matches_inference_forward():
+    torch = torch_mod()
+    inp = di.prefill_bf16(2, 2, 300, 64, seed=500)
+    say("case: training forward == forward, B2 H2 N300 causal layer 2")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    a = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.7, 2, True)
+    b, _ = da.diffattn_fwd_train(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.7, 2, True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,H,N,causal,layer,lam", [
+    (1, 2, 64, True, 0, 0.8),
+    (2, 2, 200, True, 3, 0.5),
+    (1, 3, 129, False, 1, [0.1, 0.6, 0.9]),
+    (1, 1, 33, True, 2, 0.3),
+    (1, 2, 1, True, 1, 0.8),
+    (1, 1, 1000, True, 12, 0.7778701),
+    (1, 2, 300, False, 0, 0.25),
+])
+def test_backward_vs_oracle(B, H, N, causal, layer, lam):
+    say(f"case: backward B{B} H{H} N{N} causal={causal} layer={layer} lambda={lam}")
+    _, g, ref, _ = run_case(B, H, N, causal, layer, lam, seed=510 + N)
+    check_grads(g, ref, f"bwd N{N}")
+
+
+def test_backward_deterministic():
+    torch = torch_mod()
+    say("case: backward determinism B1 H2 N257")
+    _, g1, _, dev = run_case(1, 2, 257, True, 2, 0.6, seed=530)
+    _, g2, _, _ = run_case(1, 2, 257, True, 2, 0.6, seed=530)
+    for k in ("dq1", "dk1", "dq2", "dk2", "dv", "dlambda"):
+        assert torch.equal(g1[k], g2[k]), k
