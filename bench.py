@@ -9,6 +9,10 @@ events recorded on the stream it is launched on.  Prints ONE JSON line.
             two P.V products of width 2d), i.e. B*H*N*(N+1)/2 pairs
   roofline  the prefill kernel against the bf16 dense MFMA peak; decode carries its own against HBM bandwidth
   cpu_baseline  the double-precision CPU oracle on the same prefill workload (all rows by default)
+  backward  (not part of the step) the training forward and the backward pass on the prefill workload with a
+            synthetic output gradient, timed separately: 1792 FLOP per unmasked pair on the matrix cores (the
+            dQ kernel recomputes both score maps and dP: 768; the dK/dV kernel recomputes them and forms dV, dK1,
+            dK2: 1024)
 """
 from __future__ import annotations
 
@@ -104,6 +108,50 @@ def cpu_baseline(inp_bits, lam, layer, N, target_rows):
             "seconds": round(dt, 3)}
 
 
+def bench_backward(da, di, stream, p_bits, q1, k1, q2, k2, v, lam, steps):
+    """Training forward + backward on the prefill workload; HIP events on the launch stream."""
+    import numpy as np
+    import torch
+    P = PREFILL
+    dev = q1.device
+    dy = torch.from_numpy(di.output_grad_bf16(P["B"], P["H"], P["N"], P["d"], P["seed"]).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    out = torch.empty_like(v)
+    saved = torch.empty(da.diffattn_train_saved_bytes(P["B"], P["H"], P["N"], P["d"]), dtype=torch.uint8, device=dev)
+    grads = {k: torch.empty_like(t) for k, t in (("dq1", q1), ("dk1", k1), ("dq2", q2), ("dk2", k2), ("dv", v))}
+    grads["dlambda"] = torch.empty(P["H"], dtype=torch.float32, device=dev)
+    ws = torch.empty(da.diffattn_bwd_workspace_bytes(P["B"], P["H"], P["N"], P["d"]), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        da.diffattn_fwd_train(q1, k1, q2, k2, v, lam, P["layer"], True, out=out, saved=saved, stream=stream)
+
+    def bwd():
+        da.diffattn_bwd(q1, k1, q2, k2, v, dy, saved, lam, P["layer"], True, grads=grads, workspace=ws, stream=stream)
+
+    for _ in range(2):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        ev[k][0].record(stream)
+        fwd()
+        ev[k][1].record(stream)
+        bwd()
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    f_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    b_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    pairs = prefill_pairs(P["B"], P["H"], P["N"])
+    flops = pairs * 1792
+    tf = flops / (b_ms * 1e-3) / 1e12
+    return {"workload": "causal B4 H12 N4096 d64 dv128, layer 12, synthetic N(0,1) output gradient",
+            "steps": steps, "fwd_train_ms": round(f_ms, 4), "ms": round(b_ms, 4), "flops_exec": flops,
+            "tflops_exec": round(tf, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +160,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-rows", type=int, default=4 * 12 * 4096,
                     help="oracle row sample size for cpu_baseline (default: every row of the prefill workload)")
+    ap.add_argument("--bwd-steps", type=int, default=10, help="timed backward repetitions (0 skips the backward leg)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -234,6 +283,8 @@ def main():
                                 "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": dec_traffic}},
         "wall_s": round(wall, 3),
     }
+    if args.bwd_steps > 0:
+        result["backward"] = bench_backward(da, di, stream, p_bits, pq1, pk1, pq2, pk2, pv, p_lam, args.bwd_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p_bits, p_lam, P["layer"], P["N"], args.cpu_rows)
     print(json.dumps(result), flush=True)
