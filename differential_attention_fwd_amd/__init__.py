@@ -19,7 +19,8 @@ STATUS = {0: "DIFFATTN_OK", -1: "DIFFATTN_ERR_NULL", -2: "DIFFATTN_ERR_SHAPE", -
           -4: "DIFFATTN_ERR_ALIGN", -5: "DIFFATTN_ERR_LAYER", -6: "DIFFATTN_ERR_LAMBDA",
           -7: "DIFFATTN_ERR_WORKSPACE", -8: "DIFFATTN_ERR_ALIAS", -9: "DIFFATTN_ERR_HIP"}
 EXPORTS = ["diffattn_fwd", "diffattn_fwd_heads", "diffattn_decode", "diffattn_decode_heads",
-           "diffattn_decode_workspace_bytes", "diffattn_train_saved_bytes", "diffattn_fwd_train",
+           "diffattn_decode_workspace_bytes", "diffattn_decode_varlen_workspace_bytes", "diffattn_decode_varlen",
+           "diffattn_train_saved_bytes", "diffattn_fwd_train",
            "diffattn_bwd_workspace_bytes", "diffattn_bwd", "diffattn_lambda_init", "diffattn_status_str",
            "diffattn_abi_version"]
 
@@ -51,6 +52,11 @@ def lib() -> ctypes.CDLL:
     L.diffattn_decode_heads.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, P, c_int, c_int, P,
                                         ctypes.c_size_t, P]
     L.diffattn_decode_heads.restype = c_int
+    L.diffattn_decode_varlen_workspace_bytes.argtypes = [i64, i64, i64, i64, c_int]
+    L.diffattn_decode_varlen_workspace_bytes.restype = ctypes.c_size_t
+    L.diffattn_decode_varlen.argtypes = [P, P, P, P, P, P, i64, i64, i64, i64, P, c_int, c_int, c_float, P, c_int, P,
+                                         ctypes.c_size_t, P]
+    L.diffattn_decode_varlen.restype = c_int
     L.diffattn_train_saved_bytes.argtypes = [i64, i64, i64, c_int]
     L.diffattn_train_saved_bytes.restype = ctypes.c_size_t
     L.diffattn_bwd_workspace_bytes.argtypes = [i64, i64, i64, c_int]
@@ -246,3 +252,39 @@ def diffattn_bwd(q1, k1, q2, k2, v, dy, saved, lam, layer: int, causal: bool, gr
     if st != 0:
         raise DiffAttnError(st, "diffattn_bwd")
     return grads
+
+
+def diffattn_decode_varlen_workspace_bytes(B: int, H: int, T: int, L: int, d: int) -> int:
+    return int(lib().diffattn_decode_varlen_workspace_bytes(int(B), int(H), int(T), int(L), int(d)))
+
+
+def diffattn_decode_varlen(q1, k1, q2, k2, v, lam, layer: int, lens=None, out=None, workspace=None, stream=None):
+    """Variable-length / multi-token decode (bf16, d = 64): q1, q2 [B][H][T][d]; caches [B][H][L][d] and
+    [B][H][L][2d]; lens: None or an int32 GPU tensor of B cache lengths.  Returns out [B][H][T][2d]."""
+    import torch
+    _check_tensors((q1, k1, q2, k2, v))
+    B, H, T, d = q1.shape
+    L = k1.shape[2]
+    if out is None:
+        out = torch.empty((B, H, T, 2 * d), dtype=q1.dtype, device=q1.device)
+    for t, shp in ((q2, (B, H, T, d)), (k1, (B, H, L, d)), (k2, (B, H, L, d)), (v, (B, H, L, 2 * d)),
+                   (out, (B, H, T, 2 * d))):
+        if tuple(t.shape) != tuple(shp) or t.dtype != q1.dtype:
+            raise ValueError(f"shape/dtype mismatch: {tuple(t.shape)} {t.dtype}, expected {tuple(shp)} {q1.dtype}")
+    if lens is not None:
+        if lens.dtype != torch.int32 or tuple(lens.shape) != (B,) or lens.device != q1.device:
+            raise ValueError(f"lens must be an int32 tensor of shape ({B},) on {q1.device}")
+        _check_tensors((lens,))
+    need = diffattn_decode_varlen_workspace_bytes(B, H, T, L, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q1.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lam_f, lam_p = _lambda_args(lam, H, q1.device)
+    st = lib().diffattn_decode_varlen(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
+                                      out.data_ptr(), B, H, T, L, lens.data_ptr() if lens is not None else None, d,
+                                      _dtype_code(q1), lam_f, lam_p, int(layer), ws_ptr, ws_bytes,
+                                      _stream_handle(stream, q1.device))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_decode_varlen")
+    return out

@@ -11,6 +11,12 @@
 //     lanes per 256-byte row) and accumulates both maps' partial outputs in fp32.  The split's state
 //     (m, l, O[128]) per map goes to the workspace.
 //   * decode_merge: one wave per head merges the splits by log-sum-exp and applies the epilogue.
+//   * Ragged caches: with a per-sequence length array, sequence b uses the first lens[b] cache rows (the cache is
+//     padded to L rows); splits past its end write an empty state (max -inf, sum 0), which the merge weighs by 0.
+//   * decode_multi_split: T > 1 new tokens per sequence (T <= 16), query t at cache position len - T + t seeing
+//     keys up to its own position.  The T queries sit in LDS; the split's scores for all of them are kept in LDS
+//     (T x keys <= 2048 per map); waves take queries t = wave, wave + 4, ... for the softmax and value passes, so
+//     V rows are re-read per query from cache rather than from HBM.
 #include "launch.h"
 
 namespace diffattn {
@@ -25,6 +31,8 @@ constexpr int DV = 128;
 constexpr int THREADS = 256;
 constexpr int MAX_SPLIT_KEYS = 1024;          // keys per split (scores of both maps fit in 8 KiB of LDS)
 constexpr int PART_FLOATS = 4 + 2 * DV;       // m1, l1, m2, l2, O1[128], O2[128]
+constexpr int MAX_T = 16;                     // new tokens per sequence in multi-token decode
+constexpr int MULTI_SCORES = 2048;            // T x split keys per map held in LDS by the multi-token kernel
 constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
@@ -71,13 +79,28 @@ __host__ __device__ inline SplitPlan plan_splits(int64_t BH, int64_t L) {
     return SplitPlan{(int)s, (int)keys};
 }
 
+// Cache length of sequence b: lens[b] clamped to [lo, L], or L without a length array.
+__device__ __forceinline__ int seq_len(const int* lens, int b, int lo, int L) {
+    return lens ? min(max(lens[b], lo), L) : L;
+}
+
+__device__ __forceinline__ void write_empty(float* dst, int tid) {
+    if (tid == 0) {
+        dst[0] = -INFINITY;
+        dst[1] = 0.f;
+        dst[2] = -INFINITY;
+        dst[3] = 0.f;
+    }
+    for (int k = tid; k < 2 * DV; k += THREADS) dst[4 + k] = 0.f;
+}
+
 __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* __restrict__ gq1,
                                                                const uint16_t* __restrict__ gk1,
                                                                const uint16_t* __restrict__ gq2,
                                                                const uint16_t* __restrict__ gk2,
                                                                const uint16_t* __restrict__ gv,
                                                                float* __restrict__ ws, int L, int splits,
-                                                               int split_keys) {
+                                                               int split_keys, const int* __restrict__ lens, int H) {
     __shared__ float sc1[MAX_SPLIT_KEYS], sc2[MAX_SPLIT_KEYS];
     __shared__ float red[4][8];
     __shared__ float part[4][2 * DV];
@@ -86,7 +109,11 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     const int bh = blockIdx.x / splits;
     const int sp = blockIdx.x % splits;
     const int j0 = sp * split_keys;
-    const int n = min(L, j0 + split_keys) - j0;
+    const int n = min(seq_len(lens, bh / H, 1, L), j0 + split_keys) - j0;
+    if (n <= 0) {   // past this sequence's end (ragged caches only)
+        write_empty(ws + ((size_t)bh * splits + sp) * PART_FLOATS, tid);
+        return;
+    }
     const float c = LOG2E * 0.125f;  // log2(e) / sqrt(64)
 
     const uint16_t* k1 = gk1 + ((size_t)bh * L + j0) * D;
@@ -100,7 +127,6 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     const u32x4 qb = *(const u32x4*)(gq2 + (size_t)bh * D + ch * 8);
     float mx1 = -INFINITY, mx2 = -INFINITY;
     const int r_in = wave * 8 + (lane >> 3);
-#pragma unroll 4
     for (int r0 = 0; r0 < n; r0 += 32) {
         const int r = r0 + r_in;
         const int rr = min(r, n - 1);
@@ -189,11 +215,14 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
 }
 
 // One wave per head: lane owns channels 2*lane and 2*lane + 1.
+// Work item = (head, query): blockIdx.x = bh * T + t.  Every query sees at least one key, so some split is
+// non-empty and the merged maxima are finite.
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ ws, uint16_t* __restrict__ gout,
-                                                          int splits, Epilogue ep) {
-    const int bh = blockIdx.x;
+                                                          int splits, int T, Epilogue ep) {
+    const int item = blockIdx.x;
+    const int bh = item / T;
     const int lane = threadIdx.x;
-    const float* part = ws + (size_t)bh * splits * PART_FLOATS;
+    const float* part = ws + (size_t)item * splits * PART_FLOATS;
     float M1 = -INFINITY, M2 = -INFINITY;
     for (int s = 0; s < splits; ++s) {
         M1 = fmaxf(M1, part[s * PART_FLOATS + 0]);
@@ -222,30 +251,179 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
     }
     const unsigned w = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)ya) |
                        ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)yb) << 16);
-    *(unsigned*)(gout + (size_t)bh * DV + 2 * lane) = w;
+    *(unsigned*)(gout + (size_t)item * DV + 2 * lane) = w;
+}
+
+// Multi-token split: one workgroup per (head, key split), all T queries of the head.
+__global__ __launch_bounds__(THREADS) void decode_multi_split_kernel(const uint16_t* __restrict__ gq1,
+                                                                     const uint16_t* __restrict__ gk1,
+                                                                     const uint16_t* __restrict__ gq2,
+                                                                     const uint16_t* __restrict__ gk2,
+                                                                     const uint16_t* __restrict__ gv,
+                                                                     float* __restrict__ ws, int L, int T, int splits,
+                                                                     int split_keys, const int* __restrict__ lens,
+                                                                     int H) {
+    __shared__ float sc[2][MULTI_SCORES];                    // [map][t * split_keys + r]
+    __shared__ __attribute__((aligned(16))) uint16_t qs[2][MAX_T][D];
+    __shared__ float stat[MAX_T][4];                         // m1, l1, m2, l2 per query
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int bh = blockIdx.x / splits;
+    const int sp = blockIdx.x % splits;
+    const int Lb = seq_len(lens, bh / H, T, L);
+    const int j0 = sp * split_keys;
+    const int n = min(Lb, j0 + split_keys) - j0;
+    const int pos0 = Lb - T;                                 // cache position of query 0
+    const float c = LOG2E * 0.125f;
+    float* dst0 = ws + (size_t)bh * T * splits * PART_FLOATS;
+    if (n <= 0) {
+        for (int t = 0; t < T; ++t) write_empty(dst0 + ((size_t)t * splits + sp) * PART_FLOATS, tid);
+        return;
+    }
+    for (int k = tid; k < T * D / 8; k += THREADS) {        // stage the T queries (16-byte chunks)
+        const int t = k / (D / 8), chunk = k % (D / 8);
+        *(u32x4*)&qs[0][t][chunk * 8] = *(const u32x4*)(gq1 + ((size_t)bh * T + t) * D + chunk * 8);
+        *(u32x4*)&qs[1][t][chunk * 8] = *(const u32x4*)(gq2 + ((size_t)bh * T + t) * D + chunk * 8);
+    }
+    __syncthreads();
+
+    const uint16_t* k1 = gk1 + ((size_t)bh * L + j0) * D;
+    const uint16_t* k2 = gk2 + ((size_t)bh * L + j0) * D;
+    const uint16_t* v = gv + ((size_t)bh * L + j0) * DV;
+    // Phase 1: scores of every query for the split's keys (masked keys -> -inf).
+    const int ch = lane & 7;
+    const int r_in = wave * 8 + (lane >> 3);
+    for (int r0 = 0; r0 < n; r0 += 32) {
+        const int r = r0 + r_in;
+        const int rr = min(r, n - 1);
+        const u32x4 ka = *(const u32x4*)(k1 + (size_t)rr * D + ch * 8);
+        const u32x4 kb = *(const u32x4*)(k2 + (size_t)rr * D + ch * 8);
+        for (int t = 0; t < T; ++t) {
+            float s1 = dot8(*(const u32x4*)&qs[0][t][ch * 8], ka, 0.f);
+            float s2 = dot8(*(const u32x4*)&qs[1][t][ch * 8], kb, 0.f);
+            s1 += __shfl_xor(s1, 1); s2 += __shfl_xor(s2, 1);
+            s1 += __shfl_xor(s1, 2); s2 += __shfl_xor(s2, 2);
+            s1 += __shfl_xor(s1, 4); s2 += __shfl_xor(s2, 4);
+            if (r < n && ch == 0) {
+                const bool vis = j0 + r <= pos0 + t;
+                sc[0][t * split_keys + r] = vis ? s1 * c : -INFINITY;
+                sc[1][t * split_keys + r] = vis ? s2 * c : -INFINITY;
+            }
+        }
+    }
+    __syncthreads();
+    // Phase 2: per query (wave w takes t = w, w + 4, ...), the split's max and sum per map; probabilities in place.
+    for (int t = wave; t < T; t += 4) {
+        float* s1 = &sc[0][t * split_keys];
+        float* s2 = &sc[1][t * split_keys];
+        float m1 = -INFINITY, m2 = -INFINITY;
+        for (int r = lane; r < n; r += 64) { m1 = fmaxf(m1, s1[r]); m2 = fmaxf(m2, s2[r]); }
+        m1 = wave_max(m1);
+        m2 = wave_max(m2);
+        float z1 = 0.f, z2 = 0.f;
+        if (m1 != -INFINITY) {   // the split holds at least one visible key of query t (both maps alike)
+            for (int r = lane; r < n; r += 64) {
+                const float p1 = __builtin_amdgcn_exp2f(s1[r] - m1), p2 = __builtin_amdgcn_exp2f(s2[r] - m2);
+                s1[r] = p1;
+                s2[r] = p2;
+                z1 += p1;
+                z2 += p2;
+            }
+        }
+        z1 = wave_sum(z1);
+        z2 = wave_sum(z2);
+        if (lane == 0) {
+            stat[t][0] = m1;
+            stat[t][1] = z1;
+            stat[t][2] = m2;
+            stat[t][3] = z2;
+        }
+    }
+    // Phase 3: partial outputs per query; lane takes channels 8 (lane % 16) .. + 7 of row slot lane / 16.
+    const int vc = lane & 15, slot = lane >> 4;
+    for (int t = wave; t < T; t += 4) {
+        float* dst = dst0 + ((size_t)t * splits + sp) * PART_FLOATS;
+        const float m1 = stat[t][0];   // written by this wave above
+        float a1[8], a2[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { a1[k] = 0.f; a2[k] = 0.f; }
+        if (m1 != -INFINITY) {
+            const float* p1s = &sc[0][t * split_keys];
+            const float* p2s = &sc[1][t * split_keys];
+            for (int r = slot; r < n; r += 4) {
+                const u32x4 w = *(const u32x4*)(v + (size_t)r * DV + vc * 8);
+                const float p1 = p1s[r], p2 = p2s[r];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float lo = bf_lo(w[k]), hi = bf_hi(w[k]);
+                    a1[2 * k] = __builtin_fmaf(p1, lo, a1[2 * k]);
+                    a1[2 * k + 1] = __builtin_fmaf(p1, hi, a1[2 * k + 1]);
+                    a2[2 * k] = __builtin_fmaf(p2, lo, a2[2 * k]);
+                    a2[2 * k + 1] = __builtin_fmaf(p2, hi, a2[2 * k + 1]);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            a1[k] += __shfl_xor(a1[k], 16);
+            a1[k] += __shfl_xor(a1[k], 32);
+            a2[k] += __shfl_xor(a2[k], 16);
+            a2[k] += __shfl_xor(a2[k], 32);
+        }
+        if (lane < 16) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                dst[4 + vc * 8 + k] = a1[k];
+                dst[4 + DV + vc * 8 + k] = a2[k];
+            }
+        }
+        if (lane == 0) {
+            dst[0] = stat[t][0];
+            dst[1] = stat[t][1];
+            dst[2] = stat[t][2];
+            dst[3] = stat[t][3];
+        }
+    }
+}
+
+// Split plan of a call: the single-token plan, with splits shortened for T > 1 so that T x split keys fit in LDS.
+SplitPlan plan_call(int64_t BH, int64_t L, int T) {
+    SplitPlan p = plan_splits(BH, L);
+    if (T > 1) {
+        int cap = (MULTI_SCORES / T) & ~31;
+        if (p.split_keys > cap) {
+            p.split_keys = cap;
+            p.splits = (int)((L + cap - 1) / cap);
+        }
+    }
+    return p;
 }
 
 }  // namespace
 
-size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L) {
-    if (BH <= 0 || L <= 0) return 0;
-    const SplitPlan p = plan_splits(BH, L);
-    return (size_t)BH * (size_t)p.splits * PART_FLOATS * sizeof(float);
+size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L, int T) {
+    if (BH <= 0 || L <= 0 || T < 1 || T > MAX_T) return 0;
+    const SplitPlan p = plan_call(BH, L, T);
+    return (size_t)BH * (size_t)T * (size_t)p.splits * PART_FLOATS * sizeof(float);
 }
 
 hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
-                                  const uint16_t* v, uint16_t* out, int64_t BH, int64_t L, Epilogue ep,
-                                  void* workspace, hipStream_t stream) {
-    const SplitPlan p = plan_splits(BH, L);
+                                  const uint16_t* v, uint16_t* out, int64_t BH, int64_t H, int64_t L, int T,
+                                  const int* lens, Epilogue ep, void* workspace, hipStream_t stream) {
+    const SplitPlan p = plan_call(BH, L, T);
     const int64_t blocks = BH * (int64_t)p.splits;
-    if (blocks > 0x7fffffff || BH > 0x7fffffff) return hipErrorInvalidValue;
+    if (blocks > 0x7fffffff || BH * T > 0x7fffffff || T < 1 || T > MAX_T) return hipErrorInvalidValue;
     float* ws = (float*)workspace;
-    hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1, q2, k2, v, ws,
-                       (int)L, p.splits, p.split_keys);
+    if (T == 1)
+        hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1, q2, k2, v,
+                           ws, (int)L, p.splits, p.split_keys, lens, (int)H);
+    else
+        hipLaunchKernelGGL(decode_multi_split_kernel, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1, q2,
+                           k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)BH), dim3(64), 0, stream, (const float*)ws, out, p.splits,
-                       ep);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(BH * T)), dim3(64), 0, stream, (const float*)ws, out,
+                       p.splits, T, ep);
     return hipGetLastError();
 }
 

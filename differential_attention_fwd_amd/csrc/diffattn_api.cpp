@@ -152,7 +152,15 @@ size_t diffattn_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
     int64_t BH;
     if (B < 0 || H < 0 || L <= 0 || L > DIFFATTN_MAX_LEN || d != 64 || !mul_ok(B, H, &BH) || BH > INT32_MAX)
         return 0;
-    return diffattn::decode_bf16_workspace_bytes(BH, L);
+    return diffattn::decode_bf16_workspace_bytes(BH, L, 1);
+}
+
+size_t diffattn_decode_varlen_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t L, int d) {
+    int64_t BH;
+    if (B < 0 || H < 0 || T < 1 || T > DIFFATTN_MAX_NEW_TOKENS || L < T || L > DIFFATTN_MAX_LEN || d != 64 ||
+        !mul_ok(B, H, &BH) || BH > INT32_MAX)
+        return 0;
+    return diffattn::decode_bf16_workspace_bytes(BH, L, (int)T);
 }
 
 }  // extern "C"
@@ -160,18 +168,20 @@ size_t diffattn_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
 namespace {
 
 int decode_impl(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out, int64_t B,
-                int64_t H, int64_t L, int d, int dtype, float lambda, const float* lambda_heads, bool per_head,
-                int layer, void* workspace, size_t workspace_bytes, void* stream) {
-    if (B < 0 || H < 0 || L < 0) return DIFFATTN_ERR_SHAPE;
-    if (L == 0 || L > DIFFATTN_MAX_LEN) return DIFFATTN_ERR_SHAPE;
+                int64_t H, int64_t T, int64_t L, const int32_t* lens, bool varlen, int d, int dtype, float lambda,
+                const float* lambda_heads, bool per_head, int layer, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    if (B < 0 || H < 0 || L < 0 || T < 1) return DIFFATTN_ERR_SHAPE;
+    if (L == 0 || L > DIFFATTN_MAX_LEN || T > DIFFATTN_MAX_NEW_TOKENS || L < T) return DIFFATTN_ERR_SHAPE;
     int st = check_dtype_d(dtype, d);
     if (st) return st;
+    if (varlen && dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
     Epilogue ep;
     st = make_epilogue(per_head ? 0.0f : lambda, layer, &ep);
     if (st) return st;
-    int64_t BH, q_elems, kv_rows, k_elems, v_elems;
-    if (!mul_ok(B, H, &BH) || BH > INT32_MAX || !mul_ok(BH, d, &q_elems) || !mul_ok(BH, L, &kv_rows) ||
-        !mul_ok(kv_rows, d, &k_elems) || !mul_ok(kv_rows, 2 * (int64_t)d, &v_elems))
+    int64_t BH, q_rows, q_elems, kv_rows, k_elems, v_elems;
+    if (!mul_ok(B, H, &BH) || BH > INT32_MAX || !mul_ok(BH, T, &q_rows) || !mul_ok(q_rows, d, &q_elems) ||
+        !mul_ok(BH, L, &kv_rows) || !mul_ok(kv_rows, d, &k_elems) || !mul_ok(kv_rows, 2 * (int64_t)d, &v_elems))
         return DIFFATTN_ERR_SHAPE;
     if (BH == 0) return DIFFATTN_OK;
     if (!q1 || !k1 || !q2 || !k2 || !v || !out) return DIFFATTN_ERR_NULL;
@@ -192,6 +202,11 @@ int decode_impl(const void* q1, const void* k1, const void* q2, const void* k2, 
         ep.lambda_heads = lambda_heads;
         ep.heads = (int)H;
     }
+    const Span ls{(uintptr_t)lens, (uintptr_t)lens + (size_t)B * sizeof(int32_t)};
+    if (lens) {
+        if (((uintptr_t)lens & 3u) != 0) return DIFFATTN_ERR_ALIGN;
+        if (overlaps(ls, o)) return DIFFATTN_ERR_ALIAS;
+    }
 
     hipStream_t s = (hipStream_t)stream;
     if (dtype == DIFFATTN_F32)  // exact fp32 path: one query row per head at the end of the cache
@@ -199,7 +214,7 @@ int decode_impl(const void* q1, const void* k1, const void* q2, const void* k2, 
                                                     (const float*)k2, (const float*)v, (float*)out, BH, 1, L, d, 1, ep,
                                                     s));
 
-    const size_t need = diffattn::decode_bf16_workspace_bytes(BH, L);
+    const size_t need = diffattn::decode_bf16_workspace_bytes(BH, L, (int)T);
     if (!workspace || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return DIFFATTN_ERR_ALIGN;
     const Span w{(uintptr_t)workspace, (uintptr_t)workspace + need};
@@ -208,9 +223,10 @@ int decode_impl(const void* q1, const void* k1, const void* q2, const void* k2, 
         if (overlaps(w, sp)) return DIFFATTN_ERR_ALIAS;
     if (per_head && overlaps(w, Span{(uintptr_t)lambda_heads, (uintptr_t)lambda_heads + (size_t)H * sizeof(float)}))
         return DIFFATTN_ERR_ALIAS;
+    if (lens && overlaps(w, ls)) return DIFFATTN_ERR_ALIAS;
     return hip_status(diffattn::launch_decode_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
-                                                       (const uint16_t*)k2, (const uint16_t*)v, (uint16_t*)out, BH, L,
-                                                       ep, workspace, s));
+                                                       (const uint16_t*)k2, (const uint16_t*)v, (uint16_t*)out, BH, H,
+                                                       L, (int)T, lens, ep, workspace, s));
 }
 
 }  // namespace
@@ -221,16 +237,24 @@ int diffattn_decode(const void* q1, const void* k1, const void* q2, const void* 
                     int64_t B, int64_t H, int64_t L, int d, int dtype, float lambda, int layer, int causal,
                     void* workspace, size_t workspace_bytes, void* stream) {
     (void)causal;  // the single query is the last position: every cached key is visible either way
-    return decode_impl(q1, k1, q2, k2, v, out, B, H, L, d, dtype, lambda, nullptr, false, layer, workspace,
-                       workspace_bytes, stream);
+    return decode_impl(q1, k1, q2, k2, v, out, B, H, 1, L, nullptr, false, d, dtype, lambda, nullptr, false, layer,
+                       workspace, workspace_bytes, stream);
 }
 
 int diffattn_decode_heads(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
                           int64_t B, int64_t H, int64_t L, int d, int dtype, const float* lambda_heads, int layer,
                           int causal, void* workspace, size_t workspace_bytes, void* stream) {
     (void)causal;
-    return decode_impl(q1, k1, q2, k2, v, out, B, H, L, d, dtype, 0.0f, lambda_heads, true, layer, workspace,
-                       workspace_bytes, stream);
+    return decode_impl(q1, k1, q2, k2, v, out, B, H, 1, L, nullptr, false, d, dtype, 0.0f, lambda_heads, true, layer,
+                       workspace, workspace_bytes, stream);
+}
+
+int diffattn_decode_varlen(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
+                           int64_t B, int64_t H, int64_t T, int64_t L, const int32_t* lens, int d, int dtype,
+                           float lambda, const float* lambda_heads, int layer, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return decode_impl(q1, k1, q2, k2, v, out, B, H, T, L, lens, true, d, dtype, lambda_heads ? 0.0f : lambda,
+                       lambda_heads, lambda_heads != nullptr, layer, workspace, workspace_bytes, stream);
 }
 
 

@@ -50,9 +50,11 @@ hipError_t launch_attn_f32(const float* q1, const float* k1, const float* q2, co
                            hipStream_t stream);
 
 // bf16 decode, d = 64: split kernel writing per-split partial states, then the merge + epilogue kernel.
-size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L);
+// T new tokens per (b, h) (1 <= T <= 16; queries [BH][T][d], out [BH][T][2d]); caches [BH][L][...]; lens: optional
+// device array of B cache lengths (clamped on the device to [T, L]), with b = bh / H.
+size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L, int T);
 hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
-                                  const uint16_t* v, uint16_t* out, int64_t BH, int64_t L, Epilogue ep,
-                                  void* workspace, hipStream_t stream);
+                                  const uint16_t* v, uint16_t* out, int64_t BH, int64_t H, int64_t L, int T,
+                                  const int* lens, Epilogue ep, void* workspace, hipStream_t stream);
 
 }  // namespace diffattn

@@ -62,6 +62,9 @@ enum diffattn_status {
  * address a head through a 32-bit buffer offset. */
 #define DIFFATTN_MAX_LEN (1 << 23)
 
+/* Most new tokens per sequence in one diffattn_decode_varlen call. */
+#define DIFFATTN_MAX_NEW_TOKENS 16
+
 /*
  * Prefill (square, Nq = Nk = N): the whole forward pass for B x H heads of N tokens.
  *   q1,k1,q2,k2: [B][H][N][d]; v, out: [B][H][N][2d]; element type `dtype`.
@@ -107,6 +110,25 @@ int diffattn_fwd_heads(const void *q1, const void *k1, const void *q2, const voi
 int diffattn_decode_heads(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
                           int64_t B, int64_t H, int64_t L, int d, int dtype, const float *lambda_heads, int layer,
                           int causal, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Variable-length and multi-token decode (bf16, d = 64).  Each sequence b has a cache of lens[b] valid rows in a
+ * cache padded to L rows, and T new tokens (1 <= T <= DIFFATTN_MAX_NEW_TOKENS) that are already the last T of those
+ * rows: new token t is position lens[b] - T + t and sees the keys up to and including its own position (the causal
+ * reading of the worked example applied to a cache, as for diffattn_decode).
+ *   q1, q2: [B][H][T][d];  k1, k2: [B][H][L][d];  v: [B][H][L][2d];  out: [B][H][T][2d].
+ *   lens: DEVICE array of B int32 values, 4-byte aligned, or NULL (every sequence uses all L rows).  Each value is
+ *         clamped on the device to [T, L]; it is read on `stream` and must not overlap out or the workspace.
+ *   lambda / lambda_heads: as for diffattn_fwd_train (lambda_heads NULL = one lambda for all heads).
+ *   workspace: >= diffattn_decode_varlen_workspace_bytes(B, H, T, L, d) bytes, 16-byte aligned.
+ * Errors as for diffattn_decode; T < 1, T > 16 or L < T is DIFFATTN_ERR_SHAPE; fp32 is DIFFATTN_ERR_UNSUPPORTED.
+ * With T = 1 and lens NULL the result equals diffattn_decode (same kernels).
+ */
+size_t diffattn_decode_varlen_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t L, int d);
+int diffattn_decode_varlen(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
+                           int64_t B, int64_t H, int64_t T, int64_t L, const int32_t *lens, int d, int dtype,
+                           float lambda, const float *lambda_heads, int layer, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * Training: a forward that keeps what the backward pass needs, and the backward pass.  The pages describe no

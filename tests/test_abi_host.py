@@ -206,3 +206,27 @@ def test_fwd_train_validation(lib, case, expect):
 ])
 def test_bwd_validation(lib, case, expect):
     assert bwd(lib, **case) == expect
+
+
+def dec_var(lib, T=4, L=100, lens=A[7], out=A[5], ws=A[6], ws_bytes=None, B=2, H=2, d=64, dtype=BF16, lam=0.8):
+    if ws_bytes is None:
+        ws_bytes = lib.diffattn_decode_varlen_workspace_bytes(B, H, T, L, d)
+    return lib.diffattn_decode_varlen(A[0], A[1], A[2], A[3], A[4], out, B, H, T, L, lens, d, dtype, lam, None, 1,
+                                      ws, ws_bytes, None)
+
+
+def test_varlen_workspace_sizes(lib):
+    one = lib.diffattn_decode_varlen_workspace_bytes(64, 16, 1, 8192, 64)
+    assert one == lib.diffattn_decode_workspace_bytes(64, 16, 8192, 64)
+    assert lib.diffattn_decode_varlen_workspace_bytes(2, 2, 16, 1000, 64) % (2 * 2 * 16 * 1040) == 0
+    for bad in ((2, 2, 0, 100, 64), (2, 2, 17, 100, 64), (2, 2, 8, 7, 64), (2, 2, 4, 100, 8)):
+        assert lib.diffattn_decode_varlen_workspace_bytes(*bad) == 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(T=0), E_SHAPE), (dict(T=17), E_SHAPE), (dict(T=8, L=7), E_SHAPE), (dict(dtype=F32), E_UNSUP),
+    (dict(lens=A[7] + 2), E_ALIGN), (dict(lens=A[5]), E_ALIAS), (dict(lens=A[6] + 16), E_ALIAS),
+    (dict(ws=None), E_WS), (dict(ws_bytes=64), E_WS), (dict(B=0), OK), (dict(lens=None, out=A[1]), E_ALIAS),
+])
+def test_decode_varlen_validation(lib, case, expect):
+    assert dec_var(lib, **case) == expect

@@ -347,3 +347,86 @@ def test_uniform_lambda_heads_equal_scalar_lambda():
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(c.view(torch.int16), e.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Variable-length and multi-token decode (diffattn_decode_varlen)
+# ---------------------------------------------------------------------------------------------------------------
+
+def varlen_reference(f, T, L, lens, lam, layer):
+    """Oracle: sequence b's cache cut to its clamped length, its T new tokens as the last T query rows (end-aligned
+    causal mask)."""
+    B, H = f["k1"].shape[:2]
+    out = np.zeros((B, H, T, 128))
+    for b in range(B):
+        Lb = L if lens is None else min(max(int(lens[b]), T), L)
+        sl = (slice(b, b + 1), slice(None), slice(0, Lb))
+        out[b] = oracle.diffattn(f["q1"][b:b + 1], f["k1"][sl], f["q2"][b:b + 1], f["k2"][sl], f["v"][sl], lam,
+                                 layer, True)[0]
+    return out
+
+
+def varlen_inputs(B, H, T, L, seed):
+    kv = di.decode_bf16(B, H, L, 64, seed=seed)
+    q = di.prefill_bf16(B, H, T, 64, seed=seed + 1)
+    return {"q1": q["q1"], "q2": q["q2"], "k1": kv["k1"], "k2": kv["k2"], "v": kv["v"]}
+
+
+@pytest.mark.parametrize("B,H,T,L,lens,layer", [
+    (3, 2, 1, 2000, [1, 777, 2000], 1),
+    (2, 2, 4, 300, None, 0),
+    (3, 2, 16, 1000, [16, 501, 1000], 2),
+    (2, 1, 5, 5, None, 1),
+    (2, 3, 7, 4500, [4500, 9], 3),
+    (1, 2, 2, 20000, [19999], 1),
+])
+def test_decode_varlen_vs_oracle(B, H, T, L, lens, layer):
+    torch = torch_mod()
+    inp = varlen_inputs(B, H, T, L, seed=600 + T + L)
+    say(f"case: decode varlen B{B} H{H} T{T} L{L} lens={lens} layer={layer}")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    ldev = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda:0")
+    out = da.diffattn_decode_varlen(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.8, layer, lens=ldev)
+    torch.cuda.synchronize()
+    ref = varlen_reference(widen(inp), T, L, lens, float(np.float32(0.8)), layer)
+    check_bf16(host_bf16(out), ref, f"decode varlen T{T} L{L}")
+
+
+def test_decode_varlen_per_head_lambda():
+    torch = torch_mod()
+    inp = varlen_inputs(2, 3, 3, 640, seed=650)
+    say("case: decode varlen per-head lambda B2 H3 T3 L640 lens [640, 100]")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    ldev = torch.tensor([640, 100], dtype=torch.int32, device="cuda:0")
+    out = da.diffattn_decode_varlen(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], dev_lam(LAM_HEADS), 1,
+                                    lens=ldev)
+    torch.cuda.synchronize()
+    ref = varlen_reference(widen(inp), 3, 640, [640, 100], LAM_HEADS.astype(np.float64), 1)
+    check_bf16(host_bf16(out), ref, "decode varlen per-head")
+
+
+def test_decode_varlen_single_token_equals_decode():
+    """T = 1 without lengths runs the decode kernels: bit-identical to diffattn_decode."""
+    torch = torch_mod()
+    inp = di.decode_bf16(2, 2, 3000, 64, seed=660)
+    say("case: decode varlen T1 == decode, B2 H2 L3000")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    a = da.diffattn_decode(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.8, 1)
+    b = da.diffattn_decode_varlen(dev["q1"][:, :, None], dev["k1"], dev["q2"][:, :, None], dev["k2"], dev["v"], 0.8,
+                                  1)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b[:, :, 0].contiguous().view(torch.int16))
+
+
+def test_decode_varlen_matches_prefill_rows():
+    """T new tokens at the end of a full cache equal the causal prefill's last T rows."""
+    torch = torch_mod()
+    B, H, N, T = 1, 2, 700, 9
+    inp = di.prefill_bf16(B, H, N, 64, seed=670)
+    say("case: decode varlen T9 == prefill last 9 rows, N700")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    pre = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.8, 1, True)
+    dec = da.diffattn_decode_varlen(dev["q1"][:, :, N - T:].contiguous(), dev["k1"],
+                                    dev["q2"][:, :, N - T:].contiguous(), dev["k2"], dev["v"], 0.8, 1)
+    torch.cuda.synchronize()
+    assert np.abs(host_bf16(pre)[:, :, N - T:] - host_bf16(dec)).max() <= 2e-2
