@@ -9,6 +9,8 @@ events recorded on the stream it is launched on.  Prints ONE JSON line.
             two P.V products of width 2d), i.e. B*H*N*(N+1)/2 pairs
   roofline  the prefill kernel against the bf16 dense MFMA peak; decode carries its own against HBM bandwidth
   cpu_baseline  the double-precision CPU oracle on the same prefill workload (all rows by default)
+  decode_multi  (not part of the step) multi-token decode, 4 new tokens per sequence against ragged caches of
+            4096..8192 rows at B64 H16: GB/s of the valid cache rows read
   backward  (not part of the step) the training forward and the backward pass on the prefill workload with a
             synthetic output gradient, timed separately: 1792 FLOP per unmasked pair on the matrix cores (the
             dQ kernel recomputes both score maps and dP: 768; the dK/dV kernel recomputes them and forms dV, dK1,
@@ -108,6 +110,44 @@ def cpu_baseline(inp_bits, lam, layer, N, target_rows):
             "seconds": round(dt, 3)}
 
 
+def bench_decode_multi(da, stream, k1, k2, v, Dc, steps, T=4):
+    """Multi-token decode against the decode workload's caches with seeded ragged lengths in [L/2, L]."""
+    import numpy as np
+    import torch
+    dev = k1.device
+    B, H, L, d = Dc["B"], Dc["H"], Dc["L"], Dc["d"]
+    rng = np.random.default_rng(Dc["seed"])
+    lens_np = rng.integers(L // 2, L + 1, size=B).astype(np.int32)
+    lens = torch.from_numpy(lens_np).to(dev)
+    g = torch.Generator(device=dev).manual_seed(Dc["seed"])
+    q1 = torch.randn(B, H, T, d, device=dev, generator=g).to(torch.bfloat16)
+    q2 = torch.randn(B, H, T, d, device=dev, generator=g).to(torch.bfloat16)
+    out = torch.empty(B, H, T, 2 * d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(da.diffattn_decode_varlen_workspace_bytes(B, H, T, L, d), dtype=torch.uint8, device=dev)
+
+    def run():
+        da.diffattn_decode_varlen(q1, k1, q2, k2, v, Dc["lam"], Dc["layer"], lens=lens, out=out, workspace=ws,
+                                  stream=stream)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = int(lens_np.sum()) * H * (2 * d * 2 + 2 * d * 2) + 2 * (2 * B * H * T * d + B * H * T * 2 * d)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"decode B{B} H{H} T{T} new tokens, cache lengths {int(lens_np.min())}..{int(lens_np.max())} "
+                        f"(seeded uniform in [{L // 2}, {L}]), d64 dv128", "steps": steps, "ms": round(ms, 4),
+            "bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+
+
 def bench_backward(da, di, stream, p_bits, q1, k1, q2, k2, v, lam, steps):
     """Training forward + backward on the prefill workload; HIP events on the launch stream."""
     import numpy as np
@@ -161,6 +201,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4 * 12 * 4096,
                     help="oracle row sample size for cpu_baseline (default: every row of the prefill workload)")
     ap.add_argument("--bwd-steps", type=int, default=10, help="timed backward repetitions (0 skips the backward leg)")
+    ap.add_argument("--multi-steps", type=int, default=10,
+                    help="timed multi-token decode repetitions (0 skips that leg)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -283,6 +325,8 @@ def main():
                                 "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": dec_traffic}},
         "wall_s": round(wall, 3),
     }
+    if args.multi_steps > 0:
+        result["decode_multi"] = bench_decode_multi(da, stream, dk1, dk2, dv, Dc, args.multi_steps)
     if args.bwd_steps > 0:
         result["backward"] = bench_backward(da, di, stream, p_bits, pq1, pk1, pq2, pk2, pv, p_lam, args.bwd_steps)
     if not args.no_cpu_baseline:
