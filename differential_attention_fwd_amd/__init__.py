@@ -18,7 +18,7 @@ DIFFATTN_F32 = 1
 STATUS = {0: "DIFFATTN_OK", -1: "DIFFATTN_ERR_NULL", -2: "DIFFATTN_ERR_SHAPE", -3: "DIFFATTN_ERR_UNSUPPORTED",
           -4: "DIFFATTN_ERR_ALIGN", -5: "DIFFATTN_ERR_LAYER", -6: "DIFFATTN_ERR_LAMBDA",
           -7: "DIFFATTN_ERR_WORKSPACE", -8: "DIFFATTN_ERR_ALIAS", -9: "DIFFATTN_ERR_HIP"}
-EXPORTS = ["diffattn_fwd", "diffattn_fwd_heads", "diffattn_decode", "diffattn_decode_heads",
+EXPORTS = ["diffattn_fwd", "diffattn_fwd_heads", "diffattn_fwd_strided", "diffattn_decode", "diffattn_decode_heads",
            "diffattn_decode_workspace_bytes", "diffattn_decode_varlen_workspace_bytes", "diffattn_decode_varlen",
            "diffattn_train_saved_bytes", "diffattn_fwd_train",
            "diffattn_bwd_workspace_bytes", "diffattn_bwd", "diffattn_lambda_init", "diffattn_status_str",
@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
     L.diffattn_decode_heads.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, P, c_int, c_int, P,
                                         ctypes.c_size_t, P]
     L.diffattn_decode_heads.restype = c_int
+    L.diffattn_fwd_strided.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, P, c_int, c_int, P, P]
+    L.diffattn_fwd_strided.restype = c_int
     L.diffattn_decode_varlen_workspace_bytes.argtypes = [i64, i64, i64, i64, c_int]
     L.diffattn_decode_varlen_workspace_bytes.restype = ctypes.c_size_t
     L.diffattn_decode_varlen.argtypes = [P, P, P, P, P, P, i64, i64, i64, i64, P, c_int, c_int, c_float, P, c_int, P,
@@ -287,4 +289,25 @@ def diffattn_decode_varlen(q1, k1, q2, k2, v, lam, layer: int, lens=None, out=No
                                       _stream_handle(stream, q1.device))
     if st != 0:
         raise DiffAttnError(st, "diffattn_decode_varlen")
+    return out
+
+
+def diffattn_fwd_strided(q1, k1, q2, k2, v, lam, layer: int, causal: bool, out=None, stream=None):
+    """Prefill (bf16, d = 64) on strided [B][H][N][.] views, e.g. slices of packed projection outputs; out may be a
+    strided view too (default: a new contiguous tensor).  Each tensor's last dimension must be contiguous."""
+    import torch
+    B, H, N, d = q1.shape
+    if out is None:
+        out = torch.empty((B, H, N, 2 * d), dtype=q1.dtype, device=q1.device)
+    ts = (q1, k1, q2, k2, v, out)
+    for t, w in zip(ts, (d, d, d, d, 2 * d, 2 * d)):
+        if not t.is_cuda or t.dtype != q1.dtype or tuple(t.shape) != (B, H, N, w) or t.stride(-1) != 1:
+            raise ValueError("strided prefill needs [B][H][N][w] GPU views of one dtype with a contiguous last dim")
+    strides = (ctypes.c_int64 * 18)(*[int(x) for t in ts for x in t.stride()[:3]])
+    lam_f, lam_p = _lambda_args(lam, H, q1.device)
+    st = lib().diffattn_fwd_strided(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
+                                    out.data_ptr(), B, H, N, d, _dtype_code(q1), lam_f, lam_p, int(layer),
+                                    int(bool(causal)), strides, _stream_handle(stream, q1.device))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_fwd_strided")
     return out

@@ -127,8 +127,8 @@ int fwd_impl(const void* q1, const void* k1, const void* q2, const void* k2, con
     if (dtype == DIFFATTN_BF16)
         return hip_status(diffattn::launch_prefill_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1,
                                                             (const uint16_t*)q2, (const uint16_t*)k2,
-                                                            (const uint16_t*)v, (uint16_t*)out, BH, N, causal, ep, nullptr,
-                                                            s));
+                                                            (const uint16_t*)v, (uint16_t*)out, B, H, N, causal,
+                                                            diffattn::contiguous_strides(H, N, d), ep, nullptr, s));
     return hip_status(diffattn::launch_attn_f32((const float*)q1, (const float*)k1, (const float*)q2, (const float*)k2,
                                                 (const float*)v, (float*)out, BH, N, N, d, causal, ep, s));
 }
@@ -146,6 +146,58 @@ int diffattn_fwd_heads(const void* q1, const void* k1, const void* q2, const voi
                        int64_t B, int64_t H, int64_t N, int d, int dtype, const float* lambda_heads, int layer,
                        int causal, void* stream) {
     return fwd_impl(q1, k1, q2, k2, v, out, B, H, N, d, dtype, 0.0f, lambda_heads, true, layer, causal, stream);
+}
+
+int diffattn_fwd_strided(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
+                         int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda, const float* lambda_heads,
+                         int layer, int causal, const int64_t* strides, void* stream) {
+    if (B < 0 || H < 0 || N < 0 || N > DIFFATTN_MAX_LEN) return DIFFATTN_ERR_SHAPE;
+    if (dtype != DIFFATTN_BF16 || d != 64) return DIFFATTN_ERR_UNSUPPORTED;
+    Epilogue ep;
+    int st = make_epilogue(lambda_heads ? 0.0f : lambda, layer, &ep);
+    if (st) return st;
+    int64_t BH;
+    if (!mul_ok(B, H, &BH) || BH > INT32_MAX) return DIFFATTN_ERR_SHAPE;
+    if (BH == 0 || N == 0) return DIFFATTN_OK;
+    if (!strides) return DIFFATTN_ERR_NULL;
+    if (!q1 || !k1 || !q2 || !k2 || !v || !out) return DIFFATTN_ERR_NULL;
+    if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2) || !aligned16(v) || !aligned16(out))
+        return DIFFATTN_ERR_ALIGN;
+    diffattn::Strides S;
+    const void* ptr[6] = {q1, k1, q2, k2, v, out};
+    Span span[6];
+    for (int k = 0; k < 6; ++k) {
+        S.b[k] = strides[3 * k];
+        S.h[k] = strides[3 * k + 1];
+        S.n[k] = strides[3 * k + 2];
+        const int64_t w = (k == diffattn::S_V || k == diffattn::S_OUT) ? 128 : 64;
+        if (S.b[k] < 0 || S.h[k] < 0 || S.n[k] < w) return DIFFATTN_ERR_SHAPE;
+        // 16-byte aligned rows: every stride a multiple of 8 bf16 elements.
+        if ((S.b[k] | S.h[k] | S.n[k]) & 7) return DIFFATTN_ERR_ALIGN;
+        // Element offset of the last element, and the 32-bit range of one head's rows (plus the prefetch overrun
+        // of the direct loads, 256 rows) for the tensors read through buffer offsets.
+        int64_t last, t1, t2, t3;
+        if (!mul_ok(B - 1, S.b[k], &t1) || !mul_ok(H - 1, S.h[k], &t2) || !mul_ok(N - 1, S.n[k], &t3) ||
+            t1 > INT64_MAX / 4 || t2 > INT64_MAX / 4 || t3 > INT64_MAX / 4)
+            return DIFFATTN_ERR_SHAPE;
+        last = t1 + t2 + t3 + w;
+        if (k == diffattn::S_K1 || k == diffattn::S_K2 || k == diffattn::S_V) {
+            int64_t range;
+            if (!mul_ok(N + 256, S.n[k] * 2, &range) || range + w * 2 > (int64_t)UINT32_MAX) return DIFFATTN_ERR_SHAPE;
+        }
+        span[k] = Span{(uintptr_t)ptr[k], (uintptr_t)ptr[k] + (uintptr_t)last * 2};
+    }
+    for (int k = 0; k < 5; ++k)
+        if (overlaps(span[diffattn::S_OUT], span[k])) return DIFFATTN_ERR_ALIAS;
+    if (lambda_heads) {
+        st = check_lambda_heads(lambda_heads, H, span[diffattn::S_OUT]);
+        if (st) return st;
+        ep.lambda_heads = lambda_heads;
+        ep.heads = (int)H;
+    }
+    return hip_status(diffattn::launch_prefill_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
+                                                        (const uint16_t*)k2, (const uint16_t*)v, (uint16_t*)out, B, H,
+                                                        N, causal, S, ep, nullptr, (hipStream_t)stream));
 }
 
 size_t diffattn_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
@@ -308,8 +360,9 @@ int diffattn_fwd_train(const void* q1, const void* k1, const void* q2, const voi
         ep.heads = (int)H;
     }
     return hip_status(diffattn::launch_prefill_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
-                                                        (const uint16_t*)k2, (const uint16_t*)v, (uint16_t*)out, BH,
-                                                        N, causal, ep, (float*)saved, (hipStream_t)stream));
+                                                        (const uint16_t*)k2, (const uint16_t*)v, (uint16_t*)out, B, H,
+                                                        N, causal, diffattn::contiguous_strides(H, N, d), ep,
+                                                        (float*)saved, (hipStream_t)stream));
 }
 
 int diffattn_bwd(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, const void* dy,

@@ -29,11 +29,31 @@ constexpr int SAVED_O1 = 4;
 constexpr int SAVED_O2 = 4 + 128;
 constexpr int SAVED_FLOATS = 4 + 256;   // 1040 bytes per row
 
+// Element strides of the six prefill tensors, indexed q1, k1, q2, k2, v, out: batch, head and row.  The feature
+// dimension is contiguous.
+struct Strides {
+    int64_t b[6], h[6], n[6];
+};
+enum { S_Q1 = 0, S_K1 = 1, S_Q2 = 2, S_K2 = 3, S_V = 4, S_OUT = 5 };
+
+// Dense [B][H][N][d] (and [B][H][N][2d] for v and out) strides.
+inline Strides contiguous_strides(int64_t H, int64_t N, int64_t d) {
+    Strides s;
+    for (int k = 0; k < 6; ++k) {
+        const int64_t w = (k == S_V || k == S_OUT) ? 2 * d : d;
+        s.b[k] = H * N * w;
+        s.h[k] = N * w;
+        s.n[k] = w;
+    }
+    return s;
+}
+
 // bf16 prefill, d = 64, 2d = 128: fused one-pass kernel (two online softmaxes, two MFMA accumulators).  With a
-// non-null `saved` ([BH][N][SAVED_FLOATS] fp32) it also writes each row's training statistics.
+// non-null `saved` ([BH][N][SAVED_FLOATS] fp32) it also writes each row's training statistics.  The caller has
+// checked that every head's K and V rows, N + 256 of them, span less than 4 GiB (32-bit buffer offsets).
 hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
-                                   const uint16_t* v, uint16_t* out, int64_t BH, int64_t N, int causal,
-                                   Epilogue ep, float* saved, hipStream_t stream);
+                                   const uint16_t* v, uint16_t* out, int64_t B, int64_t H, int64_t N, int causal,
+                                   const Strides& st, Epilogue ep, float* saved, hipStream_t stream);
 
 // bf16 backward, d = 64: preprocess, dQ, dK/dV and dlambda kernels (see backward_bf16.hip).  `saved` is the
 // training forward's [BH][N][SAVED_FLOATS]; `workspace` holds bwd_bf16_workspace_bytes(BH, N) bytes (256-byte

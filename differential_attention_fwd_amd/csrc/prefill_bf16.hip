@@ -129,8 +129,8 @@ template <bool SAVE>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1,
                              const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
-                             const uint16_t* __restrict__ gv, uint16_t* __restrict__ gout, int BH, int N,
-                             int n_row_tiles, int causal, Epilogue ep, float* __restrict__ saved) {
+                             const uint16_t* __restrict__ gv, uint16_t* __restrict__ gout, int BH, int H, int N,
+                             int n_row_tiles, int causal, Strides st, Epilogue ep, float* __restrict__ saved) {
     __shared__ __attribute__((aligned(16))) unsigned char kr0[K_SLOT_BYTES], kr1[K_SLOT_BYTES], kr2[K_SLOT_BYTES],
         kr3[K_SLOT_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char vr0[V_TILE_BYTES], vr1[V_TILE_BYTES], vr2[V_TILE_BYTES],
@@ -150,21 +150,26 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     const int q0 = rt * BM;
     const int q0w = q0 + wave * 32;
 
-    const size_t head_qk = (size_t)bh * (size_t)N * D;
-    const size_t head_v = (size_t)bh * (size_t)N * DV;
-    // Per-head buffer resources: rows at or beyond N read as zero (and are masked), so no clamping is needed.
-    // Byte sizes and offsets are unsigned 32-bit: a head's V is at most 2^23 x 256 bytes.
-    const unsigned k_bytes = (unsigned)N * (D * 2u), v_bytes = (unsigned)N * (DV * 2u);
-    const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc((void*)(gk1 + head_qk), (short)0, (int)k_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rk2 = __builtin_amdgcn_make_buffer_rsrc((void*)(gk2 + head_qk), (short)0, (int)k_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(gv + head_v), (short)0, (int)v_bytes, 0x00020000);
+    // This head's first element in each tensor (strides in elements; the feature dimension is contiguous).
+    const int64_t b_ = bh / H, h_ = bh % H;
+    auto base = [&](int k) { return b_ * st.b[k] + h_ * st.h[k]; };
+    // Per-head buffer resources over the head's N rows: rows at or beyond N read as zero (and are masked), so no
+    // clamping is needed.  Offsets are unsigned 32-bit; the host checked that N + 256 rows fit.
+    const unsigned k1rb = (unsigned)st.n[S_K1] * 2u, k2rb = (unsigned)st.n[S_K2] * 2u, vrb = (unsigned)st.n[S_V] * 2u;
+    const unsigned n1 = (unsigned)(N - 1);
+    const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc((void*)(gk1 + base(S_K1)), (short)0,
+                                                                         (int)(n1 * k1rb + D * 2u), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk2 = __builtin_amdgcn_make_buffer_rsrc((void*)(gk2 + base(S_K2)), (short)0,
+                                                                         (int)(n1 * k2rb + D * 2u), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(gv + base(S_V)), (short)0,
+                                                                        (int)(n1 * vrb + DV * 2u), 0x00020000);
 
     // Q fragments as the MFMA B operand: lane holds Q[q0w + l32][16 kc + 8 h .. + 7].
     bf16x8 qa[4], qb[4];
     {
         const int row = min(q0w + l32, N - 1);
-        const uint16_t* p1 = gq1 + head_qk + (size_t)row * D + 8 * h;
-        const uint16_t* p2 = gq2 + head_qk + (size_t)row * D + 8 * h;
+        const uint16_t* p1 = gq1 + base(S_Q1) + (int64_t)row * st.n[S_Q1] + 8 * h;
+        const uint16_t* p2 = gq2 + base(S_Q2) + (int64_t)row * st.n[S_Q2] + 8 * h;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             qa[kc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p1 + 16 * kc));
@@ -182,14 +187,16 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     // operations per iteration is therefore fixed, which makes the waits below exact.
     constexpr int K_PIECES_PER_WAVE = 8 / WAVES;   // K1 + K2 pieces per wave and tile
     constexpr int V_PIECES_PER_WAVE = 8 / WAVES;
-    unsigned kd_voff[K_PIECES_PER_WAVE], vd_voff[V_PIECES_PER_WAVE];
+    unsigned kd_voff[K_PIECES_PER_WAVE], kd_step[K_PIECES_PER_WAVE], vd_voff[V_PIECES_PER_WAVE];
     int kd_lds[K_PIECES_PER_WAVE];
 #pragma unroll
     for (int j = 0; j < K_PIECES_PER_WAVE; ++j) {
         const int piece = wave + WAVES * j;        // 0..3: K1, 4..7: K2
+        const unsigned rb = piece < 4 ? k1rb : k2rb;
         // K tile row 8 (piece % 4) + L / 8, stored chunk L % 8 = logical chunk ^ ((row >> 1) & 7) (see k_off).
         const int row = 8 * (piece & 3) + (lane >> 3);
-        kd_voff[j] = row * 128 + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
+        kd_voff[j] = (unsigned)row * rb + ((((lane & 7) ^ ((row >> 1) & 7))) << 4);
+        kd_step[j] = (unsigned)BN * rb;            // bytes per tile
         kd_lds[j] = (piece >> 2) * K_TILE_BYTES + 1024 * (piece & 3);
     }
 #pragma unroll
@@ -197,8 +204,9 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
         // Raw V: position p holds row p / 256 and stored chunk (p / 16) % 16 = logical chunk ^ (2 (row & 3)).
         const int p = 1024 * (wave + WAVES * j) + 16 * lane;
         const int row = p >> 8, pchunk = (p >> 4) & 15;
-        vd_voff[j] = row * 256 + ((pchunk ^ ((row & 3) << 1)) << 4);
+        vd_voff[j] = (unsigned)row * vrb + ((pchunk ^ ((row & 3) << 1)) << 4);
     }
+    const unsigned vd_step = (unsigned)BN * vrb;
     // Transpose raw V -> V^T with ds_read_b64_tr_b16.  A 16-lane group reads a block of 4 keys x 16 channels (lane
     // 4 jj + q supplies key jj, channels 4 q .. 4 q + 3) and lane i receives channel i of the block for the 4 keys:
     // 8 bytes of one V^T row, stored with one 64-bit write.  The 64 blocks of a tile are shared out over the
@@ -223,7 +231,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
 #pragma unroll
         for (int j = 0; j < K_PIECES_PER_WAVE; ++j) {
             // The tile offset goes into the VGPR offset: the SGPR offset is not part of the buffer range check.
-            const unsigned ko = kd_voff[j] + (unsigned)t * (BN * 128u);
+            const unsigned ko = kd_voff[j] + (unsigned)t * kd_step[j];
             if ((wave + WAVES * j) < 4)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rk1, (lds_void*)(slot + kd_lds[j]), 16, (int)ko, 0, 0, 0);
             else
@@ -235,7 +243,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
 #pragma unroll
         for (int j = 0; j < V_PIECES_PER_WAVE; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(slot + 1024 * (wave + WAVES * j)), 16,
-                                                     (int)(vd_voff[j] + (unsigned)t * (BN * 256u)), 0, 0, 0);
+                                                     (int)(vd_voff[j] + (unsigned)t * vd_step), 0, 0, 0);
     };
     // Transposition of raw V slot S into the V^T buffer of tile t, in two steps (read, then write) so that the
     // tile's computation hides the latency of the transposing reads.
@@ -405,7 +413,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
             *(f32x4*)srow = f32x4{st1.ml + __builtin_amdgcn_logf(l1), st2.ml + __builtin_amdgcn_logf(l2), rr, 0.f};
     }
     if (q < N) {
-        uint16_t* orow = gout + head_v + (size_t)q * DV + 4 * h;
+        uint16_t* orow = gout + base(S_OUT) + (int64_t)q * st.n[S_OUT] + 4 * h;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -421,17 +429,18 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
 }  // namespace
 
 hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
-                                   const uint16_t* v, uint16_t* out, int64_t BH, int64_t N, int causal,
-                                   Epilogue ep, float* saved, hipStream_t stream) {
+                                   const uint16_t* v, uint16_t* out, int64_t B, int64_t H, int64_t N, int causal,
+                                   const Strides& st, Epilogue ep, float* saved, hipStream_t stream) {
+    const int64_t BH = B * H;
     const int n_row_tiles = (int)((N + BM - 1) / BM);
     const int64_t blocks = (int64_t)n_row_tiles * BH;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     if (saved)
         hipLaunchKernelGGL(prefill_bf16_d64_kernel<true>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1,
-                           q2, k2, v, out, (int)BH, (int)N, n_row_tiles, causal ? 1 : 0, ep, saved);
+                           q2, k2, v, out, (int)BH, (int)H, (int)N, n_row_tiles, causal ? 1 : 0, st, ep, saved);
     else
         hipLaunchKernelGGL(prefill_bf16_d64_kernel<false>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1,
-                           q2, k2, v, out, (int)BH, (int)N, n_row_tiles, causal ? 1 : 0, ep, saved);
+                           q2, k2, v, out, (int)BH, (int)H, (int)N, n_row_tiles, causal ? 1 : 0, st, ep, saved);
     return hipGetLastError();
 }
 

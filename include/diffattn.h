@@ -112,6 +112,22 @@ int diffattn_decode_heads(const void *q1, const void *k1, const void *q2, const 
                           int causal, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Strided prefill (bf16, d = 64): diffattn_fwd with every tensor addressed through element strides, so that
+ * q1, k1, q2, k2 and v can be read straight out of packed projection outputs (the pages split one projection into
+ * the two query/key halves: [U] worked example) and out written into any row layout.
+ *   strides: HOST array of 18 int64 values, for q1, k1, q2, k2, v, out in that order: the batch, head and row
+ *            strides in elements.  The feature dimension (d, or 2d for v and out) is contiguous.  Element
+ *            (b, h, n, c) of tensor t is at base_t + b*strides[3t] + h*strides[3t+1] + n*strides[3t+2] + c.
+ *   Every stride must be >= 0, a multiple of 8 (16-byte rows; else DIFFATTN_ERR_ALIGN), and a row stride at least
+ *   the row width.  One head's K1, K2 and V rows, N + 256 of them, must span less than 4 GiB
+ *   (else DIFFATTN_ERR_SHAPE).  Outputs must not overlap the inputs' address ranges (bounding boxes).
+ *   lambda / lambda_heads as for diffattn_fwd_train.  Contiguous strides give diffattn_fwd's result bit for bit.
+ */
+int diffattn_fwd_strided(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
+                         int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda, const float *lambda_heads,
+                         int layer, int causal, const int64_t *strides, void *stream);
+
+/*
  * Variable-length and multi-token decode (bf16, d = 64).  Each sequence b has a cache of lens[b] valid rows in a
  * cache padded to L rows, and T new tokens (1 <= T <= DIFFATTN_MAX_NEW_TOKENS) that are already the last T of those
  * rows: new token t is position lens[b] - T + t and sees the keys up to and including its own position (the causal

@@ -230,3 +230,32 @@ def test_varlen_workspace_sizes(lib):
 ])
 def test_decode_varlen_validation(lib, case, expect):
     assert dec_var(lib, **case) == expect
+
+
+def contiguous_strides(B, H, N):
+    out = []
+    for w in (64, 64, 64, 64, 128, 128):
+        out += [H * N * w, N * w, w]
+    return out
+
+
+def fwd_strided(lib, strides="default", out=A[5], B=1, H=2, N=64, d=64, dtype=BF16, lam=0.5):
+    if strides == "default":
+        strides = contiguous_strides(B, H, N)
+    arr = (ctypes.c_int64 * 18)(*strides) if strides is not None else None
+    return lib.diffattn_fwd_strided(A[0], A[1], A[2], A[3], A[4], out, B, H, N, d, dtype, lam, None, 1, 1, arr, None)
+
+
+def _with(idx, val, B=1, H=2, N=64):
+    s = contiguous_strides(B, H, N)
+    s[idx] = val
+    return s
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(strides=None), E_NULL), (dict(strides=_with(2, 68)), E_ALIGN), (dict(strides=_with(14, 64)), E_SHAPE),
+    (dict(strides=_with(1, -8)), E_SHAPE), (dict(strides=_with(5, 1 << 26)), E_SHAPE), (dict(out=A[0]), E_ALIAS),
+    (dict(dtype=F32), E_UNSUP), (dict(N=0), OK), (dict(strides=_with(11, 64 * 2 * 64 * 4096)), E_SHAPE),
+])
+def test_fwd_strided_validation(lib, case, expect):
+    assert fwd_strided(lib, **case) == expect

@@ -430,3 +430,55 @@ def test_decode_varlen_matches_prefill_rows():
                                     dev["q2"][:, :, N - T:].contiguous(), dev["k2"], dev["v"], 0.8, 1)
     torch.cuda.synchronize()
     assert np.abs(host_bf16(pre)[:, :, N - T:] - host_bf16(dec)).max() <= 2e-2
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Strided prefill (diffattn_fwd_strided): operands read out of packed projection outputs
+# ---------------------------------------------------------------------------------------------------------------
+
+def test_prefill_strided_packed_projection():
+    """q1, k1, q2, k2, v as views of one [B][N][H][6][64] projection output, out into a [B][N][H][128] buffer:
+    bit-identical to the contiguous call, and within tolerance of the oracle."""
+    torch = torch_mod()
+    B, H, N = 2, 3, 333
+    inp = di.prefill_bf16(B, H, N, 64, seed=700)
+    say("case: strided prefill from a packed projection, B2 H3 N333 causal layer 2")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    proj = torch.empty((B, N, H, 6, 64), dtype=torch.bfloat16, device="cuda:0")
+    for i, k in enumerate(("q1", "k1", "q2", "k2")):
+        proj[:, :, :, i] = dev[k].permute(0, 2, 1, 3)
+    proj[:, :, :, 4:6] = dev["v"].permute(0, 2, 1, 3).reshape(B, N, H, 2, 64)
+    views = [proj[:, :, :, i].permute(0, 2, 1, 3) for i in range(4)]
+    vview = proj[:, :, :, 4:6].reshape(B, N, H, 128).permute(0, 2, 1, 3)
+    obuf = torch.zeros((B, N, H, 128), dtype=torch.bfloat16, device="cuda:0")
+    oview = obuf.permute(0, 2, 1, 3)
+    da.diffattn_fwd_strided(views[0], views[1], views[2], views[3], vview, 0.7, 2, True, out=oview)
+    ref_dev = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.7, 2, True)
+    torch.cuda.synchronize()
+    assert torch.equal(oview.contiguous().view(torch.int16), ref_dev.view(torch.int16))
+    f = widen(inp)
+    ref = oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], float(np.float32(0.7)), 2, True)
+    check_bf16(host_bf16(oview.contiguous()), ref, "strided prefill")
+
+
+def test_prefill_strided_interleaved_heads():
+    """Q and K with the two halves interleaved per head ([B][N][2H][64], half 1 at even, half 2 at odd heads),
+    non-causal, per-head lambda: bit-identical to the contiguous call."""
+    torch = torch_mod()
+    B, H, N = 1, 4, 200
+    inp = di.prefill_bf16(B, H, N, 64, seed=710)
+    say("case: strided prefill, interleaved query/key halves, B1 H4 N200 non-causal per-head lambda")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    q = torch.empty((B, N, 2 * H, 64), dtype=torch.bfloat16, device="cuda:0")
+    k = torch.empty_like(q)
+    q[:, :, 0::2] = dev["q1"].permute(0, 2, 1, 3)
+    q[:, :, 1::2] = dev["q2"].permute(0, 2, 1, 3)
+    k[:, :, 0::2] = dev["k1"].permute(0, 2, 1, 3)
+    k[:, :, 1::2] = dev["k2"].permute(0, 2, 1, 3)
+    lam = dev_lam([0.2, 0.4, 0.6, 0.8])
+    got = da.diffattn_fwd_strided(q[:, :, 0::2].permute(0, 2, 1, 3), k[:, :, 0::2].permute(0, 2, 1, 3),
+                                  q[:, :, 1::2].permute(0, 2, 1, 3), k[:, :, 1::2].permute(0, 2, 1, 3), dev["v"],
+                                  lam, 0, False)
+    want = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], lam, 0, False)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
