@@ -9,29 +9,30 @@
 //   * A workgroup of 4 waves (one per SIMD) owns 128 query rows of one (batch, head); each wave owns 32 rows.  Two
 //     workgroups share a CU, so each SIMD runs two independent waves and the matrix cores of one overlap the
 //     softmax of the other.  Key tiles are 32 keys.
-//   * Loads go straight from global memory to LDS (buffer_load ... lds, no registers) through 4-slot rings: the
-//     K1 and K2 tiles three tiles ahead, the raw V tile four ahead.  Every step transposes the next raw V tile
-//     LDS-to-LDS (ds_read_b64_tr_b16, then 64-bit writes after the step's own work) into a channel-major V^T tile,
-//     double-buffered, so that every MFMA operand is one 128-bit LDS read.  Ring slots are separate __shared__
-//     arrays and the loop is unrolled by four, so the compiler can tell reads of one slot from loads still landing
-//     in another.  One workgroup barrier per tile.
+//   * Loads go straight from global memory to LDS (buffer_load ... lds, no registers) through 4-slot rings, three
+//     tiles ahead: K1, K2 and V tiles, all row-major (one key per row).  Ring slots are separate __shared__ arrays
+//     and the loop is unrolled by four, so the compiler can tell reads of one slot from loads still landing in
+//     another.  One workgroup barrier per tile.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held in
 //     registers).  In the accumulator layout every lane owns ONE query row (lane % 32) and 16 of the 32 keys, so
 //     row statistics need only the lane pair (l, l ^ 32), exchanged with v_permlane32_swap.
 //   * P^T stays in registers and feeds O^T = V^T P^T directly as the MFMA B operand.  The k-order of that product
-//     is the accumulator's key order; the transposed V tile stores keys in that order, so the A operand of each
-//     MFMA is one contiguous 16-byte read, shared by the two maps.  O^T's layout gives each lane one query row
-//     again, so the online-softmax rescale of O is lane-local.
-//   * Two online softmaxes run side by side (running max and sum per map, two O accumulators).  The running max
-//     only moves when a row's new maximum exceeds it by more than 2^8 (wave-uniform decision), so the O rescale
-//     is rare; exponents use exp2 with log2(e)/sqrt(d) folded into one FMA; row sums add the bf16-rounded
-//     probabilities pairwise with v_dot2_f32_bf16.  Map 2's exponentials are issued between map 1's value MFMAs.
+//     is the accumulator's key order.  The A operand (V^T: one channel, 8 keys per lane) comes from the row-major
+//     V tile through two transposing reads (ds_read_b64_tr_b16, 4 keys each) that pick the keys in that order;
+//     each fragment is shared by the two maps.  O^T's layout gives each lane one query row again, so the
+//     online-softmax rescale of O is lane-local.
+//   * Two online softmaxes run side by side (running offset and sum per map, two O accumulators).  Probabilities
+//     are taken at the running offset first; only when a lane's 16 of them sum to more than 2^8 (a wave-uniform
+//     decision) is the row max taken and O rescaled, so neither the max nor the rescale is on the common path.
+//     Exponents use exp2 with log2(e)/sqrt(d) folded into one FMA; sums add the bf16-rounded probabilities
+//     pairwise with v_dot2_f32_bf16.  Map 2's exponentials are issued between map 1's value MFMAs.
 //   * Epilogue: O1/l1 - lambda O2/l2, RMS over the 128 channels (pair-reduced), scale, bf16 round-to-nearest-even.
 //   * Causal: row tiles are launched heaviest first; tiles wholly above a wave's rows are skipped by that wave,
 //     and only diagonal or ragged-tail tiles pay for masking.
 //
 // This translation unit is compiled with -fno-honor-nans: no NaN can arise (inputs are finite, masked scores are
-// -inf, and every processed row has a visible key in its first tile), and it lets v_max3 run without quieting.
+// -inf, the running offsets start at -FLT_MAX rather than -inf, and every processed row has a visible key in its
+// first tile), and it lets v_max3 run without quieting.
 #include "launch.h"
 #include "tiles.h"
 
@@ -46,8 +47,7 @@ constexpr int BN = 32;                          // keys per tile
 constexpr int THREADS = 64 * WAVES;
 constexpr int K_TILE_BYTES = BN * D * 2;        // 4 KiB
 constexpr int V_TILE_BYTES = BN * DV * 2;       // 8 KiB
-constexpr int RING = 4;                         // ring slots: K tile t in slot t % 4 (loaded three tiles ahead),
-                                                // raw V tile t in slot t % 4 (loaded four ahead)
+constexpr int RING = 4;                         // ring slots: K and V tiles t in slot t % 4, loaded three ahead
 constexpr int K_SLOT_BYTES = 2 * K_TILE_BYTES;
 
 // Compile-time ring slot.  Each ring slot is its own __shared__ array, so the compiler can tell an LDS read of one
@@ -60,7 +60,9 @@ template <int S, class T> __device__ __forceinline__ T* pick4(T* a, T* b, T* c, 
     else if constexpr (S % 4 == 2) return c;
     else return d;
 }
-constexpr float RESCALE_THRESHOLD = 8.0f;       // log2 units: p never exceeds 2^8 between rescales
+// A lane's 16 probabilities of a tile may sum to at most 2^8 at the running offset; above that (or +inf) the tile takes
+// the exact path.  So no probability ever exceeds 2^8 between rescales.
+constexpr unsigned P_SUM_LIMIT_BITS = 0x43800000u;   // bits of 256.0f; compared as integers, +inf and NaN exceed it
 
 __device__ __forceinline__ float max16(const f32x16& s) {
     const float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
@@ -69,30 +71,12 @@ __device__ __forceinline__ float max16(const f32x16& s) {
     return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[15]));
 }
 
-// Online-softmax state of one map for the lane's query row.  The running max is kept in score units (ms) and in
-// log2 units (ml = ms * c, the exponent offset); it only moves when a tile's max exceeds it by more than
-// RESCALE_THRESHOLD log2 units (mt = ms + RESCALE_THRESHOLD / c), a wave-uniform decision, so the rescale of O and l
-// is rare.
+// Online-softmax state of one map for the lane's query row: the running offset in score units (ms) and in log2
+// units (ml = ms * c), and the running sum l.  Both offsets start at -FLT_MAX, so the first tile's probabilities
+// overflow to +inf (never NaN, also for masked -inf scores) and take the exact path.
 struct MapState {
-    float ms, ml, mt, l;
+    float ms, ml, l;
 };
-
-__device__ __forceinline__ void update_max(const f32x16& s, MapState& st, f32x16 (&o)[4], float c, float thr) {
-    const float x = pair_max(max16(s));
-    if (__any(x > st.mt)) {
-        const float ms = fmaxf(st.ms, x);
-        const float ml = ms * c;
-        const float alpha = __builtin_amdgcn_exp2f(st.ml - ml);
-        st.ms = ms;
-        st.ml = ml;
-        st.mt = ms + thr;
-        st.l *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
-    }
-}
 
 // p = exp2(s * c - ml) for the lane's 16 keys, packed as P^T: two bf16x8 B operands.
 __device__ __forceinline__ void exp_pack(const f32x16& s, float ml, float c, bf16x8& lo, bf16x8& hi) {
@@ -109,9 +93,9 @@ __device__ __forceinline__ void exp_pack(const f32x16& s, float ml, float c, bf1
     hi = __builtin_bit_cast(bf16x8, b);
 }
 
-// Adds the lane's 16 packed probabilities to l: pairwise bf16 dot products with (1, 1), so the sum is of the same
+// Sum of the lane's 16 packed probabilities: pairwise bf16 dot products with (1, 1), so the sum is of the same
 // bf16-rounded values that multiply V.
-__device__ __forceinline__ float sum_packed(const bf16x8& lo, const bf16x8& hi, float l) {
+__device__ __forceinline__ float sum_packed(const bf16x8& lo, const bf16x8& hi) {
     const u32x4 a = __builtin_bit_cast(u32x4, lo), b = __builtin_bit_cast(u32x4, hi);
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     float t0 = 0.f, t1 = 0.f;
@@ -121,7 +105,33 @@ __device__ __forceinline__ float sum_packed(const bf16x8& lo, const bf16x8& hi, 
         t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ak), one, t0, false);
         t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, bk), one, t1, false);
     }
-    return l + (t0 + t1);
+    return t0 + t1;
+}
+
+// Probabilities of one map for the lane's 16 scores of a tile, packed as P^T (lo, hi), and their sum.  They are
+// first taken at the running offset.  Only if some lane's sum exceeds 2^8 (a wave-uniform decision; the first tile
+// always does) is the row max taken: the offset moves to it, O and l are rescaled, and the probabilities are taken
+// again.  Between rescales every probability is at most 2^8, and after the first few tiles the row max is almost
+// never needed.
+__device__ __forceinline__ float softmax_tile(const f32x16& s, MapState& st, f32x16 (&o)[4], float c, bf16x8& lo,
+                                              bf16x8& hi) {
+    exp_pack(s, st.ml, c, lo, hi);
+    float part = sum_packed(lo, hi);
+    if (__any(__float_as_uint(part) > P_SUM_LIMIT_BITS)) {
+        const float ms = fmaxf(st.ms, pair_max(max16(s)));
+        const float ml = ms * c;
+        const float alpha = __builtin_amdgcn_exp2f(st.ml - ml);
+        st.ms = ms;
+        st.ml = ml;
+        st.l *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
+        exp_pack(s, ml, c, lo, hi);
+        part = sum_packed(lo, hi);
+    }
+    return part;
 }
 
 // SAVE: also write each row's training statistics (SAVED_* in launch.h) for the backward pass.
@@ -135,7 +145,6 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
         kr3[K_SLOT_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char vr0[V_TILE_BYTES], vr1[V_TILE_BYTES], vr2[V_TILE_BYTES],
         vr3[V_TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char vtb[2 * V_TILE_BYTES];   // transposed V, double buffer
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -207,25 +216,6 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
         vd_voff[j] = (unsigned)row * vrb + ((pchunk ^ ((row & 3) << 1)) << 4);
     }
     const unsigned vd_step = (unsigned)BN * vrb;
-    // Transpose raw V -> V^T with ds_read_b64_tr_b16.  A 16-lane group reads a block of 4 keys x 16 channels (lane
-    // 4 jj + q supplies key jj, channels 4 q .. 4 q + 3) and lane i receives channel i of the block for the 4 keys:
-    // 8 bytes of one V^T row, stored with one 64-bit write.  The 64 blocks of a tile are shared out over the
-    // workgroup's 16-lane groups: group g takes blocks g + GROUPS b (keys 4 ((g + GROUPS b) / 8) .. + 3, channels
-    // 16 (g % 8) .. + 15); consecutive blocks of a group lie (GROUPS / 8) x 1 KiB apart in the raw tile.
-    constexpr int GROUPS = THREADS / 16;
-    constexpr int TR_BLOCKS = 64 / GROUPS;
-    const int grp = tid >> 4, gl = tid & 15;
-    const int cgb = grp & 7;
-    const int tr_ch = 16 * cgb + 4 * (gl & 3);   // first channel of the 8 bytes this lane supplies
-    const int tr_rd = vr_off(4 * (grp >> 3) + (gl >> 2), tr_ch >> 3) + (tr_ch & 7) * 2;
-    int tr_wr[TR_BLOCKS];
-#pragma unroll
-    for (int b = 0; b < TR_BLOCKS; ++b) {
-        const int pos = key_pos(4 * ((grp + GROUPS * b) >> 3));   // the block's 4 keys sit at 4 consecutive positions
-        tr_wr[b] = vt_off(16 * cgb + gl, pos >> 3) + (pos & 7) * 2;
-    }
-
-    auto vslot = [&](int t) { return vtb + (t & 1) * V_TILE_BYTES; };
     auto issue_k = [&](auto S, int t) {   // S = t % 4
         unsigned char* slot = pick4<decltype(S)::value>(kr0, kr1, kr2, kr3);
 #pragma unroll
@@ -245,27 +235,18 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(slot + 1024 * (wave + WAVES * j)), 16,
                                                      (int)(vd_voff[j] + (unsigned)t * vd_step), 0, 0, 0);
     };
-    // Transposition of raw V slot S into the V^T buffer of tile t, in two steps (read, then write) so that the
-    // tile's computation hides the latency of the transposing reads.
-    s16x4 trx[TR_BLOCKS];
-    auto transpose_read = [&](auto S) {
-        const unsigned char* raw = pick4<decltype(S)::value>(vr0, vr1, vr2, vr3);
-#pragma unroll
-        for (int b = 0; b < TR_BLOCKS; ++b)
-            trx[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(raw + tr_rd + (GROUPS / 8) * 1024 * b));
-    };
-    auto transpose_write = [&](int t) {
-        unsigned char* vt = vslot(t);
-#pragma unroll
-        for (int b = 0; b < TR_BLOCKS; ++b) *(s16x4*)(vt + tr_wr[b]) = trx[b];
-    };
-
-    // Per-lane read offsets: K A-operand (row l32, chunk 2 kc + h) and V^T A-operand (channel 32 cb + l32,
-    // chunk 2 ks + h; the four channel blocks are 2 KiB apart).
-    // k_off(l32, 2 kc + h) = k_rd0 ^ (32 kc): the chunk swizzle is an XOR on bits 4..6 of the offset.
+    // Per-lane read offsets.  K A-operand: row l32, chunk 2 kc + h; k_off(l32, 2 kc + h) = k_rd0 ^ (32 kc), the
+    // chunk swizzle being an XOR on bits 4..6 of the offset.
+    // V^T A-operand of channel block cb and key half ks: lane (h, l32) needs channel 32 cb + l32 of the keys at
+    // accumulator positions 16 ks + 8 h .. + 7, i.e. keys 16 ks + 4 h + 0..3, then 16 ks + 8 + 4 h + 0..3.  Each
+    // comes from one ds_read_b64_tr_b16: the lane's 16-lane group reads a block of 4 keys x 16 channels, lane
+    // 4 jj + q of the group supplying key jj, channels 4 q .. 4 q + 3 of the block, and lane i of the group
+    // receiving channel i of the 4 keys.  The 4-key blocks sit at multiples of 4 rows, so the raw-tile swizzle
+    // depends only on jj; moving to channel block cb XORs 64 cb into the offset, moving by 8 keys adds 2 KiB.
     const int k_rd0 = k_off(l32, h);
-    const int v_rd0 = vt_off(l32, h);
-    const int v_rd1 = vt_off(l32, 2 + h);
+    const int trl = lane & 15;
+    const int tr_ch = 16 * ((lane >> 4) & 1) + 4 * (trl & 3);   // first channel this lane supplies (block cb = 0)
+    const int v_rd0 = vr_off(4 * h + (trl >> 2), tr_ch >> 3) + (tr_ch & 7) * 2;
 
     f32x16 o1[4], o2[4];
 #pragma unroll
@@ -273,35 +254,34 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
 #pragma unroll
         for (int i = 0; i < 16; ++i) { o1[cb][i] = 0.f; o2[cb][i] = 0.f; }
     const float c = LOG2E * 0.125f;  // log2(e) / sqrt(64)
-    const float thr = RESCALE_THRESHOLD / c;
-    MapState st1 = {-INFINITY, -INFINITY, -INFINITY, 0.f}, st2 = st1;
+    MapState st1 = {-__FLT_MAX__, -__FLT_MAX__, 0.f}, st2 = st1;
 
-    // Load schedule.  Iteration t (between two workgroup barriers) issues the direct loads of K(t + 2) and raw
-    // V(t + 3), transposes raw V(t + 1) into the V^T buffer of tile t + 1, and computes tile t.  At its end it waits
-    // for everything but its own loads, so a load issued in iteration u is usable from iteration u + 1 on
-    // (and has had the whole of iteration u to land).
+    // Load schedule.  Iteration t (between two workgroup barriers) issues the direct loads of K(t + 3) and V(t + 3)
+    // into the slot that tile t - 1 left (every wave has passed the barrier after reading it), and computes tile t.
+    // At its end it waits for everything but the loads of this iteration and the previous one, so tile t + 1 has
+    // landed and a load has two whole iterations to land.
     issue_k(Slot<0>{}, 0);
     issue_v(Slot<0>{}, 0);
     issue_k(Slot<1>{}, 1);
     issue_v(Slot<1>{}, 1);
     issue_k(Slot<2>{}, 2);
     issue_v(Slot<2>{}, 2);
-    issue_v(Slot<3>{}, 3);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * (K_PIECES_PER_WAVE + V_PIECES_PER_WAVE)));
     lds_barrier();
-    transpose_read(Slot<0>{});
-    transpose_write(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-    lds_barrier();
+    // Two transposing reads make one V^T fragment (the 8 keys of one accumulator position block).
+    auto v_frag = [&](const unsigned char* p) __attribute__((always_inline)) {
+        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * 256));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     auto step = [&](auto S, int t) {   // S = t % 4
         constexpr int s0 = decltype(S)::value;
         issue_k(Slot<(s0 + 3) % 4>{}, t + 3);
-        issue_v(Slot<s0>{}, t + 4);
-        transpose_read(Slot<(s0 + 1) % 4>{});
+        issue_v(Slot<(s0 + 3) % 4>{}, t + 3);
         const int kv0 = t * BN;
         if (!causal || kv0 <= q0w + 31) {
             const unsigned char* kb_ = pick4<s0>(kr0, kr1, kr2, kr3);
-            const unsigned char* vb_ = vslot(t);
+            const unsigned char* vb_ = pick4<s0>(vr0, vr1, vr2, vr3);
             f32x16 s1, s2;
 #pragma unroll
             for (int i = 0; i < 16; ++i) { s1[i] = 0.f; s2[i] = 0.f; }
@@ -323,32 +303,27 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
                     s2[i] = vis ? s2[i] : -INFINITY;
                 }
             }
-            update_max(s1, st1, o1, c, thr);
-            update_max(s2, st2, o2, c, thr);
-
             bf16x8 p1[2], p2[2];
-            exp_pack(s1, st1.ml, c, p1[0], p1[1]);
+            const float part1 = softmax_tile(s1, st1, o1, c, p1[0], p1[1]);
             bf16x8 va[4][2];
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) va[cb][0] = *(const bf16x8*)(vb_ + v_rd0 + 2048 * cb);
+            for (int cb = 0; cb < 4; ++cb) va[cb][0] = v_frag(vb_ + (v_rd0 ^ (64 * cb)));
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o1[cb] = mfma(va[cb][0], p1[0], o1[cb]);
-            exp_pack(s2, st2.ml, c, p2[0], p2[1]);
+            const float part2 = softmax_tile(s2, st2, o2, c, p2[0], p2[1]);
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) va[cb][1] = *(const bf16x8*)(vb_ + v_rd1 + 2048 * cb);
+            for (int cb = 0; cb < 4; ++cb) va[cb][1] = v_frag(vb_ + (v_rd0 ^ (64 * cb)) + 16 * 256);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o2[cb] = mfma(va[cb][0], p2[0], o2[cb]);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o1[cb] = mfma(va[cb][1], p1[1], o1[cb]);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o2[cb] = mfma(va[cb][1], p2[1], o2[cb]);
-            st1.l = sum_packed(p1[0], p1[1], st1.l);
-            st2.l = sum_packed(p2[0], p2[1], st2.l);
+            st1.l += part1;
+            st2.l += part2;
         }
-        transpose_write(t + 1);
-        // The loads of this iteration and the previous one (K(t + 2), V(t + 3), K(t + 3), V(t + 4)) may stay in
-        // flight past the barrier; everything older, in particular K(t + 1) and V(t + 2), has landed, and the
-        // transposed V(t + 1) is written.
+        // The loads of this iteration and the previous one (tiles t + 3 and t + 2) may stay in flight past the
+        // barrier; tile t + 1 has landed.
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * (K_PIECES_PER_WAVE + V_PIECES_PER_WAVE)));
         lds_barrier();
     };
