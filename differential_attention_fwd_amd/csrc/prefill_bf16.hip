@@ -282,6 +282,9 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
         if (!causal || kv0 <= q0w + 31) {
             const unsigned char* kb_ = pick4<s0>(kr0, kr1, kr2, kr3);
             const unsigned char* vb_ = pick4<s0>(vr0, vr1, vr2, vr3);
+            // Wave priority: high while this wave issues matrix work, low for map 1's softmax, so that of the two
+            // waves on a SIMD the one with MFMAs ready wins the issue arbitration.
+            __builtin_amdgcn_s_setprio(1);
             f32x16 s1, s2;
 #pragma unroll
             for (int i = 0; i < 16; ++i) { s1[i] = 0.f; s2[i] = 0.f; }
@@ -304,7 +307,9 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
                 }
             }
             bf16x8 p1[2], p2[2];
+            __builtin_amdgcn_s_setprio(0);
             const float part1 = softmax_tile(s1, st1, o1, c, p1[0], p1[1]);
+            __builtin_amdgcn_s_setprio(1);
             bf16x8 va[4][2];
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) va[cb][0] = v_frag(vb_ + (v_rd0 ^ (64 * cb)));
@@ -321,6 +326,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
             for (int cb = 0; cb < 4; ++cb) o2[cb] = mfma(va[cb][1], p2[1], o2[cb]);
             st1.l += part1;
             st2.l += part2;
+            __builtin_amdgcn_s_setprio(0);
         }
         // The loads of this iteration and the previous one (tiles t + 3 and t + 2) may stay in flight past the
         // barrier; tile t + 1 has landed.
