@@ -18,13 +18,15 @@
 //   2. bwd_dq:       per 128-row query block (4 waves x 32 rows), loop over key tiles up to the diagonal:
 //                    S^T = K Q^T and dP^T = V dO^T on MFMA, ds in registers, dQ^T += K^T ds^T with K^T tiles
 //                    transposed in LDS.  Same register plan as the forward (two waves per SIMD).
-//   3. bwd_dkdv:     per 128-key block (4 waves x 32 keys), loop over query tiles from the diagonal: S = Q K^T and
-//                    dP = dO V^T with the wave's K and V rows held in registers, then dV^T += dO^T W and
-//                    dK^T += Q^T ds from transposed Q and dO tiles.  Its 128 accumulator registers plus the score
-//                    tiles need one wave per SIMD (the accumulators live in AGPRs).
+//   3. bwd_dkdv:     per 64-key block (4 waves x 16 keys, v_mfma_f32_16x16x32_bf16), loop over query tiles from the
+//                    diagonal: S = Q K^T and dP = dO V^T with the wave's K and V rows held in registers, then
+//                    dV^T += dO^T W and dK^T += Q^T ds, the transposed operands read from the row-major tiles with
+//                    ds_read_b64_tr_b16.  Two waves per SIMD.  Q, dO and stats tiles come straight from global
+//                    memory to LDS (buffer_load ... lds) through a 4-slot ring, three tiles ahead, one barrier per
+//                    tile.
 //   4. bwd_dlambda:  per head, a fixed-order sum of the rows' dlambda shares (deterministic).
-// Tiles move global -> registers -> LDS (one tile ahead), are transposed in LDS with ds_read_b64_tr_b16, and
-// three workgroup barriers separate loading, transposing and computing.
+// In bwd_dq, tiles move global -> registers -> LDS (one tile ahead), are transposed in LDS with ds_read_b64_tr_b16,
+// and three workgroup barriers separate loading, transposing and computing.
 #include "launch.h"
 #include "tiles.h"
 
@@ -275,161 +277,265 @@ void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------------------------------
-// 3. dK, dV: per 128-key block; lane owns key k0w + l32 in every product.
+// 3. dK, dV: per 64-key block (4 waves x 16 keys); lane owns key k0w + (lane % 16) in every product.
 // ---------------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Products per 32-query tile, all with v_mfma_f32_16x16x32_bf16 (A 16 x 32: lane holds A[m = l % 16][k = 8 (l / 16)
+// + j]; B 32 x 16: lane holds B[k = 8 (l / 16) + j][n = l % 16]; D 16 x 16: lane holds D[m = 4 (l / 16) + i][n = l %
+// 16]), in 16-query blocks mb:
+//   S = Q K^T and dP = dO V^T: A = Q or dO rows from LDS, B = the wave's K^T or V^T held in registers.  Lane l then
+//   holds key l % 16 and queries 16 mb + 4 g + i (g = l / 16), so a lane's 8 values of W = a - lambda b, ds1 and
+//   ds2 over the two blocks are, in order, exactly the B operand (k = queries 4 g + 0..3, then 16 + 4 g + 0..3)
+//   of the next products:
+//   dV^T += dO^T W and dK^T += Q^T ds: A = dO^T or Q^T (one feature, those 8 queries per lane) from two
+//   ds_read_b64_tr_b16 reads of the row-major tile.
+// The Q and dO tiles are swizzled so that both the 16-row 128-bit reads and the 4-row transposing reads hit
+// distinct LDS bank quads.
+constexpr int KW = 16;                            // keys per wave
+constexpr int KBLK = KW * WAVES;                  // keys per workgroup
+constexpr int Q_TILE_BYTES = TILE * D * 2;        // 4 KiB
+constexpr int DO_TILE_BYTES = TILE * DV * 2;      // 8 KiB
+constexpr int ST_TILE_BYTES = TILE * STAT_FLOATS * 4;
+constexpr int SLOT_BYTES = 2 * Q_TILE_BYTES + DO_TILE_BYTES + ST_TILE_BYTES;   // Q1 | Q2 | dO | stats
+constexpr int ST_OFF = 2 * Q_TILE_BYTES + DO_TILE_BYTES;
+constexpr int DKDV_LOADS = 5;                     // direct loads per wave and tile: Q1, Q2, 2 x dO, stats
+
+// Q tile: row r (query) of 128 bytes; chunk c at c ^ q_sw(r).  Rows r and r + 2 (same LDS bank half) differ in
+// bit 1 of the swizzle, so a transposing read's 4 rows x 32 bytes and a 16-row read of one chunk both hit distinct
+// bank quads.
+__device__ __forceinline__ int q_sw(int r) {
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
+}
+__device__ __forceinline__ int q_off(int r, int c) { return r * 128 + ((c ^ q_sw(r)) << 4); }
+// dO tile: row r of 256 bytes; chunk c at c ^ do_sw(r), a bijection of r % 16 onto the 16 chunk positions.
+__device__ __forceinline__ int do_sw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+__device__ __forceinline__ int do_off(int r, int c) { return r * 256 + ((c ^ do_sw(r)) << 4); }
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int V> struct Slot { static constexpr int value = V; };
+template <int S, class T> __device__ __forceinline__ T* pick4(T* a, T* b, T* c, T* d) {
+    if constexpr (S % 4 == 0) return a;
+    else if constexpr (S % 4 == 1) return b;
+    else if constexpr (S % 4 == 2) return c;
+    else return d;
+}
+
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1,
                      const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
                      const uint16_t* __restrict__ gv, const uint16_t* __restrict__ gdo,
                      const float* __restrict__ stats, uint16_t* __restrict__ dk1, uint16_t* __restrict__ dk2,
-                     uint16_t* __restrict__ dv, int BH, int N, int n_blocks, int causal, Epilogue ep) {
-    __shared__ __attribute__((aligned(16))) unsigned char q1s[TILE * D * 2], q2s[TILE * D * 2], dos[TILE * DV * 2];
-    __shared__ __attribute__((aligned(16))) unsigned char q1t[TILE * D * 2], q2t[TILE * D * 2], dot[TILE * DV * 2];
-    __shared__ __attribute__((aligned(16))) float sts[STAT_FLOATS][TILE];   // lse1, lse2, E1, E2 per query
+                     uint16_t* __restrict__ dv, int BH, int N, int causal, Epilogue ep) {
+    __shared__ __attribute__((aligned(16))) unsigned char sl0[SLOT_BYTES], sl1[SLOT_BYTES], sl2[SLOT_BYTES],
+        sl3[SLOT_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = lane >> 5, l32 = lane & 31;
+    const int g = lane >> 4, l16 = lane & 15;
     const int bid = blockIdx.x;
     const int kb = bid / BH;   // key blocks in order: the first ones see the most queries under the causal mask
     const int bh = bid % BH;
-    const int k0 = kb * BLOCK, k0w = k0 + TILE * wave;
+    const int k0 = kb * KBLK, k0w = k0 + KW * wave;
     const size_t hqk = (size_t)bh * N * D, hv = (size_t)bh * N * DV;
-    const int key = k0w + l32, kc_row = min(key, N - 1);
-    (void)n_blocks;
-
-    bf16x8 kb1[4], kb2[4], vb[8];   // the wave's K and V rows as B operands (k = feature, n = key)
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-        kb1[kc] = *(const bf16x8*)(gk1 + hqk + (size_t)kc_row * D + 16 * kc + 8 * h);
-        kb2[kc] = *(const bf16x8*)(gk2 + hqk + (size_t)kc_row * D + 16 * kc + 8 * h);
-    }
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) vb[kc] = *(const bf16x8*)(gv + hv + (size_t)kc_row * DV + 16 * kc + 8 * h);
+    const int key = k0w + l16, kc_row = min(key, N - 1);
     const float c = LOG2E * 0.125f;
     const float lam = lambda_of(ep, bh);
 
-    f32x16 av[4], ak1[2], ak2[2];   // dV^T, dK1^T, dK2^T: feature 32 blk + 8 (i/4) + 4 h + i % 4, key = lane's key
+    // Per-head buffer resources: rows at or beyond N read as zero.  Offsets are unsigned 32-bit; N is at most 2^23,
+    // so (N + 96) rows of 256 bytes fit.
+    const __amdgpu_buffer_rsrc_t rq1 = __builtin_amdgcn_make_buffer_rsrc((void*)(gq1 + hqk), (short)0, N * (D * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq2 = __builtin_amdgcn_make_buffer_rsrc((void*)(gq2 + hqk), (short)0, N * (D * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rdo = __builtin_amdgcn_make_buffer_rsrc((void*)(gdo + hv), (short)0, N * (DV * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc((void*)(stats + (size_t)bh * N * STAT_FLOATS),
+                                                                         (short)0, N * (STAT_FLOATS * 4), 0x00020000);
+
+    // Direct loads per wave and tile: Q1 rows 8 wave .. + 7, Q2 the same, dO rows 4 p .. 4 p + 3 for pieces
+    // p = wave and wave + 4 (lane L writes position 16 L of a 1 KiB piece), and stat `wave` of the tile's 32 queries
+    // (lanes 0..31, 4 bytes each, so the stats land as [stat][query]).  Loads are issued unconditionally, also for
+    // tiles past the end (out of range: zeros), so every iteration issues the same number.
+    const int qrow = 8 * wave + (lane >> 3);
+    const unsigned q_voff = (unsigned)qrow * (D * 2) + ((((lane & 7) ^ q_sw(qrow))) << 4);
+    unsigned do_voff[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) av[cb][i] = 0.f;
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) { ak1[nb][i] = 0.f; ak2[nb][i] = 0.f; }
+    for (int j = 0; j < 2; ++j) {
+        const int r = 4 * (wave + WAVES * j) + (lane >> 4);
+        do_voff[j] = (unsigned)r * (DV * 2) + ((((lane & 15) ^ do_sw(r))) << 4);
     }
+    const unsigned st_voff = (unsigned)(lane & 31) * (STAT_FLOATS * 4) + 4u * (unsigned)wave;
+    auto issue = [&](auto S, int u) __attribute__((always_inline)) {
+        unsigned char* s = pick4<decltype(S)::value>(sl0, sl1, sl2, sl3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq1, (lds_void*)(s + 1024 * wave), 16,
+                                                 (int)(q_voff + (unsigned)u * (TILE * D * 2)), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq2, (lds_void*)(s + Q_TILE_BYTES + 1024 * wave), 16,
+                                                 (int)(q_voff + (unsigned)u * (TILE * D * 2)), 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rdo, (lds_void*)(s + 2 * Q_TILE_BYTES + 1024 * (wave + WAVES * j)),
+                                                     16, (int)(do_voff[j] + (unsigned)u * (TILE * DV * 2)), 0, 0, 0);
+        if (lane < 32)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rst, (lds_void*)(s + ST_OFF + 128 * wave), 4,
+                                                     (int)(st_voff + (unsigned)u * (TILE * STAT_FLOATS * 4)), 0, 0, 0);
+    };
 
     const int n_qt = (N + TILE - 1) / TILE;
     const int u_first = causal ? k0 / TILE : 0;                  // workgroup's first query tile
-    const int u_wave = causal ? k0w / TILE : 0;                  // this wave's first query tile with visible queries
-    const int a_rd0 = k_off(l32, h);                            // Q tile A-operand read (row l32, chunk 2 kc + h)
-    const int t_rd0 = vt_off(l32, h), t_rd1 = vt_off(l32, 2 + h);
+    const int n_iter = n_qt - u_first;
+    if (n_iter > 0) issue(Slot<0>{}, u_first);
+    if (n_iter > 0) issue(Slot<1>{}, u_first + 1);
+    if (n_iter > 0) issue(Slot<2>{}, u_first + 2);
 
-    u32x4 rq1[1], rq2[1], rdo[2];
-    f32x4 rst = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto load_q = [&](int u) __attribute__((always_inline)) {
-        load_tile<D>(gq1 + hqk, u * TILE, N, tid, rq1);
-        load_tile<D>(gq2 + hqk, u * TILE, N, tid, rq2);
-        load_tile<DV>(gdo + hv, u * TILE, N, tid, rdo);
-        const int qr = u * TILE + tid;
-        if (tid < TILE && qr < N) rst = *(const f32x4*)(stats + ((size_t)bh * N + qr) * STAT_FLOATS);
+    // The wave's K1, K2 and V rows as B operands (k = feature, n = key): lane holds feature 32 kh + 8 g .. + 7 of
+    // key `key`.  Loaded after the first tiles' direct loads and used before the loop, so the compiler waits for
+    // them there and places no wait for them inside the loop.
+    bf16x8 kb1[2], kb2[2], vb[4];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+        kb1[kh] = *(const bf16x8*)(gk1 + hqk + (size_t)kc_row * D + 32 * kh + 8 * g);
+        kb2[kh] = *(const bf16x8*)(gk2 + hqk + (size_t)kc_row * D + 32 * kh + 8 * g);
+    }
+#pragma unroll
+    for (int kh = 0; kh < 4; ++kh) vb[kh] = *(const bf16x8*)(gv + hv + (size_t)kc_row * DV + 32 * kh + 8 * g);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) asm volatile("" ::"v"(kb1[kh]), "v"(kb2[kh]));
+#pragma unroll
+    for (int kh = 0; kh < 4; ++kh) asm volatile("" ::"v"(vb[kh]));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+
+    f32x4 av[8], ak1[4], ak2[4];   // dV^T, dK1^T, dK2^T: feature 16 fb + 4 g + i, key = lane's key
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int fb = 0; fb < 8; ++fb) av[fb][i] = 0.f;
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) { ak1[fb][i] = 0.f; ak2[fb][i] = 0.f; }
+    }
+
+    // Read offsets.  16-row reads (A operands of S and dP): row 16 mb + l16, logical chunk 4 kh + g; the swizzles
+    // depend only on the row's low bits, so q_off(16 mb + l16, 4 kh + g) = (q_rd0 ^ 64 kh) + 2048 mb and likewise
+    // for dO with 4096 mb.  Transposing reads (A operands of dV^T and dK^T): lane 4 jj + qq of 16-lane group g
+    // supplies row 4 g + jj (then 16 + 4 g + jj), features 16 fb + 4 qq .. + 3; feature block fb XORs 32 fb into
+    // the offset.
+    const int q_rd0 = q_off(l16, g), do_rd0 = do_off(l16, g);
+    const int jj = (lane >> 2) & 3, qq = lane & 3;
+    const int q_tr0 = q_off(4 * g + jj, qq >> 1) + 8 * (qq & 1);
+    const int do_tr0 = do_off(4 * g + jj, qq >> 1) + 8 * (qq & 1);
+    auto tr_frag = [&](const unsigned char* p, int step) __attribute__((always_inline)) {
+        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + step));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    if (u_first < n_qt) load_q(u_first);
-    for (int u = u_first; u < n_qt; ++u) {
-        __syncthreads();
-        store_tile<D>(q1s, tid, rq1);
-        store_tile<D>(q2s, tid, rq2);
-        store_tile<DV>(dos, tid, rdo);
-        if (tid < TILE) {
+
+    auto step = [&](auto S, int j) __attribute__((always_inline)) {   // S = j % 4
+        constexpr int s0 = decltype(S)::value;
+        const int u = u_first + j;
+        issue(Slot<(s0 + 3) % 4>{}, u + 3);
+        if (!causal || u * TILE + TILE - 1 >= k0w) {
+            const unsigned char* sb = pick4<s0>(sl0, sl1, sl2, sl3);
+            const unsigned char* q1s = sb;
+            const unsigned char* q2s = sb + Q_TILE_BYTES;
+            const unsigned char* dos = sb + 2 * Q_TILE_BYTES;
+            const float* sts = (const float*)(sb + ST_OFF);
+            __builtin_amdgcn_s_setprio(1);
+            f32x4 s1[2], s2[2], dp[2];
 #pragma unroll
-            for (int k = 0; k < STAT_FLOATS; ++k) sts[k][tid] = rst[k];
-        }
-        __syncthreads();
-        transpose_tile<D>(q1s, q1t, tid);
-        transpose_tile<D>(q2s, q2t, tid);
-        transpose_tile<DV>(dos, dot, tid);
-        if (u + 1 < n_qt) load_q(u + 1);
-        __syncthreads();
-        if (u < u_wave) continue;
-        // S = Q K^T and dP = dO V^T: lane holds key `key`, queries u*32 + 8 (i/4) + 4 h + i % 4.
-        f32x16 s1, s2, dp;
+            for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { s1[i] = 0.f; s2[i] = 0.f; dp[i] = 0.f; }
+                for (int i = 0; i < 4; ++i) { s1[mb][i] = 0.f; s2[mb][i] = 0.f; dp[mb][i] = 0.f; }
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            s1 = mfma(*(const bf16x8*)(q1s + (a_rd0 ^ (32 * kc))), kb1[kc], s1);
-            s2 = mfma(*(const bf16x8*)(q2s + (a_rd0 ^ (32 * kc))), kb2[kc], s2);
-        }
+                for (int kh = 0; kh < 2; ++kh) {
+                    const int off = (q_rd0 ^ (64 * kh)) + 2048 * mb;
+                    s1[mb] = mfma16(*(const bf16x8*)(q1s + off), kb1[kh], s1[mb]);
+                    s2[mb] = mfma16(*(const bf16x8*)(q2s + off), kb2[kh], s2[mb]);
+                }
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc) dp = mfma(*(const bf16x8*)(dos + vr_off(l32, 2 * kc + h)), vb[kc], dp);
-        float w[16], g1[16], g2[16];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int qo = 8 * g + 4 * h;   // first of the 4 queries of element group g
-            const f32x4 L1 = *(const f32x4*)&sts[0][qo], L2 = *(const f32x4*)&sts[1][qo];
-            const f32x4 E1 = *(const f32x4*)&sts[2][qo], E2 = *(const f32x4*)&sts[3][qo];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * g + e;
-                const int qq = u * TILE + qo + e;
-                const bool vis = qq < N && (!causal || key <= qq);
-                const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -L1[e]));
-                const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -L2[e]));
-                w[i] = vis ? a - lam * b : 0.f;
-                g1[i] = vis ? a * (dp[i] - E1[e]) : 0.f;
-                g2[i] = vis ? b * (dp[i] - E2[e]) : 0.f;   // times -lambda at the end
+                for (int kh = 0; kh < 4; ++kh)
+                    dp[mb] = mfma16(*(const bf16x8*)(dos + (do_rd0 ^ (64 * kh)) + 4096 * mb), vb[kh], dp[mb]);
             }
-        }
-        bf16x8 pw[2], p1[2], p2[2];
+            __builtin_amdgcn_s_setprio(0);
+            const bool edge = (causal && u * TILE < k0w + KW - 1) || u * TILE + TILE > N;
+            float w[8], g1[8], g2[8];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            u32x4 x, y, z;
+            for (int mb = 0; mb < 2; ++mb) {
+                const int qo = 16 * mb + 4 * g;   // first of the lane's 4 queries in block mb
+                const f32x4 L1 = *(const f32x4*)(sts + 0 * TILE + qo), L2 = *(const f32x4*)(sts + 1 * TILE + qo);
+                const f32x4 E1 = *(const f32x4*)(sts + 2 * TILE + qo), E2 = *(const f32x4*)(sts + 3 * TILE + qo);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int x = 4 * mb + i;
+                    const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[mb][i], c, -L1[i]));
+                    const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[mb][i], c, -L2[i]));
+                    w[x] = a - lam * b;
+                    g1[x] = a * (dp[mb][i] - E1[i]);
+                    g2[x] = b * (dp[mb][i] - E2[i]);   // times -lambda at the end
+                }
+            }
+            if (edge) {
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const int qr = u * TILE + 16 * (x >> 2) + 4 * g + (x & 3);
+                    const bool vis = qr < N && (!causal || key <= qr);
+                    w[x] = vis ? w[x] : 0.f;
+                    g1[x] = vis ? g1[x] : 0.f;
+                    g2[x] = vis ? g2[x] : 0.f;
+                }
+            }
+            u32x4 xw, x1, x2;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                x[k] = pack2(w[8 * ks + 2 * k], w[8 * ks + 2 * k + 1]);
-                y[k] = pack2(g1[8 * ks + 2 * k], g1[8 * ks + 2 * k + 1]);
-                z[k] = pack2(g2[8 * ks + 2 * k], g2[8 * ks + 2 * k + 1]);
+                xw[k] = pack2(w[2 * k], w[2 * k + 1]);
+                x1[k] = pack2(g1[2 * k], g1[2 * k + 1]);
+                x2[k] = pack2(g2[2 * k], g2[2 * k + 1]);
             }
-            pw[ks] = __builtin_bit_cast(bf16x8, x);
-            p1[ks] = __builtin_bit_cast(bf16x8, y);
-            p2[ks] = __builtin_bit_cast(bf16x8, z);
-        }
-        // dV^T += dO^T W, dK^T += Q^T ds: A = transposed tiles (feature rows 32 blk + l32, query chunk 2 ks + h).
+            const bf16x8 pw = __builtin_bit_cast(bf16x8, xw), p1 = __builtin_bit_cast(bf16x8, x1),
+                         p2 = __builtin_bit_cast(bf16x8, x2);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int tr = ks ? t_rd1 : t_rd0;
+            for (int fb = 0; fb < 8; ++fb) av[fb] = mfma16(tr_frag(dos + (do_tr0 ^ (32 * fb)), 16 * 256), pw, av[fb]);
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) av[cb] = mfma(*(const bf16x8*)(dot + tr + 2048 * cb), pw[ks], av[cb]);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                ak1[nb] = mfma(*(const bf16x8*)(q1t + tr + 2048 * nb), p1[ks], ak1[nb]);
-                ak2[nb] = mfma(*(const bf16x8*)(q2t + tr + 2048 * nb), p2[ks], ak2[nb]);
+            for (int fb = 0; fb < 4; ++fb) {
+                ak1[fb] = mfma16(tr_frag(q1s + (q_tr0 ^ (32 * fb)), 16 * 128), p1, ak1[fb]);
+                ak2[fb] = mfma16(tr_frag(q2s + (q_tr0 ^ (32 * fb)), 16 * 128), p2, ak2[fb]);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
+        // The loads of this iteration and the previous one may stay in flight past the barrier; tile u + 1 has
+        // landed.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * DKDV_LOADS));
+        lds_barrier();
+    };
+    for (int j = 0; j < n_iter; j += 4) {
+        step(Slot<0>{}, j);
+        if (j + 1 < n_iter) step(Slot<1>{}, j + 1);
+        if (j + 2 < n_iter) step(Slot<2>{}, j + 2);
+        if (j + 3 < n_iter) step(Slot<3>{}, j + 3);
     }
+    // Drain the trailing prefetches before the workgroup can retire (their LDS writes must not outlive it).
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     if (key >= N) return;
     const float sc1 = 0.125f, sc2 = -lam * 0.125f;
-    uint16_t* r1 = dk1 + hqk + (size_t)key * D + 4 * h;
-    uint16_t* r2 = dk2 + hqk + (size_t)key * D + 4 * h;
-    uint16_t* rvv = dv + hv + (size_t)key * DV + 4 * h;
+    uint16_t* r1 = dk1 + hqk + (size_t)key * D + 4 * g;
+    uint16_t* r2 = dk2 + hqk + (size_t)key * D + 4 * g;
+    uint16_t* rvv = dv + hv + (size_t)key * DV + 4 * g;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
+    for (int fb = 0; fb < 4; ++fb) {
+        u32x2 w1, w2;
+        w1[0] = pack2(ak1[fb][0] * sc1, ak1[fb][1] * sc1);
+        w1[1] = pack2(ak1[fb][2] * sc1, ak1[fb][3] * sc1);
+        w2[0] = pack2(ak2[fb][0] * sc2, ak2[fb][1] * sc2);
+        w2[1] = pack2(ak2[fb][2] * sc2, ak2[fb][3] * sc2);
+        *(u32x2*)(r1 + 16 * fb) = w1;
+        *(u32x2*)(r2 + 16 * fb) = w2;
+    }
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            u32x2 w1, w2;
-            w1[0] = pack2(ak1[nb][4 * g4] * sc1, ak1[nb][4 * g4 + 1] * sc1);
-            w1[1] = pack2(ak1[nb][4 * g4 + 2] * sc1, ak1[nb][4 * g4 + 3] * sc1);
-            w2[0] = pack2(ak2[nb][4 * g4] * sc2, ak2[nb][4 * g4 + 1] * sc2);
-            w2[1] = pack2(ak2[nb][4 * g4 + 2] * sc2, ak2[nb][4 * g4 + 3] * sc2);
-            *(u32x2*)(r1 + 32 * nb + 8 * g4) = w1;
-            *(u32x2*)(r2 + 32 * nb + 8 * g4) = w2;
-        }
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            u32x2 wv;
-            wv[0] = pack2(av[cb][4 * g4], av[cb][4 * g4 + 1]);
-            wv[1] = pack2(av[cb][4 * g4 + 2], av[cb][4 * g4 + 3]);
-            *(u32x2*)(rvv + 32 * cb + 8 * g4) = wv;
-        }
+    for (int fb = 0; fb < 8; ++fb) {
+        u32x2 wv;
+        wv[0] = pack2(av[fb][0], av[fb][1]);
+        wv[1] = pack2(av[fb][2], av[fb][3]);
+        *(u32x2*)(rvv + 16 * fb) = wv;
     }
 }
 
@@ -476,7 +582,8 @@ hipError_t launch_bwd_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uin
     const int64_t pre_blocks = (rows + WAVES - 1) / WAVES;
     const int n_blocks = (int)((N + BLOCK - 1) / BLOCK);
     const int64_t grid = (int64_t)n_blocks * BH;
-    if (pre_blocks > 0x7fffffff || grid > 0x7fffffff) return hipErrorInvalidValue;
+    const int64_t kv_grid = (int64_t)((N + KBLK - 1) / KBLK) * BH;
+    if (pre_blocks > 0x7fffffff || grid > 0x7fffffff || kv_grid > 0x7fffffff) return hipErrorInvalidValue;
     if (rows == 0) {   // only dlambda (zeros)
         hipLaunchKernelGGL(bwd_dlambda_kernel, dim3((unsigned)H), dim3(THREADS), 0, stream, dl_rows, dlambda, (int)B,
                            (int)H, 0);
@@ -486,8 +593,8 @@ hipError_t launch_bwd_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uin
                        dl_rows, rows, (int)N, ep);
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)grid), dim3(THREADS), 0, stream, q1, k1, q2, k2, v, dO, stats,
                        dq1, dq2, (int)BH, (int)N, n_blocks, causal ? 1 : 0, ep);
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)grid), dim3(THREADS), 0, stream, q1, k1, q2, k2, v, dO, stats,
-                       dk1, dk2, dv, (int)BH, (int)N, n_blocks, causal ? 1 : 0, ep);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_grid), dim3(THREADS), 0, stream, q1, k1, q2, k2, v, dO,
+                       stats, dk1, dk2, dv, (int)BH, (int)N, causal ? 1 : 0, ep);
     hipLaunchKernelGGL(bwd_dlambda_kernel, dim3((unsigned)H), dim3(THREADS), 0, stream, dl_rows, dlambda, (int)B,
                        (int)H, (int)N);
     return hipGetLastError();
