@@ -16,8 +16,9 @@
 // Kernels (all launched on one stream, in order):
 //   1. bwd_pre:      per row, dO (bf16) and (lse1, lse2, E1, E2), and the row's share of dlambda.
 //   2. bwd_dq:       per 128-row query block (4 waves x 32 rows), loop over key tiles up to the diagonal:
-//                    S^T = K Q^T and dP^T = V dO^T on MFMA, ds in registers, dQ^T += K^T ds^T with K^T tiles
-//                    transposed in LDS.  Same register plan as the forward (two waves per SIMD).
+//                    S^T = K Q^T and dP^T = V dO^T on MFMA, ds in registers, dQ^T += K^T ds^T with the K^T
+//                    operands read from the row-major K tiles with ds_read_b64_tr_b16.  Same register plan and
+//                    load rings as the forward (two waves per SIMD).
 //   3. bwd_dkdv:     per 64-key block (4 waves x 16 keys, v_mfma_f32_16x16x32_bf16), loop over query tiles from the
 //                    diagonal: S = Q K^T and dP = dO V^T with the wave's K and V rows held in registers, then
 //                    dV^T += dO^T W and dK^T += Q^T ds, the transposed operands read from the row-major tiles with
@@ -25,8 +26,7 @@
 //                    memory to LDS (buffer_load ... lds) through a 4-slot ring, three tiles ahead, one barrier per
 //                    tile.
 //   4. bwd_dlambda:  per head, a fixed-order sum of the rows' dlambda shares (deterministic).
-// In bwd_dq, tiles move global -> registers -> LDS (one tile ahead), are transposed in LDS with ds_read_b64_tr_b16,
-// and three workgroup barriers separate loading, transposing and computing.
+
 #include "launch.h"
 #include "tiles.h"
 
@@ -42,63 +42,30 @@ constexpr int BLOCK = TILE * WAVES;   // rows (dq) or keys (dkdv) per workgroup
 constexpr int STAT_FLOATS = 4;    // per row in the workspace: lse1, lse2, E1, E2
 
 // ---------------------------------------------------------------------------------------------------------------
-// Tile staging: a 32-row tile of width W (64 or 128 bf16) is read from global memory into registers (16 bytes per
-// chunk, rows at or beyond N read as zero), then written to LDS row-major with the forward's swizzles (k_off for
-// W = 64, vr_off for W = 128), then transposed into a [W][32] tile (vt_off, rows in key_pos order).
+// LDS tile layouts and helpers shared by the dQ and dK/dV kernels.
 // ---------------------------------------------------------------------------------------------------------------
-template <int W>
-__device__ __forceinline__ int row_off(int row, int chunk) {
-    if constexpr (W == 64) return k_off(row, chunk);
-    else return vr_off(row, chunk);
+// Q tile: row r (query) of 128 bytes; chunk c at c ^ q_sw(r).  Rows r and r + 2 (same LDS bank half) differ in
+// bit 1 of the swizzle, so a transposing read's 4 rows x 32 bytes and a 16-row read of one chunk both hit distinct
+// bank quads.
+__device__ __forceinline__ int q_sw(int r) {
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
+}
+__device__ __forceinline__ int q_off(int r, int c) { return r * 128 + ((c ^ q_sw(r)) << 4); }
+// dO tile: row r of 256 bytes; chunk c at c ^ do_sw(r), a bijection of r % 16 onto the 16 chunk positions.
+__device__ __forceinline__ int do_sw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+__device__ __forceinline__ int do_off(int r, int c) { return r * 256 + ((c ^ do_sw(r)) << 4); }
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Chunks of one tile per thread.
-template <int W> constexpr int chunks_per_thread() { return TILE * W * 2 / 16 / THREADS; }   // 1 (W=64), 2 (W=128)
-
-template <int W>
-__device__ __forceinline__ void load_tile(const uint16_t* head, int row0, int N, int tid, u32x4 (&r)[chunks_per_thread<W>()]) {
-    constexpr int CPR = W / 8;   // chunks per row
-#pragma unroll
-    for (int k = 0; k < chunks_per_thread<W>(); ++k) {
-        const int u = tid + THREADS * k;
-        const int row = u / CPR, chunk = u % CPR;
-        const int g = row0 + row;
-        r[k] = g < N ? *(const u32x4*)(head + (size_t)g * W + chunk * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-template <int W>
-__device__ __forceinline__ void store_tile(unsigned char* lds, int tid, const u32x4 (&r)[chunks_per_thread<W>()]) {
-    constexpr int CPR = W / 8;
-#pragma unroll
-    for (int k = 0; k < chunks_per_thread<W>(); ++k) {
-        const int u = tid + THREADS * k;
-        *(u32x4*)(lds + row_off<W>(u / CPR, u % CPR)) = r[k];
-    }
-}
-
-// Row-major [32][W] tile -> [W][32] tile.  A 16-lane group transposes a block of 4 rows x 16 channels with one
-// ds_read_b64_tr_b16 (lane 4 jj + q supplies row jj, channels 4 q .. 4 q + 3; lane i receives channel i for the
-// 4 rows) and one 64-bit write.  Block b of group g: channel group (g + 16 b) % (W / 16), row block
-// (g + 16 b) / (W / 16).
-template <int W>
-__device__ __forceinline__ void transpose_tile(const unsigned char* src, unsigned char* dst, int tid) {
-    constexpr int CG = W / 16;
-    constexpr int PER = 8 * CG / 16;   // blocks per 16-lane group: 2 (W=64) or 4 (W=128)
-    const int grp = tid >> 4, gl = tid & 15;
-    s16x4 x[PER];
-#pragma unroll
-    for (int b = 0; b < PER; ++b) {
-        const int blk = grp + 16 * b, cg = blk % CG, kb = blk / CG;
-        const int row = 4 * kb + (gl >> 2), ch0 = 16 * cg + 4 * (gl & 3);
-        x[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + row_off<W>(row, ch0 >> 3) + (ch0 & 7) * 2));
-    }
-#pragma unroll
-    for (int b = 0; b < PER; ++b) {
-        const int blk = grp + 16 * b, cg = blk % CG, kb = blk / CG;
-        const int pos = key_pos(4 * kb);
-        *(s16x4*)(dst + vt_off(16 * cg + gl, pos >> 3) + (pos & 7) * 2) = x[b];
-    }
+template <int V> struct Slot { static constexpr int value = V; };
+template <int S, class T> __device__ __forceinline__ T* pick4(T* a, T* b, T* c, T* d) {
+    if constexpr (S % 4 == 0) return a;
+    else if constexpr (S % 4 == 1) return b;
+    else if constexpr (S % 4 == 2) return c;
+    else return d;
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -152,14 +119,20 @@ __global__ __launch_bounds__(THREADS) void bwd_pre_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------------------------------------------------------
 // 2. dQ: per 128-row query block; lane owns query row q0w + l32 (as in the forward).
 // ---------------------------------------------------------------------------------------------------------------
+// K1, K2 and V tiles come straight from global memory to LDS (buffer_load ... lds) through 4-slot rings, three
+// tiles ahead, one barrier per tile.  K tiles use the q_sw swizzle (16-row 128-bit reads for S^T = K Q^T and
+// 4-row transposing reads for dQ^T += K^T ds^T are both free of bank conflicts); the V tile, read only by rows for
+// dP^T = V dO^T, uses do_sw.
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1,
                    const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
                    const uint16_t* __restrict__ gv, const uint16_t* __restrict__ gdo,
                    const float* __restrict__ stats, uint16_t* __restrict__ dq1, uint16_t* __restrict__ dq2,
                    int BH, int N, int n_blocks, int causal, Epilogue ep) {
-    __shared__ __attribute__((aligned(16))) unsigned char k1s[TILE * D * 2], k2s[TILE * D * 2], vs[TILE * DV * 2];
-    __shared__ __attribute__((aligned(16))) unsigned char k1t[TILE * D * 2], k2t[TILE * D * 2];
+    constexpr int K_TILE = TILE * D * 2, V_TILE = TILE * DV * 2;
+    __shared__ __attribute__((aligned(16))) unsigned char kr0[2 * K_TILE], kr1[2 * K_TILE], kr2[2 * K_TILE],
+        kr3[2 * K_TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char vr0[V_TILE], vr1[V_TILE], vr2[V_TILE], vr3[V_TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -170,7 +143,48 @@ void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict_
     const int q0 = qb * BLOCK, q0w = q0 + TILE * wave;
     const size_t hqk = (size_t)bh * N * D, hv = (size_t)bh * N * DV;
     const int q = q0w + l32, qc = min(q, N - 1);
+    const float c = LOG2E * 0.125f;
 
+    // Per-head buffer resources: rows at or beyond N read as zero.  N is at most 2^23, so the offsets fit.
+    const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc((void*)(gk1 + hqk), (short)0, N * (D * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk2 = __builtin_amdgcn_make_buffer_rsrc((void*)(gk2 + hqk), (short)0, N * (D * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(gv + hv), (short)0, N * (DV * 2), 0x00020000);
+
+    // Direct loads per wave and tile: K1 rows 8 wave .. + 7, K2 the same, V rows 4 p .. 4 p + 3 for pieces
+    // p = wave and wave + 4 (lane L writes position 16 L of a 1 KiB piece).  Issued unconditionally, also past the
+    // end (out of range: zeros), so every iteration issues the same number.
+    const int krow = 8 * wave + (lane >> 3);
+    const unsigned k_voff = (unsigned)krow * (D * 2) + ((((lane & 7) ^ q_sw(krow))) << 4);
+    unsigned v_voff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = 4 * (wave + WAVES * j) + (lane >> 4);
+        v_voff[j] = (unsigned)r * (DV * 2) + ((((lane & 15) ^ do_sw(r))) << 4);
+    }
+    auto issue = [&](auto S, int t) __attribute__((always_inline)) {
+        constexpr int s0 = decltype(S)::value;
+        unsigned char* ks = pick4<s0>(kr0, kr1, kr2, kr3);
+        unsigned char* vs = pick4<s0>(vr0, vr1, vr2, vr3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk1, (lds_void*)(ks + 1024 * wave), 16,
+                                                 (int)(k_voff + (unsigned)t * K_TILE), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk2, (lds_void*)(ks + K_TILE + 1024 * wave), 16,
+                                                 (int)(k_voff + (unsigned)t * K_TILE), 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vs + 1024 * (wave + WAVES * j)), 16,
+                                                     (int)(v_voff[j] + (unsigned)t * V_TILE), 0, 0, 0);
+    };
+    constexpr int DQ_LOADS = 4;
+
+    const int q_last = min(N, q0 + BLOCK) - 1;
+    const int n_tiles = causal ? (q_last / TILE + 1) : (N + TILE - 1) / TILE;
+    const int t_last = causal ? min(n_tiles - 1, (q0w + TILE - 1) / TILE) : n_tiles - 1;
+    issue(Slot<0>{}, 0);
+    issue(Slot<1>{}, 1);
+    issue(Slot<2>{}, 2);
+
+    // The wave's Q1, Q2 and dO rows as B operands and the row's statistics; loaded after the first tiles' direct
+    // loads and used before the loop, so the compiler places no wait for them inside it.
     bf16x8 qa[4], qbf[4], dob[8];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
@@ -179,9 +193,15 @@ void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict_
     }
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) dob[kc] = *(const bf16x8*)(gdo + hv + (size_t)qc * DV + 16 * kc + 8 * h);
-    const f32x4 st = *(const f32x4*)(stats + ((size_t)bh * N + qc) * STAT_FLOATS);
+    f32x4 st = *(const f32x4*)(stats + ((size_t)bh * N + qc) * STAT_FLOATS);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) asm volatile("" ::"v"(qa[kc]), "v"(qbf[kc]));
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) asm volatile("" ::"v"(dob[kc]));
+    asm volatile("" ::"v"(st));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
     const float lse1 = st[0], lse2 = st[1], e1 = st[2], e2 = st[3];
-    const float c = LOG2E * 0.125f;
 
     f32x16 acc1[2], acc2[2];   // dQ^T blocks: d = 32 mb + 8 (i / 4) + 4 h + i % 4, query = lane's row
 #pragma unroll
@@ -189,75 +209,96 @@ void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict_
 #pragma unroll
         for (int i = 0; i < 16; ++i) { acc1[mb][i] = 0.f; acc2[mb][i] = 0.f; }
 
-    const int q_last = min(N, q0 + BLOCK) - 1;
-    const int n_tiles = causal ? (q_last / TILE + 1) : (N + TILE - 1) / TILE;
-    const int t_last = causal ? min(n_tiles - 1, (q0w + TILE - 1) / TILE) : n_tiles - 1;
-    const int k_rd0 = k_off(l32, h);
-    const int t_rd0 = vt_off(l32, h), t_rd1 = vt_off(l32, 2 + h);
+    // Read offsets.  S^T's A operand: K row l32, chunk 2 kc + h: q_off(l32, 2 kc + h) = k_rd0 ^ (32 kc).  dP^T's
+    // A operand: V row l32, chunk 2 kc + h: do_off(l32, 2 kc + h) = v_rd0 ^ (32 kc).  dQ^T's A operand (K^T, feature
+    // block mb, key half ks): lane 4 jj + qq of 16-lane group G supplies key row 16 ks + 4 h + jj (first read) or
+    // 16 ks + 8 + 4 h + jj (second), features 32 mb + 16 (G & 1) + 4 qq .. + 3, and receives feature
+    // 32 mb + l32 of those 4 keys; mb XORs 64 mb into the offset, ks adds 2 KiB.
+    const int k_rd0 = q_off(l32, h), v_rd0 = do_off(l32, h);
+    const int grp = (lane >> 4) & 1, jj = (lane >> 2) & 3, qq = lane & 3;
+    const int kt_a = q_off(4 * h + jj, 2 * grp + (qq >> 1)) + 8 * (qq & 1);
+    const int kt_b = q_off(8 + 4 * h + jj, 2 * grp + (qq >> 1)) + 8 * (qq & 1);
+    auto kt_frag = [&](const unsigned char* p, int mb, int ks) __attribute__((always_inline)) {
+        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + (kt_a ^ (64 * mb)) + 2048 * ks));
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + (kt_b ^ (64 * mb)) + 2048 * ks));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 
-    u32x4 rk1[1], rk2[1], rv[2];
-    load_tile<D>(gk1 + hqk, 0, N, tid, rk1);
-    load_tile<D>(gk2 + hqk, 0, N, tid, rk2);
-    load_tile<DV>(gv + hv, 0, N, tid, rv);
-    for (int t = 0; t < n_tiles; ++t) {
-        __syncthreads();
-        store_tile<D>(k1s, tid, rk1);
-        store_tile<D>(k2s, tid, rk2);
-        store_tile<DV>(vs, tid, rv);
-        __syncthreads();
-        transpose_tile<D>(k1s, k1t, tid);
-        transpose_tile<D>(k2s, k2t, tid);
-        if (t + 1 < n_tiles) {
-            load_tile<D>(gk1 + hqk, (t + 1) * TILE, N, tid, rk1);
-            load_tile<D>(gk2 + hqk, (t + 1) * TILE, N, tid, rk2);
-            load_tile<DV>(gv + hv, (t + 1) * TILE, N, tid, rv);
-        }
-        __syncthreads();
-        if (t > t_last) continue;
-        // S^T = K Q^T (both maps) and dP^T = V dO^T: lane holds query q, keys t*32 + 8 (i/4) + 4 h + i % 4.
-        f32x16 s1, s2, dp;
+    auto step = [&](auto S, int t) __attribute__((always_inline)) {   // S = t % 4
+        constexpr int s0 = decltype(S)::value;
+        issue(Slot<(s0 + 3) % 4>{}, t + 3);
+        if (t <= t_last) {
+            const unsigned char* k1s = pick4<s0>(kr0, kr1, kr2, kr3);
+            const unsigned char* k2s = k1s + K_TILE;
+            const unsigned char* vs = pick4<s0>(vr0, vr1, vr2, vr3);
+            __builtin_amdgcn_s_setprio(1);
+            // S^T = K Q^T (both maps) and dP^T = V dO^T: lane holds query q, keys t*32 + 8 (i/4) + 4 h + i % 4.
+            f32x16 s1, s2, dp;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { s1[i] = 0.f; s2[i] = 0.f; dp[i] = 0.f; }
+            for (int i = 0; i < 16; ++i) { s1[i] = 0.f; s2[i] = 0.f; dp[i] = 0.f; }
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            s1 = mfma(*(const bf16x8*)(k1s + (k_rd0 ^ (32 * kc))), qa[kc], s1);
-            s2 = mfma(*(const bf16x8*)(k2s + (k_rd0 ^ (32 * kc))), qbf[kc], s2);
-        }
-#pragma unroll
-        for (int kc = 0; kc < 8; ++kc) dp = mfma(*(const bf16x8*)(vs + vr_off(l32, 2 * kc + h)), dob[kc], dp);
-        const int kv0 = t * TILE;
-        float g1[16], g2[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = kv0 + 8 * (i >> 2) + 4 * h + (i & 3);
-            const bool vis = key < N && (!causal || key <= q);
-            const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -lse1));
-            const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -lse2));
-            g1[i] = vis ? a * (dp[i] - e1) : 0.f;
-            g2[i] = vis ? b * (dp[i] - e2) : 0.f;   // times -lambda at the end
-        }
-        bf16x8 p1[2], p2[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            u32x4 a, b;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                a[k] = pack2(g1[8 * ks + 2 * k], g1[8 * ks + 2 * k + 1]);
-                b[k] = pack2(g2[8 * ks + 2 * k], g2[8 * ks + 2 * k + 1]);
+            for (int kc = 0; kc < 4; ++kc) {
+                s1 = mfma(*(const bf16x8*)(k1s + (k_rd0 ^ (32 * kc))), qa[kc], s1);
+                s2 = mfma(*(const bf16x8*)(k2s + (k_rd0 ^ (32 * kc))), qbf[kc], s2);
             }
-            p1[ks] = __builtin_bit_cast(bf16x8, a);
-            p2[ks] = __builtin_bit_cast(bf16x8, b);
-        }
-        // dQ^T += K^T ds^T: A = K^T rows d = 32 mb + l32, key chunk 2 ks + h.
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+            for (int kc = 0; kc < 8; ++kc) dp = mfma(*(const bf16x8*)(vs + (v_rd0 ^ (32 * kc))), dob[kc], dp);
+            __builtin_amdgcn_s_setprio(0);
+            const int kv0 = t * TILE;
+            const bool edge = (causal && kv0 + TILE - 1 > q0w) || kv0 + TILE > N;
+            float g1[16], g2[16];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const int off = (ks ? t_rd1 : t_rd0) + 2048 * mb;
-                acc1[mb] = mfma(*(const bf16x8*)(k1t + off), p1[ks], acc1[mb]);
-                acc2[mb] = mfma(*(const bf16x8*)(k2t + off), p2[ks], acc2[mb]);
+            for (int i = 0; i < 16; ++i) {
+                const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -lse1));
+                const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[i], c, -lse2));
+                g1[i] = a * (dp[i] - e1);
+                g2[i] = b * (dp[i] - e2);   // times -lambda at the end
             }
+            if (edge) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kv0 + 8 * (i >> 2) + 4 * h + (i & 3);
+                    const bool vis = key < N && (!causal || key <= q);
+                    g1[i] = vis ? g1[i] : 0.f;
+                    g2[i] = vis ? g2[i] : 0.f;
+                }
+            }
+            bf16x8 p1[2], p2[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                u32x4 a, b;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    a[k] = pack2(g1[8 * ks + 2 * k], g1[8 * ks + 2 * k + 1]);
+                    b[k] = pack2(g2[8 * ks + 2 * k], g2[8 * ks + 2 * k + 1]);
+                }
+                p1[ks] = __builtin_bit_cast(bf16x8, a);
+                p2[ks] = __builtin_bit_cast(bf16x8, b);
+            }
+            __builtin_amdgcn_s_setprio(1);
+            // dQ^T += K^T ds^T.
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    acc1[mb] = mfma(kt_frag(k1s, mb, ks), p1[ks], acc1[mb]);
+                    acc2[mb] = mfma(kt_frag(k2s, mb, ks), p2[ks], acc2[mb]);
+                }
+            __builtin_amdgcn_s_setprio(0);
+        }
+        // The loads of this iteration and the previous one may stay in flight past the barrier; tile t + 1 has
+        // landed.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * DQ_LOADS));
+        lds_barrier();
+    };
+    for (int t = 0; t < n_tiles; t += 4) {
+        step(Slot<0>{}, t);
+        if (t + 1 < n_tiles) step(Slot<1>{}, t + 1);
+        if (t + 2 < n_tiles) step(Slot<2>{}, t + 2);
+        if (t + 3 < n_tiles) step(Slot<3>{}, t + 3);
     }
+    // Drain the trailing prefetches before the workgroup can retire (their LDS writes must not outlive it).
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     if (q >= N) return;
     const float sc1 = 0.125f, sc2 = -lambda_of(ep, bh) * 0.125f;
     uint16_t* r1 = dq1 + hqk + (size_t)q * D + 4 * h;
@@ -298,30 +339,6 @@ constexpr int ST_TILE_BYTES = TILE * STAT_FLOATS * 4;
 constexpr int SLOT_BYTES = 2 * Q_TILE_BYTES + DO_TILE_BYTES + ST_TILE_BYTES;   // Q1 | Q2 | dO | stats
 constexpr int ST_OFF = 2 * Q_TILE_BYTES + DO_TILE_BYTES;
 constexpr int DKDV_LOADS = 5;                     // direct loads per wave and tile: Q1, Q2, 2 x dO, stats
-
-// Q tile: row r (query) of 128 bytes; chunk c at c ^ q_sw(r).  Rows r and r + 2 (same LDS bank half) differ in
-// bit 1 of the swizzle, so a transposing read's 4 rows x 32 bytes and a 16-row read of one chunk both hit distinct
-// bank quads.
-__device__ __forceinline__ int q_sw(int r) {
-    const int x = (r >> 1) & 7;
-    return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
-}
-__device__ __forceinline__ int q_off(int r, int c) { return r * 128 + ((c ^ q_sw(r)) << 4); }
-// dO tile: row r of 256 bytes; chunk c at c ^ do_sw(r), a bijection of r % 16 onto the 16 chunk positions.
-__device__ __forceinline__ int do_sw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
-__device__ __forceinline__ int do_off(int r, int c) { return r * 256 + ((c ^ do_sw(r)) << 4); }
-
-__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-template <int V> struct Slot { static constexpr int value = V; };
-template <int S, class T> __device__ __forceinline__ T* pick4(T* a, T* b, T* c, T* d) {
-    if constexpr (S % 4 == 0) return a;
-    else if constexpr (S % 4 == 1) return b;
-    else if constexpr (S % 4 == 2) return c;
-    else return d;
-}
 
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1,
