@@ -22,8 +22,8 @@
 //   3. bwd_dkdv:     per 64-key block (4 waves x 16 keys, v_mfma_f32_16x16x32_bf16), loop over query tiles from the
 //                    diagonal: S = Q K^T and dP = dO V^T with the wave's K and V rows held in registers, then
 //                    dV^T += dO^T W and dK^T += Q^T ds, the transposed operands read from the row-major tiles with
-//                    ds_read_b64_tr_b16.  Two waves per SIMD.  Q, dO and stats tiles come straight from global
-//                    memory to LDS (buffer_load ... lds) through a 4-slot ring, three tiles ahead, one barrier per
+//                    ds_read_b64_tr_b16.  Three waves per SIMD.  Q, dO and stats tiles come straight from global
+//                    memory to LDS (buffer_load ... lds) through a 3-slot ring, two tiles ahead, one barrier per
 //                    tile.
 //   4. bwd_dlambda:  per head, a fixed-order sum of the rows' dlambda shares (deterministic).
 
@@ -61,6 +61,11 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 }
 
 template <int V> struct Slot { static constexpr int value = V; };
+template <int S, class T> __device__ __forceinline__ T* pick3(T* a, T* b, T* c) {
+    if constexpr (S % 3 == 0) return a;
+    else if constexpr (S % 3 == 1) return b;
+    else return c;
+}
 template <int S, class T> __device__ __forceinline__ T* pick4(T* a, T* b, T* c, T* d) {
     if constexpr (S % 4 == 0) return a;
     else if constexpr (S % 4 == 1) return b;
@@ -340,14 +345,13 @@ constexpr int SLOT_BYTES = 2 * Q_TILE_BYTES + DO_TILE_BYTES + ST_TILE_BYTES;   /
 constexpr int ST_OFF = 2 * Q_TILE_BYTES + DO_TILE_BYTES;
 constexpr int DKDV_LOADS = 5;                     // direct loads per wave and tile: Q1, Q2, 2 x dO, stats
 
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1,
                      const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
                      const uint16_t* __restrict__ gv, const uint16_t* __restrict__ gdo,
                      const float* __restrict__ stats, uint16_t* __restrict__ dk1, uint16_t* __restrict__ dk2,
                      uint16_t* __restrict__ dv, int BH, int N, int causal, Epilogue ep) {
-    __shared__ __attribute__((aligned(16))) unsigned char sl0[SLOT_BYTES], sl1[SLOT_BYTES], sl2[SLOT_BYTES],
-        sl3[SLOT_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char sl0[SLOT_BYTES], sl1[SLOT_BYTES], sl2[SLOT_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -383,7 +387,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
     }
     const unsigned st_voff = (unsigned)(lane & 31) * (STAT_FLOATS * 4) + 4u * (unsigned)wave;
     auto issue = [&](auto S, int u) __attribute__((always_inline)) {
-        unsigned char* s = pick4<decltype(S)::value>(sl0, sl1, sl2, sl3);
+        unsigned char* s = pick3<decltype(S)::value>(sl0, sl1, sl2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rq1, (lds_void*)(s + 1024 * wave), 16,
                                                  (int)(q_voff + (unsigned)u * (TILE * D * 2)), 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rq2, (lds_void*)(s + Q_TILE_BYTES + 1024 * wave), 16,
@@ -402,7 +406,6 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
     const int n_iter = n_qt - u_first;
     if (n_iter > 0) issue(Slot<0>{}, u_first);
     if (n_iter > 0) issue(Slot<1>{}, u_first + 1);
-    if (n_iter > 0) issue(Slot<2>{}, u_first + 2);
 
     // The wave's K1, K2 and V rows as B operands (k = feature, n = key): lane holds feature 32 kh + 8 g .. + 7 of
     // key `key`.  Loaded after the first tiles' direct loads and used before the loop, so the compiler waits for
@@ -449,9 +452,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
     auto step = [&](auto S, int j) __attribute__((always_inline)) {   // S = j % 4
         constexpr int s0 = decltype(S)::value;
         const int u = u_first + j;
-        issue(Slot<(s0 + 3) % 4>{}, u + 3);
+        issue(Slot<(s0 + 2) % 3>{}, u + 2);
         if (!causal || u * TILE + TILE - 1 >= k0w) {
-            const unsigned char* sb = pick4<s0>(sl0, sl1, sl2, sl3);
+            const unsigned char* sb = pick3<s0>(sl0, sl1, sl2);
             const unsigned char* q1s = sb;
             const unsigned char* q2s = sb + Q_TILE_BYTES;
             const unsigned char* dos = sb + 2 * Q_TILE_BYTES;
@@ -519,16 +522,15 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
             }
             __builtin_amdgcn_s_setprio(0);
         }
-        // The loads of this iteration and the previous one may stay in flight past the barrier; tile u + 1 has
-        // landed.
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * DKDV_LOADS));
+        // The loads of this iteration (tile u + 2, into the slot tile u - 1 left) may stay in flight past the
+        // barrier; tile u + 1 has landed.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(DKDV_LOADS));
         lds_barrier();
     };
-    for (int j = 0; j < n_iter; j += 4) {
+    for (int j = 0; j < n_iter; j += 3) {
         step(Slot<0>{}, j);
         if (j + 1 < n_iter) step(Slot<1>{}, j + 1);
         if (j + 2 < n_iter) step(Slot<2>{}, j + 2);
-        if (j + 3 < n_iter) step(Slot<3>{}, j + 3);
     }
     // Drain the trailing prefetches before the workgroup can retire (their LDS writes must not outlive it).
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
@@ -559,18 +561,29 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
 // ---------------------------------------------------------------------------------------------------------------
 // 4. dlambda: one workgroup per head, fixed summation order.
 // ---------------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(THREADS) void bwd_dlambda_kernel(const float* __restrict__ dl_rows, float* __restrict__ dlambda,
-                                                              int B, int H, int N) {
-    __shared__ float red[THREADS];
+constexpr int DL_THREADS = 1024;
+constexpr int DL_UNROLL = 4;
+static_assert(DL_UNROLL == 4, "the per-thread total below adds four accumulators");
+__global__ __launch_bounds__(DL_THREADS) void bwd_dlambda_kernel(const float* __restrict__ dl_rows,
+                                                                 float* __restrict__ dlambda, int B, int H, int N) {
+    __shared__ float red[DL_THREADS];
     const int hh = blockIdx.x, tid = threadIdx.x;
-    float acc = 0.f;
+    // Each thread sums a fixed subset of the head's B x N row shares in a fixed order, with DL_UNROLL independent
+    // accumulators so that as many loads are in flight; then a fixed-shape tree over the threads.
+    float acc[DL_UNROLL];
+#pragma unroll
+    for (int k = 0; k < DL_UNROLL; ++k) acc[k] = 0.f;
     for (int b = 0; b < B; ++b) {
         const float* p = dl_rows + ((size_t)b * H + hh) * N;
-        for (int i = tid; i < N; i += THREADS) acc += p[i];
+        int i = tid;
+        for (; i + (DL_UNROLL - 1) * DL_THREADS < N; i += DL_UNROLL * DL_THREADS)
+#pragma unroll
+            for (int k = 0; k < DL_UNROLL; ++k) acc[k] += p[i + k * DL_THREADS];
+        for (; i < N; i += DL_THREADS) acc[0] += p[i];
     }
-    red[tid] = acc;
+    red[tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     __syncthreads();
-    for (int s = THREADS / 2; s > 0; s >>= 1) {
+    for (int s = DL_THREADS / 2; s > 0; s >>= 1) {
         if (tid < s) red[tid] += red[tid + s];
         __syncthreads();
     }
@@ -602,8 +615,8 @@ hipError_t launch_bwd_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uin
     const int64_t kv_grid = (int64_t)((N + KBLK - 1) / KBLK) * BH;
     if (pre_blocks > 0x7fffffff || grid > 0x7fffffff || kv_grid > 0x7fffffff) return hipErrorInvalidValue;
     if (rows == 0) {   // only dlambda (zeros)
-        hipLaunchKernelGGL(bwd_dlambda_kernel, dim3((unsigned)H), dim3(THREADS), 0, stream, dl_rows, dlambda, (int)B,
-                           (int)H, 0);
+        hipLaunchKernelGGL(bwd_dlambda_kernel, dim3((unsigned)H), dim3(DL_THREADS), 0, stream, dl_rows, dlambda,
+                           (int)B, (int)H, 0);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)pre_blocks), dim3(THREADS), 0, stream, dy, saved, dO, stats,
@@ -612,7 +625,7 @@ hipError_t launch_bwd_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uin
                        dq1, dq2, (int)BH, (int)N, n_blocks, causal ? 1 : 0, ep);
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_grid), dim3(THREADS), 0, stream, q1, k1, q2, k2, v, dO,
                        stats, dk1, dk2, dv, (int)BH, (int)N, causal ? 1 : 0, ep);
-    hipLaunchKernelGGL(bwd_dlambda_kernel, dim3((unsigned)H), dim3(THREADS), 0, stream, dl_rows, dlambda, (int)B,
+    hipLaunchKernelGGL(bwd_dlambda_kernel, dim3((unsigned)H), dim3(DL_THREADS), 0, stream, dl_rows, dlambda, (int)B,
                        (int)H, (int)N);
     return hipGetLastError();
 }
