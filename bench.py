@@ -11,6 +11,8 @@ events recorded on the stream it is launched on.  Prints ONE JSON line.
   cpu_baseline  the double-precision CPU oracle on the same prefill workload (all rows by default)
   decode_multi  (not part of the step) multi-token decode, 4 new tokens per sequence against ragged caches of
             4096..8192 rows at B64 H16: GB/s of the valid cache rows read
+  decode_paged  (not part of the step) the decode workload read from 64-row pages of a shuffled page pool through
+            a block table: GB/s of the same bytes as decode
   backward  (not part of the step) the training forward and the backward pass on the prefill workload with a
             synthetic output gradient, timed separately: 1792 FLOP per unmasked pair on the matrix cores (the
             dQ kernel recomputes both score maps and dP: 768; the dK/dV kernel recomputes them and forms dV, dK1,
@@ -124,6 +126,7 @@ def bench_decode_multi(da, stream, k1, k2, v, Dc, steps, T=4):
     q2 = torch.randn(B, H, T, d, device=dev, generator=g).to(torch.bfloat16)
     out = torch.empty(B, H, T, 2 * d, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(da.diffattn_decode_varlen_workspace_bytes(B, H, T, L, d), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()   # inputs are made on torch's current stream; the kernels run on `stream`
 
     def run():
         da.diffattn_decode_varlen(q1, k1, q2, k2, v, Dc["lam"], Dc["layer"], lens=lens, out=out, workspace=ws,
@@ -148,6 +151,54 @@ def bench_decode_multi(da, stream, k1, k2, v, Dc, steps, T=4):
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
 
 
+def bench_decode_paged(da, stream, q1, k1, q2, k2, v, Dc, steps, ref_out, nbytes, P=64):
+    """Single-token decode on the decode workload with its caches split into P-row pages, stored in a seeded
+    shuffled order in page pools and found through a block table."""
+    import torch
+    dev = k1.device
+    B, H, L, d = Dc["B"], Dc["H"], Dc["L"], Dc["d"]
+    max_pages = L // P
+    g = torch.Generator(device="cpu").manual_seed(Dc["seed"] + 1)
+    perm = torch.randperm(B * max_pages, generator=g).to(dev)
+
+    def pool(x):
+        w = x.shape[-1]
+        pages = x.view(B, H, max_pages, P, w).permute(0, 2, 1, 3, 4).reshape(B * max_pages, H, P, w)
+        out = torch.empty_like(pages)
+        out[perm] = pages
+        return out
+
+    k1p, k2p, vp = pool(k1), pool(k2), pool(v)
+    table = perm.to(torch.int32).view(B, max_pages).contiguous()
+    out = torch.empty(B, H, 1, 2 * d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(da.diffattn_decode_paged_workspace_bytes(B, H, 1, max_pages, P, d), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()   # the pools are built on torch's current stream; the kernels run on `stream`
+
+    def run():
+        da.diffattn_decode_paged(q1[:, :, None], k1p, q2[:, :, None], k2p, vp, table, Dc["lam"], Dc["layer"],
+                                 out=out, workspace=ws, stream=stream)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    if not torch.equal(out[:, :, 0].view(torch.int16), ref_out.view(torch.int16)):
+        raise RuntimeError("paged decode differs from the contiguous decode on the same rows")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del k1p, k2p, vp
+    return {"workload": f"decode B{B} H{H} L{L} d64 dv128 in {P}-row pages (shuffled pool, block table)",
+            "steps": steps, "ms": round(ms, 4), "bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+
+
 def bench_backward(da, di, stream, p_bits, q1, k1, q2, k2, v, lam, steps):
     """Training forward + backward on the prefill workload; HIP events on the launch stream."""
     import numpy as np
@@ -161,6 +212,7 @@ def bench_backward(da, di, stream, p_bits, q1, k1, q2, k2, v, lam, steps):
     grads = {k: torch.empty_like(t) for k, t in (("dq1", q1), ("dk1", k1), ("dq2", q2), ("dk2", k2), ("dv", v))}
     grads["dlambda"] = torch.empty(P["H"], dtype=torch.float32, device=dev)
     ws = torch.empty(da.diffattn_bwd_workspace_bytes(P["B"], P["H"], P["N"], P["d"]), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()   # inputs are made on torch's current stream; the kernels run on `stream`
 
     def fwd():
         da.diffattn_fwd_train(q1, k1, q2, k2, v, lam, P["layer"], True, out=out, saved=saved, stream=stream)
@@ -203,6 +255,8 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=10, help="timed backward repetitions (0 skips the backward leg)")
     ap.add_argument("--multi-steps", type=int, default=10,
                     help="timed multi-token decode repetitions (0 skips that leg)")
+    ap.add_argument("--paged-steps", type=int, default=10,
+                    help="timed paged decode repetitions (0 skips that leg)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -327,6 +381,9 @@ def main():
     }
     if args.multi_steps > 0:
         result["decode_multi"] = bench_decode_multi(da, stream, dk1, dk2, dv, Dc, args.multi_steps)
+    if args.paged_steps > 0:
+        result["decode_paged"] = bench_decode_paged(da, stream, dq1, dk1, dq2, dk2, dv, Dc, args.paged_steps, dout,
+                                                    dbytes)
     if args.bwd_steps > 0:
         result["backward"] = bench_backward(da, di, stream, p_bits, pq1, pk1, pq2, pk2, pv, p_lam, args.bwd_steps)
     if not args.no_cpu_baseline:

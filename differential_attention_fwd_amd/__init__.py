@@ -20,6 +20,7 @@ STATUS = {0: "DIFFATTN_OK", -1: "DIFFATTN_ERR_NULL", -2: "DIFFATTN_ERR_SHAPE", -
           -7: "DIFFATTN_ERR_WORKSPACE", -8: "DIFFATTN_ERR_ALIAS", -9: "DIFFATTN_ERR_HIP"}
 EXPORTS = ["diffattn_fwd", "diffattn_fwd_heads", "diffattn_fwd_strided", "diffattn_decode", "diffattn_decode_heads",
            "diffattn_decode_workspace_bytes", "diffattn_decode_varlen_workspace_bytes", "diffattn_decode_varlen",
+           "diffattn_decode_paged_workspace_bytes", "diffattn_decode_paged",
            "diffattn_train_saved_bytes", "diffattn_fwd_train",
            "diffattn_bwd_workspace_bytes", "diffattn_bwd", "diffattn_lambda_init", "diffattn_status_str",
            "diffattn_abi_version"]
@@ -59,6 +60,11 @@ def lib() -> ctypes.CDLL:
     L.diffattn_decode_varlen.argtypes = [P, P, P, P, P, P, i64, i64, i64, i64, P, c_int, c_int, c_float, P, c_int, P,
                                          ctypes.c_size_t, P]
     L.diffattn_decode_varlen.restype = c_int
+    L.diffattn_decode_paged_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, c_int]
+    L.diffattn_decode_paged_workspace_bytes.restype = ctypes.c_size_t
+    L.diffattn_decode_paged.argtypes = [P, P, P, P, P, P, i64, i64, i64, P, i64, i64, i64, P, c_int, c_int, c_float, P,
+                                        c_int, P, ctypes.c_size_t, P]
+    L.diffattn_decode_paged.restype = c_int
     L.diffattn_train_saved_bytes.argtypes = [i64, i64, i64, c_int]
     L.diffattn_train_saved_bytes.restype = ctypes.c_size_t
     L.diffattn_bwd_workspace_bytes.argtypes = [i64, i64, i64, c_int]
@@ -289,6 +295,51 @@ def diffattn_decode_varlen(q1, k1, q2, k2, v, lam, layer: int, lens=None, out=No
                                       _stream_handle(stream, q1.device))
     if st != 0:
         raise DiffAttnError(st, "diffattn_decode_varlen")
+    return out
+
+
+def diffattn_decode_paged_workspace_bytes(B: int, H: int, T: int, max_pages: int, page_size: int, d: int) -> int:
+    return int(lib().diffattn_decode_paged_workspace_bytes(int(B), int(H), int(T), int(max_pages), int(page_size),
+                                                           int(d)))
+
+
+def diffattn_decode_paged(q1, k1_pages, q2, k2_pages, v_pages, block_table, lam, layer: int, lens=None, out=None,
+                          workspace=None, stream=None):
+    """Paged decode (bf16, d = 64): q1, q2 [B][H][T][d]; page pools k1/k2 [num_pages][H][page_size][d] and
+    v [num_pages][H][page_size][2d]; block_table an int32 GPU tensor [B][max_pages] (logical row r of sequence b is
+    row r % page_size of page block_table[b][r // page_size]); lens: None or an int32 GPU tensor of B cache lengths.
+    Returns out [B][H][T][2d]."""
+    import torch
+    _check_tensors((q1, k1_pages, q2, k2_pages, v_pages, block_table))
+    B, H, T, d = q1.shape
+    num_pages, _, page_size, _ = k1_pages.shape
+    max_pages = block_table.shape[1] if block_table.dim() == 2 else -1
+    if out is None:
+        out = torch.empty((B, H, T, 2 * d), dtype=q1.dtype, device=q1.device)
+    for t, shp in ((q2, (B, H, T, d)), (k1_pages, (num_pages, H, page_size, d)),
+                   (k2_pages, (num_pages, H, page_size, d)), (v_pages, (num_pages, H, page_size, 2 * d)),
+                   (out, (B, H, T, 2 * d))):
+        if tuple(t.shape) != tuple(shp) or t.dtype != q1.dtype:
+            raise ValueError(f"shape/dtype mismatch: {tuple(t.shape)} {t.dtype}, expected {tuple(shp)} {q1.dtype}")
+    if block_table.dtype != torch.int32 or tuple(block_table.shape) != (B, max_pages) or block_table.device != q1.device:
+        raise ValueError(f"block_table must be an int32 tensor of shape ({B}, max_pages) on {q1.device}")
+    if lens is not None:
+        if lens.dtype != torch.int32 or tuple(lens.shape) != (B,) or lens.device != q1.device:
+            raise ValueError(f"lens must be an int32 tensor of shape ({B},) on {q1.device}")
+        _check_tensors((lens,))
+    need = diffattn_decode_paged_workspace_bytes(B, H, T, max_pages, page_size, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q1.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lam_f, lam_p = _lambda_args(lam, H, q1.device)
+    st = lib().diffattn_decode_paged(q1.data_ptr(), k1_pages.data_ptr(), q2.data_ptr(), k2_pages.data_ptr(),
+                                     v_pages.data_ptr(), out.data_ptr(), B, H, T, block_table.data_ptr(), max_pages,
+                                     page_size, num_pages, lens.data_ptr() if lens is not None else None, d,
+                                     _dtype_code(q1), lam_f, lam_p, int(layer), ws_ptr, ws_bytes,
+                                     _stream_handle(stream, q1.device))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_decode_paged")
     return out
 
 

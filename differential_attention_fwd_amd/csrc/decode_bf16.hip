@@ -17,6 +17,8 @@
 //     keys up to its own position.  The T queries sit in LDS; the split's scores for all of them are kept in LDS
 //     (T x keys <= 2048 per map); waves take queries t = wave, wave + 4, ... for the softmax and value passes, so
 //     V rows are re-read per query from cache rather than from HBM.
+//   * Paged caches (template flag PAGED): a sequence's rows live in fixed-size pages of a pool shared by all
+//     sequences, found through a per-sequence block table; every row address goes through cache_row.
 #include "launch.h"
 
 namespace diffattn {
@@ -79,6 +81,20 @@ __host__ __device__ inline SplitPlan plan_splits(int64_t BH, int64_t L) {
     return SplitPlan{(int)s, (int)keys};
 }
 
+// Index of cache row r (logical position in its sequence) of head bh, in rows of the cache tensors: contiguous
+// [B][H][L][w], or paged pools [num_pages][H][page][w] through the block table (entries clamped to the pool).
+template <bool PAGED>
+__device__ __forceinline__ size_t cache_row(const DecodePages& pg, int bh, int H, int L, int r) {
+    if constexpr (!PAGED) {
+        return (size_t)bh * L + r;
+    } else {
+        const int b = bh / H, h = bh - b * H;
+        int page = pg.table[(size_t)b * pg.max_pages + (r >> pg.log2_page)];
+        page = min(max(page, 0), pg.num_pages - 1);
+        return (((size_t)page * H + h) << pg.log2_page) + (r & ((1 << pg.log2_page) - 1));
+    }
+}
+
 // Cache length of sequence b: lens[b] clamped to [lo, L], or L without a length array.
 __device__ __forceinline__ int seq_len(const int* lens, int b, int lo, int L) {
     return lens ? min(max(lens[b], lo), L) : L;
@@ -94,13 +110,15 @@ __device__ __forceinline__ void write_empty(float* dst, int tid) {
     for (int k = tid; k < 2 * DV; k += THREADS) dst[4 + k] = 0.f;
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* __restrict__ gq1,
                                                                const uint16_t* __restrict__ gk1,
                                                                const uint16_t* __restrict__ gq2,
                                                                const uint16_t* __restrict__ gk2,
                                                                const uint16_t* __restrict__ gv,
                                                                float* __restrict__ ws, int L, int splits,
-                                                               int split_keys, const int* __restrict__ lens, int H) {
+                                                               int split_keys, const int* __restrict__ lens, int H,
+                                                               DecodePages pg) {
     __shared__ float sc1[MAX_SPLIT_KEYS], sc2[MAX_SPLIT_KEYS];
     __shared__ float red[4][8];
     __shared__ float part[4][2 * DV];
@@ -116,10 +134,6 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     }
     const float c = LOG2E * 0.125f;  // log2(e) / sqrt(64)
 
-    const uint16_t* k1 = gk1 + ((size_t)bh * L + j0) * D;
-    const uint16_t* k2 = gk2 + ((size_t)bh * L + j0) * D;
-    const uint16_t* v = gv + ((size_t)bh * L + j0) * DV;
-
     // Phase 1: scores.  Lane handles 16-byte chunk (lane % 8) of row (lane / 8) of an 8-row group; the workgroup
     // covers 32 rows per step.
     const int ch = lane & 7;
@@ -130,8 +144,9 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     for (int r0 = 0; r0 < n; r0 += 32) {
         const int r = r0 + r_in;
         const int rr = min(r, n - 1);
-        const u32x4 ka = *(const u32x4*)(k1 + (size_t)rr * D + ch * 8);
-        const u32x4 kb = *(const u32x4*)(k2 + (size_t)rr * D + ch * 8);
+        const size_t kr = cache_row<PAGED>(pg, bh, H, L, j0 + rr);
+        const u32x4 ka = *(const u32x4*)(gk1 + kr * D + ch * 8);
+        const u32x4 kb = *(const u32x4*)(gk2 + kr * D + ch * 8);
         float s1 = dot8(qa, ka, 0.f), s2 = dot8(qb, kb, 0.f);
         s1 += __shfl_xor(s1, 1); s2 += __shfl_xor(s2, 1);
         s1 += __shfl_xor(s1, 2); s2 += __shfl_xor(s2, 2);
@@ -176,7 +191,7 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     for (int r0 = 0; r0 < n; r0 += 16) {
         const int r = r0 + vr_in;
         if (r < n) {
-            const u32x4 w = *(const u32x4*)(v + (size_t)r * DV + vc * 8);
+            const u32x4 w = *(const u32x4*)(gv + cache_row<PAGED>(pg, bh, H, L, j0 + r) * DV + vc * 8);
             const float p1 = sc1[r], p2 = sc2[r];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -255,6 +270,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
 }
 
 // Multi-token split: one workgroup per (head, key split), all T queries of the head.
+template <bool PAGED>
 __global__ __launch_bounds__(THREADS) void decode_multi_split_kernel(const uint16_t* __restrict__ gq1,
                                                                      const uint16_t* __restrict__ gk1,
                                                                      const uint16_t* __restrict__ gq2,
@@ -262,7 +278,7 @@ __global__ __launch_bounds__(THREADS) void decode_multi_split_kernel(const uint1
                                                                      const uint16_t* __restrict__ gv,
                                                                      float* __restrict__ ws, int L, int T, int splits,
                                                                      int split_keys, const int* __restrict__ lens,
-                                                                     int H) {
+                                                                     int H, DecodePages pg) {
     __shared__ float sc[2][MULTI_SCORES];                    // [map][t * split_keys + r]
     __shared__ __attribute__((aligned(16))) uint16_t qs[2][MAX_T][D];
     __shared__ float stat[MAX_T][4];                         // m1, l1, m2, l2 per query
@@ -287,17 +303,15 @@ __global__ __launch_bounds__(THREADS) void decode_multi_split_kernel(const uint1
     }
     __syncthreads();
 
-    const uint16_t* k1 = gk1 + ((size_t)bh * L + j0) * D;
-    const uint16_t* k2 = gk2 + ((size_t)bh * L + j0) * D;
-    const uint16_t* v = gv + ((size_t)bh * L + j0) * DV;
     // Phase 1: scores of every query for the split's keys (masked keys -> -inf).
     const int ch = lane & 7;
     const int r_in = wave * 8 + (lane >> 3);
     for (int r0 = 0; r0 < n; r0 += 32) {
         const int r = r0 + r_in;
         const int rr = min(r, n - 1);
-        const u32x4 ka = *(const u32x4*)(k1 + (size_t)rr * D + ch * 8);
-        const u32x4 kb = *(const u32x4*)(k2 + (size_t)rr * D + ch * 8);
+        const size_t kr = cache_row<PAGED>(pg, bh, H, L, j0 + rr);
+        const u32x4 ka = *(const u32x4*)(gk1 + kr * D + ch * 8);
+        const u32x4 kb = *(const u32x4*)(gk2 + kr * D + ch * 8);
         for (int t = 0; t < T; ++t) {
             float s1 = dot8(*(const u32x4*)&qs[0][t][ch * 8], ka, 0.f);
             float s2 = dot8(*(const u32x4*)&qs[1][t][ch * 8], kb, 0.f);
@@ -351,7 +365,7 @@ __global__ __launch_bounds__(THREADS) void decode_multi_split_kernel(const uint1
             const float* p1s = &sc[0][t * split_keys];
             const float* p2s = &sc[1][t * split_keys];
             for (int r = slot; r < n; r += 4) {
-                const u32x4 w = *(const u32x4*)(v + (size_t)r * DV + vc * 8);
+                const u32x4 w = *(const u32x4*)(gv + cache_row<PAGED>(pg, bh, H, L, j0 + r) * DV + vc * 8);
                 const float p1 = p1s[r], p2 = p2s[r];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
@@ -409,17 +423,29 @@ size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L, int T) {
 
 hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
                                   const uint16_t* v, uint16_t* out, int64_t BH, int64_t H, int64_t L, int T,
-                                  const int* lens, Epilogue ep, void* workspace, hipStream_t stream) {
+                                  const int* lens, const DecodePages* pages, Epilogue ep, void* workspace,
+                                  hipStream_t stream) {
     const SplitPlan p = plan_call(BH, L, T);
     const int64_t blocks = BH * (int64_t)p.splits;
     if (blocks > 0x7fffffff || BH * T > 0x7fffffff || T < 1 || T > MAX_T) return hipErrorInvalidValue;
+    if (pages && ((int64_t)pages->max_pages << pages->log2_page) != L) return hipErrorInvalidValue;
     float* ws = (float*)workspace;
-    if (T == 1)
-        hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1, q2, k2, v,
-                           ws, (int)L, p.splits, p.split_keys, lens, (int)H);
-    else
-        hipLaunchKernelGGL(decode_multi_split_kernel, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1, q2,
-                           k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H);
+    const DecodePages pg = pages ? *pages : DecodePages{nullptr, 0, 0, 0};
+    if (T == 1) {
+        if (pages)
+            hipLaunchKernelGGL(decode_split_kernel<true>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1, q2,
+                               k2, v, ws, (int)L, p.splits, p.split_keys, lens, (int)H, pg);
+        else
+            hipLaunchKernelGGL(decode_split_kernel<false>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1,
+                               q2, k2, v, ws, (int)L, p.splits, p.split_keys, lens, (int)H, pg);
+    } else {
+        if (pages)
+            hipLaunchKernelGGL(decode_multi_split_kernel<true>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1,
+                               k1, q2, k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg);
+        else
+            hipLaunchKernelGGL(decode_multi_split_kernel<false>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1,
+                               k1, q2, k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(BH * T)), dim3(64), 0, stream, (const float*)ws, out,

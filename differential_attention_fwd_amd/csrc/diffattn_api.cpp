@@ -278,7 +278,7 @@ int decode_impl(const void* q1, const void* k1, const void* q2, const void* k2, 
     if (lens && overlaps(w, ls)) return DIFFATTN_ERR_ALIAS;
     return hip_status(diffattn::launch_decode_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
                                                        (const uint16_t*)k2, (const uint16_t*)v, (uint16_t*)out, BH, H,
-                                                       L, (int)T, lens, ep, workspace, s));
+                                                       L, (int)T, lens, nullptr, ep, workspace, s));
 }
 
 }  // namespace
@@ -299,6 +299,83 @@ int diffattn_decode_heads(const void* q1, const void* k1, const void* q2, const 
     (void)causal;
     return decode_impl(q1, k1, q2, k2, v, out, B, H, 1, L, nullptr, false, d, dtype, 0.0f, lambda_heads, true, layer,
                        workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+// Page size checks of the paged decode: a power of two in [16, DIFFATTN_MAX_PAGE_SIZE]; returns log2, or -1.
+int page_log2(int64_t page_size) {
+    if (page_size < 16 || page_size > DIFFATTN_MAX_PAGE_SIZE || (page_size & (page_size - 1)) != 0) return -1;
+    int l = 0;
+    while ((int64_t{1} << l) < page_size) ++l;
+    return l;
+}
+
+}  // namespace
+
+size_t diffattn_decode_paged_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t max_pages, int64_t page_size,
+                                             int d) {
+    int64_t L;
+    if (max_pages < 1 || page_log2(page_size) < 0 || !mul_ok(max_pages, page_size, &L)) return 0;
+    return diffattn_decode_varlen_workspace_bytes(B, H, T, L, d);
+}
+
+int diffattn_decode_paged(const void* q1, const void* k1_pages, const void* q2, const void* k2_pages,
+                          const void* v_pages, void* out, int64_t B, int64_t H, int64_t T,
+                          const int32_t* block_table, int64_t max_pages, int64_t page_size, int64_t num_pages,
+                          const int32_t* lens, int d, int dtype, float lambda, const float* lambda_heads, int layer,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    const int lp = page_log2(page_size);
+    int64_t L;
+    if (B < 0 || H < 0 || T < 1 || T > DIFFATTN_MAX_NEW_TOKENS || max_pages < 1 || max_pages > INT32_MAX ||
+        num_pages < 1 || num_pages > INT32_MAX || lp < 0 || !mul_ok(max_pages, page_size, &L) ||
+        L > DIFFATTN_MAX_LEN || L < T)
+        return DIFFATTN_ERR_SHAPE;
+    int st = check_dtype_d(dtype, d);
+    if (st) return st;
+    if (dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
+    Epilogue ep;
+    st = make_epilogue(lambda_heads ? 0.0f : lambda, layer, &ep);
+    if (st) return st;
+    int64_t BH, q_elems, pool_rows, k_elems, v_elems, table_elems;
+    if (!mul_ok(B, H, &BH) || BH > INT32_MAX || !mul_ok(BH * T, d, &q_elems) || !mul_ok(num_pages, H, &pool_rows) ||
+        !mul_ok(pool_rows, page_size, &pool_rows) || !mul_ok(pool_rows, d, &k_elems) ||
+        !mul_ok(pool_rows, 2 * (int64_t)d, &v_elems) || !mul_ok(B, max_pages, &table_elems))
+        return DIFFATTN_ERR_SHAPE;
+    if (BH == 0) return DIFFATTN_OK;
+    if (!q1 || !k1_pages || !q2 || !k2_pages || !v_pages || !out || !block_table) return DIFFATTN_ERR_NULL;
+    if (!aligned16(q1) || !aligned16(k1_pages) || !aligned16(q2) || !aligned16(k2_pages) || !aligned16(v_pages) ||
+        !aligned16(out) || ((uintptr_t)block_table & 3u) != 0 || ((uintptr_t)lens & 3u) != 0)
+        return DIFFATTN_ERR_ALIGN;
+    const Span o{(uintptr_t)out, (uintptr_t)out + (size_t)q_elems * 2 * 2};
+    const Span ins[7] = {{(uintptr_t)q1, (uintptr_t)q1 + (size_t)q_elems * 2},
+                         {(uintptr_t)k1_pages, (uintptr_t)k1_pages + (size_t)k_elems * 2},
+                         {(uintptr_t)q2, (uintptr_t)q2 + (size_t)q_elems * 2},
+                         {(uintptr_t)k2_pages, (uintptr_t)k2_pages + (size_t)k_elems * 2},
+                         {(uintptr_t)v_pages, (uintptr_t)v_pages + (size_t)v_elems * 2},
+                         {(uintptr_t)block_table, (uintptr_t)block_table + (size_t)table_elems * 4},
+                         {(uintptr_t)lens, (uintptr_t)lens + (lens ? (size_t)B * 4 : 0)}};
+    for (const Span& sp : ins)
+        if (overlaps(o, sp)) return DIFFATTN_ERR_ALIAS;
+    if (lambda_heads) {
+        st = check_lambda_heads(lambda_heads, H, o);
+        if (st) return st;
+        ep.lambda_heads = lambda_heads;
+        ep.heads = (int)H;
+    }
+    const size_t need = diffattn::decode_bf16_workspace_bytes(BH, L, (int)T);
+    if (!workspace || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DIFFATTN_ERR_ALIGN;
+    const Span w{(uintptr_t)workspace, (uintptr_t)workspace + need};
+    if (overlaps(w, o)) return DIFFATTN_ERR_ALIAS;
+    for (const Span& sp : ins)
+        if (overlaps(w, sp)) return DIFFATTN_ERR_ALIAS;
+    if (lambda_heads && overlaps(w, Span{(uintptr_t)lambda_heads, (uintptr_t)lambda_heads + (size_t)H * sizeof(float)}))
+        return DIFFATTN_ERR_ALIAS;
+    const diffattn::DecodePages pg{block_table, (int)max_pages, lp, (int)num_pages};
+    return hip_status(diffattn::launch_decode_bf16_d64(
+        (const uint16_t*)q1, (const uint16_t*)k1_pages, (const uint16_t*)q2, (const uint16_t*)k2_pages,
+        (const uint16_t*)v_pages, (uint16_t*)out, BH, H, L, (int)T, lens, &pg, ep, workspace, (hipStream_t)stream));
 }
 
 int diffattn_decode_varlen(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,

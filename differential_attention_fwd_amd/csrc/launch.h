@@ -72,9 +72,19 @@ hipError_t launch_attn_f32(const float* q1, const float* k1, const float* q2, co
 // bf16 decode, d = 64: split kernel writing per-split partial states, then the merge + epilogue kernel.
 // T new tokens per (b, h) (1 <= T <= 16; queries [BH][T][d], out [BH][T][2d]); caches [BH][L][...]; lens: optional
 // device array of B cache lengths (clamped on the device to [T, L]), with b = bh / H.
+// Paged decode caches: the rows of sequence b live in pages of 2^log2_page rows in pools [num_pages][H][page][w];
+// logical row r of sequence b is row r % page of page table[b * max_pages + r / page] (entries clamped to
+// [0, num_pages)).  L = max_pages * page.
+struct DecodePages {
+    const int* table;
+    int max_pages, log2_page, num_pages;
+};
+
 size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L, int T);
+// pages == nullptr: contiguous caches [B][H][L][w].
 hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
                                   const uint16_t* v, uint16_t* out, int64_t BH, int64_t H, int64_t L, int T,
-                                  const int* lens, Epilogue ep, void* workspace, hipStream_t stream);
+                                  const int* lens, const DecodePages* pages, Epilogue ep, void* workspace,
+                                  hipStream_t stream);
 
 }  // namespace diffattn

@@ -62,8 +62,11 @@ enum diffattn_status {
  * address a head through a 32-bit buffer offset. */
 #define DIFFATTN_MAX_LEN (1 << 23)
 
-/* Most new tokens per sequence in one diffattn_decode_varlen call. */
+/* Most new tokens per sequence in one diffattn_decode_varlen or diffattn_decode_paged call. */
 #define DIFFATTN_MAX_NEW_TOKENS 16
+
+/* Largest page of a paged decode cache (rows). */
+#define DIFFATTN_MAX_PAGE_SIZE 65536
 
 /*
  * Prefill (square, Nq = Nk = N): the whole forward pass for B x H heads of N tokens.
@@ -145,6 +148,33 @@ int diffattn_decode_varlen(const void *q1, const void *k1, const void *q2, const
                            int64_t B, int64_t H, int64_t T, int64_t L, const int32_t *lens, int d, int dtype,
                            float lambda, const float *lambda_heads, int layer, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/*
+ * Paged decode (bf16, d = 64): diffattn_decode_varlen over caches kept in fixed-size pages of a pool shared by all
+ * sequences, the layout of a serving cache that grows a page at a time.  The method is the same (the pages fix the
+ * computation, not where the cache rows live); only the addressing of cache rows differs.
+ *   k1_pages, k2_pages: [num_pages][H][page_size][d];  v_pages: [num_pages][H][page_size][2d].
+ *   block_table: DEVICE array [B][max_pages] of int32, 4-byte aligned: logical cache row r of sequence b (every
+ *                head) is row r % page_size of page block_table[b * max_pages + r / page_size].  Entries are read
+ *                on `stream`, only for rows below the sequence's length, and clamped on the device to
+ *                [0, num_pages), so no access leaves the pools; a clamped entry reads that page.
+ *   page_size:   a power of two in [16, DIFFATTN_MAX_PAGE_SIZE].  L = max_pages * page_size plays the role of the
+ *                padded length of diffattn_decode_varlen (L <= DIFFATTN_MAX_LEN, L >= T).
+ *   q1, q2, out, T, lens, lambda, lambda_heads, layer: as for diffattn_decode_varlen (lens NULL = L rows each).
+ *   workspace: >= diffattn_decode_paged_workspace_bytes(B, H, T, max_pages, page_size, d) bytes, 16-byte aligned,
+ *              overlapping nothing else.
+ * Errors as for diffattn_decode_varlen; a page_size that is not a power of two in range, max_pages < 1 or
+ * num_pages < 1 is DIFFATTN_ERR_SHAPE; block_table NULL is DIFFATTN_ERR_NULL; a block table or lens not 4-byte
+ * aligned is DIFFATTN_ERR_ALIGN; out overlapping any input (pools, table, lens) is DIFFATTN_ERR_ALIAS.  The result
+ * equals diffattn_decode_varlen on the cache gathered page by page (same kernels, same split plan for L).
+ */
+size_t diffattn_decode_paged_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t max_pages, int64_t page_size,
+                                             int d);
+int diffattn_decode_paged(const void *q1, const void *k1_pages, const void *q2, const void *k2_pages,
+                          const void *v_pages, void *out, int64_t B, int64_t H, int64_t T,
+                          const int32_t *block_table, int64_t max_pages, int64_t page_size, int64_t num_pages,
+                          const int32_t *lens, int d, int dtype, float lambda, const float *lambda_heads, int layer,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Training: a forward that keeps what the backward pass needs, and the backward pass.  The pages describe no

@@ -259,3 +259,33 @@ def _with(idx, val, B=1, H=2, N=64):
 ])
 def test_fwd_strided_validation(lib, case, expect):
     assert fwd_strided(lib, **case) == expect
+
+
+def dec_paged(lib, T=2, max_pages=4, page=16, num_pages=8, table=G[0], lens=G[1], out=A[5], ws=G[2], ws_bytes=None,
+              B=2, H=2, d=64, dtype=BF16, lam=0.8, layer=1):
+    if ws_bytes is None:
+        ws_bytes = lib.diffattn_decode_paged_workspace_bytes(B, H, T, max_pages, page, d)
+    return lib.diffattn_decode_paged(A[0], A[1], A[2], A[3], A[4], out, B, H, T, table, max_pages, page, num_pages,
+                                     lens, d, dtype, lam, None, layer, ws, ws_bytes, None)
+
+
+def test_paged_workspace_sizes(lib):
+    assert (lib.diffattn_decode_paged_workspace_bytes(4, 8, 3, 20, 64, 64) ==
+            lib.diffattn_decode_varlen_workspace_bytes(4, 8, 3, 20 * 64, 64))
+    for bad in ((2, 2, 1, 4, 24, 64), (2, 2, 1, 4, 8, 64), (2, 2, 1, 0, 16, 64), (2, 2, 1, 4, 1 << 17, 64),
+                (2, 2, 1, 1 << 20, 16, 64), (2, 2, 0, 4, 16, 64), (2, 2, 1, 4, 16, 8)):
+        assert lib.diffattn_decode_paged_workspace_bytes(*bad) == 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(page=24), E_SHAPE), (dict(page=8), E_SHAPE), (dict(page=1 << 17), E_SHAPE), (dict(max_pages=0), E_SHAPE),
+    (dict(num_pages=0), E_SHAPE), (dict(T=0), E_SHAPE), (dict(T=17), E_SHAPE),
+    (dict(max_pages=1 << 20, ws=None), E_SHAPE), (dict(dtype=F32), E_UNSUP), (dict(d=8), E_UNSUP),
+    (dict(table=None), E_NULL), (dict(table=G[0] + 2), E_ALIGN), (dict(lens=G[1] + 2), E_ALIGN),
+    (dict(out=G[0]), E_ALIAS), (dict(out=A[1] + 64), E_ALIAS), (dict(out=G[1]), E_ALIAS),
+    (dict(ws=None), E_WS), (dict(ws_bytes=64), E_WS), (dict(ws=G[2] + 8), E_ALIGN), (dict(ws=G[0]), E_ALIAS),
+    (dict(ws=A[4] + 4096), E_ALIAS), (dict(B=0), OK), (dict(lam=float("nan")), E_LAMBDA), (dict(layer=-1), E_LAYER),
+    (dict(lens=None, out=A[3]), E_ALIAS),
+])
+def test_decode_paged_validation(lib, case, expect):
+    assert dec_paged(lib, **case) == expect

@@ -482,3 +482,86 @@ def test_prefill_strided_interleaved_heads():
     want = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], lam, 0, False)
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Paged decode (diffattn_decode_paged): caches in fixed-size pages of a shared pool, found through a block table.
+# The paging is layout only, so the reference is the varlen decode (and the oracle) on the cache gathered page by
+# page through the same table.
+# ---------------------------------------------------------------------------------------------------------------
+
+def paged_case(B, H, T, P, max_pages, lens, seed, bad_entries=False):
+    """Pools [num_pages][H][P][.] holding each sequence's pages in a random order (unused pages and table tails hold
+    junk), the int32 block table, and the contiguous [B][H][L][.] caches gathered through the clamped table."""
+    rng = np.random.default_rng(seed)
+    L = P * max_pages
+    inp = varlen_inputs(B, H, T, L, seed)
+    need = [max_pages if lens is None else -(-min(max(int(lens[b]), T), L) // P) for b in range(B)]
+    num_pages = sum(need) + 3
+    perm = rng.permutation(num_pages)
+    junk = di.decode_bf16(1, num_pages * H, P, 64, seed=seed + 7)
+    pools = {"k1": junk["k1"].reshape(num_pages, H, P, 64).copy(), "k2": junk["k2"].reshape(num_pages, H, P, 64).copy(),
+             "v": junk["v"].reshape(num_pages, H, P, 128).copy()}
+    table = rng.integers(-1000, 1000, size=(B, max_pages)).astype(np.int32)   # tails: never read
+    i = 0
+    for b in range(B):
+        for j in range(need[b]):
+            pg = int(perm[i])
+            i += 1
+            table[b, j] = pg
+            for k in pools:
+                pools[k][pg] = inp[k][b, :, j * P:(j + 1) * P]
+    if bad_entries:   # in-use entries outside the pool: clamped on the device to [0, num_pages)
+        table[0, 0] = -7
+        table[B - 1, need[B - 1] - 1] = num_pages + 5
+    gathered = {k: np.zeros_like(inp[k]) for k in ("k1", "k2", "v")}
+    for b in range(B):
+        for j in range(need[b]):
+            pg = min(max(int(table[b, j]), 0), num_pages - 1)
+            for k in gathered:
+                gathered[k][b, :, j * P:(j + 1) * P] = pools[k][pg]
+    cont = {"q1": inp["q1"], "q2": inp["q2"], **gathered}
+    return cont, pools, table, L
+
+
+@pytest.mark.parametrize("B,H,T,P,max_pages,lens,layer,bad", [
+    (3, 2, 1, 16, 40, [1, 300, 640], 1, False),
+    (2, 3, 4, 64, 20, None, 0, False),
+    (2, 2, 16, 128, 9, [1100, 17], 2, False),
+    (4, 2, 3, 256, 33, [8448, 5000, 3, 100], 1, False),
+    (2, 2, 2, 32, 10, [320, 200], 1, True),
+])
+def test_decode_paged(B, H, T, P, max_pages, lens, layer, bad):
+    torch = torch_mod()
+    say(f"case: decode paged B{B} H{H} T{T} page {P} x {max_pages} lens={lens} layer={layer} bad={bad}")
+    cont, pools, table, L = paged_case(B, H, T, P, max_pages, lens, seed=700 + T + P, bad_entries=bad)
+    dev = {k: dev_bf16(v) for k, v in cont.items()}
+    pdev = {k: dev_bf16(v) for k, v in pools.items()}
+    tdev = torch.from_numpy(table).to("cuda:0")
+    ldev = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda:0")
+    assert (da.diffattn_decode_paged_workspace_bytes(B, H, T, max_pages, P, 64) ==
+            da.diffattn_decode_varlen_workspace_bytes(B, H, T, L, 64))
+    out = da.diffattn_decode_paged(dev["q1"], pdev["k1"], dev["q2"], pdev["k2"], pdev["v"], tdev, 0.8, layer,
+                                   lens=ldev)
+    ref_dev = da.diffattn_decode_varlen(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.8, layer, lens=ldev)
+    torch.cuda.synchronize()
+    # Same kernels and split plan on the same rows: identical bits.
+    assert torch.equal(out.view(torch.int16), ref_dev.view(torch.int16))
+    ref = varlen_reference(widen(cont), T, L, lens, float(np.float32(0.8)), layer)
+    check_bf16(host_bf16(out), ref, f"decode paged T{T} page {P}")
+
+
+def test_decode_paged_per_head_lambda():
+    torch = torch_mod()
+    B, H, T, P, max_pages, lens = 2, 3, 3, 64, 12, [700, 64]
+    say(f"case: decode paged per-head lambda B{B} H{H} T{T} page {P} x {max_pages}")
+    cont, pools, table, L = paged_case(B, H, T, P, max_pages, lens, seed=760)
+    dev = {k: dev_bf16(v) for k, v in cont.items()}
+    pdev = {k: dev_bf16(v) for k, v in pools.items()}
+    tdev = torch.from_numpy(table).to("cuda:0")
+    ldev = torch.tensor(lens, dtype=torch.int32, device="cuda:0")
+    out = da.diffattn_decode_paged(dev["q1"], pdev["k1"], dev["q2"], pdev["k2"], pdev["v"], tdev, dev_lam(LAM_HEADS),
+                                   1, lens=ldev)
+    torch.cuda.synchronize()
+    ref = varlen_reference(widen(cont), T, L, lens, LAM_HEADS.astype(np.float64), 1)
+    check_bf16(host_bf16(out), ref, "decode paged per-head")
