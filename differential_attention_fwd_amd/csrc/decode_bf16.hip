@@ -13,10 +13,10 @@
 //   * decode_merge: one wave per head merges the splits by log-sum-exp and applies the epilogue.
 //   * Ragged caches: with a per-sequence length array, sequence b uses the first lens[b] cache rows (the cache is
 //     padded to L rows); splits past its end write an empty state (max -inf, sum 0), which the merge weighs by 0.
-//   * decode_multi_split: T > 1 new tokens per sequence (T <= 16), query t at cache position len - T + t seeing
-//     keys up to its own position.  The T queries sit in LDS; the split's scores for all of them are kept in LDS
-//     (T x keys <= 2048 per map); waves take queries t = wave, wave + 4, ... for the softmax and value passes, so
-//     V rows are re-read per query from cache rather than from HBM.
+//   * decode_multi_mfma: T > 1 new tokens per sequence (T <= 16), query t at cache position len - T + t seeing
+//     keys up to its own position.  One wave per (head, key split) puts the T queries in the 16 columns of
+//     16x16x32 MFMA tiles: scores K Q^T and outputs V^T P^T on the matrix cores, an online softmax per query in
+//     between (see the kernel).
 //   * Paged caches (template flag PAGED): a sequence's rows live in fixed-size pages of a pool shared by all
 //     sequences, found through a per-sequence block table; every row address goes through cache_row.
 #include "launch.h"
@@ -34,7 +34,6 @@ constexpr int THREADS = 256;
 constexpr int MAX_SPLIT_KEYS = 1024;          // keys per split (scores of both maps fit in 8 KiB of LDS)
 constexpr int PART_FLOATS = 4 + 2 * DV;       // m1, l1, m2, l2, O1[128], O2[128]
 constexpr int MAX_T = 16;                     // new tokens per sequence in multi-token decode
-constexpr int MULTI_SCORES = 2048;            // T x split keys per map held in LDS by the multi-token kernel
 constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
@@ -269,148 +268,331 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
     *(unsigned*)(gout + (size_t)item * DV + 2 * lane) = w;
 }
 
-// Multi-token split: one workgroup per (head, key split), all T queries of the head.
-template <bool PAGED>
-__global__ __launch_bounds__(THREADS) void decode_multi_split_kernel(const uint16_t* __restrict__ gq1,
-                                                                     const uint16_t* __restrict__ gk1,
-                                                                     const uint16_t* __restrict__ gq2,
-                                                                     const uint16_t* __restrict__ gk2,
-                                                                     const uint16_t* __restrict__ gv,
-                                                                     float* __restrict__ ws, int L, int T, int splits,
-                                                                     int split_keys, const int* __restrict__ lens,
-                                                                     int H, DecodePages pg) {
-    __shared__ float sc[2][MULTI_SCORES];                    // [map][t * split_keys + r]
-    __shared__ __attribute__((aligned(16))) uint16_t qs[2][MAX_T][D];
-    __shared__ float stat[MAX_T][4];                         // m1, l1, m2, l2 per query
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }   // vm only
+constexpr int waitcnt_lgkm0() { return 15 | (7 << 4) | (0 << 8) | (3 << 14); }                       // lgkm only
+template <int V> struct Slot2 { static constexpr int value = V; };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Multi-token split on the matrix cores: one wave per (head, key split), all T <= 16 queries of the head as the 16
+// columns of v_mfma_f32_16x16x32_bf16 tiles (A 16 x 32: lane holds A[m = l % 16][k = 8 (l / 16) + j]; B 32 x 16:
+// lane holds B[k = 8 (l / 16) + j][n = l % 16]; D 16 x 16: lane holds D[m = 4 (l / 16) + i][n = l % 16]).
+//   * Scores S^T = K Q^T per 32-key tile: A = K rows from LDS, B = the queries.  Lane l then holds query t = l % 16
+//     and keys 4 g + i, 16 + 4 g + i of the tile (g = l / 16), which are, in order, its 8 probabilities as the B
+//     operand of O^T = V^T P^T.
+//   * K1, K2 and V tiles go straight to LDS (global_load_lds_dwordx4, 16 bytes per lane) through a 2-slot ring, one
+//     tile ahead; each V^T A operand (one channel, the lane's 8 keys) is two ds_read_b64_tr_b16 reads of the
+//     row-major V tile.  Only this wave reads its slots, so a vmcnt wait orders them (no barrier).  The loads are
+//     issued as inline assembly: the compiler then tracks no vector-memory operation inside the loop and adds no
+//     waits of its own (its tracking of direct-to-LDS loads cannot tell the two slots apart across the loop and
+//     would wait for the prefetch as well).
+//   * Online softmax per query and map, offsets moved only when a tile's max exceeds them by more than 2^8 (so no
+//     probability exceeds 2^8); offsets start at -FLT_MAX so a query with no visible key in the split keeps an empty
+//     state without NaN.  The split's state per query goes to the workspace in the merge kernel's format.
+constexpr int MQ = 16;                 // query columns of the tile
+constexpr int MT = 32;                 // keys per tile
+constexpr int MV_TILE = MT * DV * 2;   // 8 KiB
+constexpr int MK_TILE = MT * D * 2;    // 4 KiB
+constexpr int PT_MAX = 128;            // page-table entries staged per split (split keys / 16 + 2 <= 66 needed)
+constexpr float MULTI_RESCALE = 8.0f;  // log2 units
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+    return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)a) |
+           ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)b) << 16);
+}
+// Combine a per-lane value over the four lanes holding one query column (l, l ^ 16, l ^ 32, l ^ 48).
+__device__ __forceinline__ float col_max(float x) {
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+    auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float col_sum(float x) {
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+// Raw V tile in LDS: row r (key) of 256 bytes, chunk c at c ^ (2 (r & 3)): the 4 rows x 32 bytes of a transposing
+// read hit 8 distinct bank quads.
+__device__ __forceinline__ int mv_off(int row, int chunk) { return row * 256 + ((chunk ^ ((row & 3) << 1)) << 4); }
+// K tile in LDS: row r of 128 bytes, chunk c at c ^ ((r >> 1) & 7): the 16 rows of one chunk read by a 16-lane group
+// hit 16 distinct bank quads.
+__device__ __forceinline__ int mk_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+// One 16-byte-per-lane direct load from global memory to LDS: lane L writes LDS [lds + 16 L, lds + 16 L + 16) with
+// the 16 bytes at src.  The s_nop is the wait state an LDS DMA needs after an SALU write of M0 (the compiler cannot
+// insert it inside the asm); nothing else in this kernel keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ unsigned lds_u32(const void* p) {
+    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+struct MultiMap {
+    float m, l;   // running offset (log2 units of the scaled scores) and this lane's part of the sum
+};
+
+// One map's tile: scores (already scaled to log2 units, masked -inf) -> packed probabilities; moves the offset
+// (and rescales O and l) when the tile's column max exceeds it by more than MULTI_RESCALE.
+__device__ __forceinline__ bf16x8 multi_softmax(const f32x4 (&s)[2], MultiMap& st, f32x4 (&o)[8]) {
+    const float x = col_max(fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                  fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))));
+    if (__any(x > st.m + MULTI_RESCALE)) {
+        const float mn = fmaxf(st.m, x);
+        const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+        st.m = mn;
+        st.l *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[cb][i] *= alpha;
+    }
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[e >> 2][e & 3] - st.m);
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = pack_bf16(p[2 * k], p[2 * k + 1]);
+    const bf16x8 pk = __builtin_bit_cast(bf16x8, w);
+    // The sum is of the bf16-rounded probabilities that multiply V.
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    const unsigned w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+    float t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), one, 0.f, false);
+    float t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), one, 0.f, false);
+    t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), one, t0, false);
+    t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), one, t1, false);
+    st.l += t0 + t1;
+    return pk;
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* __restrict__ gq1,
+                                                               const uint16_t* __restrict__ gk1,
+                                                               const uint16_t* __restrict__ gq2,
+                                                               const uint16_t* __restrict__ gk2,
+                                                               const uint16_t* __restrict__ gv,
+                                                               float* __restrict__ ws, int L, int T, int splits,
+                                                               int split_keys, const int* __restrict__ lens, int H,
+                                                               DecodePages pg) {
+    __shared__ __attribute__((aligned(16))) unsigned char vs0[MV_TILE], vs1[MV_TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char ks0[2 * MK_TILE], ks1[2 * MK_TILE];   // K1 | K2
+    __shared__ int ptab[PT_MAX];   // paged caches: the split's page indices, clamped to the pool
+
+    const int lane = threadIdx.x;
+    const int g = lane >> 4, l16 = lane & 15;
     const int bh = blockIdx.x / splits;
     const int sp = blockIdx.x % splits;
     const int Lb = seq_len(lens, bh / H, T, L);
     const int j0 = sp * split_keys;
     const int n = min(Lb, j0 + split_keys) - j0;
     const int pos0 = Lb - T;                                 // cache position of query 0
-    const float c = LOG2E * 0.125f;
     float* dst0 = ws + (size_t)bh * T * splits * PART_FLOATS;
     if (n <= 0) {
-        for (int t = 0; t < T; ++t) write_empty(dst0 + ((size_t)t * splits + sp) * PART_FLOATS, tid);
+        for (int t = 0; t < T; ++t) {
+            float* dst = dst0 + ((size_t)t * splits + sp) * PART_FLOATS;
+            if (lane == 0) {
+                dst[0] = -INFINITY;
+                dst[1] = 0.f;
+                dst[2] = -INFINITY;
+                dst[3] = 0.f;
+            }
+            for (int k = lane; k < 2 * DV; k += 64) dst[4 + k] = 0.f;
+        }
         return;
     }
-    for (int k = tid; k < T * D / 8; k += THREADS) {        // stage the T queries (16-byte chunks)
-        const int t = k / (D / 8), chunk = k % (D / 8);
-        *(u32x4*)&qs[0][t][chunk * 8] = *(const u32x4*)(gq1 + ((size_t)bh * T + t) * D + chunk * 8);
-        *(u32x4*)&qs[1][t][chunk * 8] = *(const u32x4*)(gq2 + ((size_t)bh * T + t) * D + chunk * 8);
-    }
-    __syncthreads();
+    const float c = LOG2E * 0.125f;
+    const int t_col = l16;                                   // this lane's query column
+    const bool t_ok = t_col < T;
 
-    // Phase 1: scores of every query for the split's keys (masked keys -> -inf).
-    const int ch = lane & 7;
-    const int r_in = wave * 8 + (lane >> 3);
-    for (int r0 = 0; r0 < n; r0 += 32) {
-        const int r = r0 + r_in;
-        const int rr = min(r, n - 1);
-        const size_t kr = cache_row<PAGED>(pg, bh, H, L, j0 + rr);
-        const u32x4 ka = *(const u32x4*)(gk1 + kr * D + ch * 8);
-        const u32x4 kb = *(const u32x4*)(gk2 + kr * D + ch * 8);
-        for (int t = 0; t < T; ++t) {
-            float s1 = dot8(*(const u32x4*)&qs[0][t][ch * 8], ka, 0.f);
-            float s2 = dot8(*(const u32x4*)&qs[1][t][ch * 8], kb, 0.f);
-            s1 += __shfl_xor(s1, 1); s2 += __shfl_xor(s2, 1);
-            s1 += __shfl_xor(s1, 2); s2 += __shfl_xor(s2, 2);
-            s1 += __shfl_xor(s1, 4); s2 += __shfl_xor(s2, 4);
-            if (r < n && ch == 0) {
-                const bool vis = j0 + r <= pos0 + t;
-                sc[0][t * split_keys + r] = vis ? s1 * c : -INFINITY;
-                sc[1][t * split_keys + r] = vis ? s2 * c : -INFINITY;
+    // Queries as B operands (k = feature 32 kh + 8 g + j, n = query); columns t >= T are zero.
+    bf16x8 qa[2], qb[2];
+    {
+        const int tq = min(t_col, T - 1);   // every lane loads (no divergent branch); columns t >= T are zeroed
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            u32x4 a = *(const u32x4*)(gq1 + ((size_t)bh * T + tq) * D + 32 * kh + 8 * g);
+            u32x4 b = *(const u32x4*)(gq2 + ((size_t)bh * T + tq) * D + 32 * kh + 8 * g);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                a[k] = t_ok ? a[k] : 0u;
+                b[k] = t_ok ? b[k] : 0u;
             }
+            qa[kh] = __builtin_bit_cast(bf16x8, a);
+            qb[kh] = __builtin_bit_cast(bf16x8, b);
         }
     }
-    __syncthreads();
-    // Phase 2: per query (wave w takes t = w, w + 4, ...), the split's max and sum per map; probabilities in place.
-    for (int t = wave; t < T; t += 4) {
-        float* s1 = &sc[0][t * split_keys];
-        float* s2 = &sc[1][t * split_keys];
-        float m1 = -INFINITY, m2 = -INFINITY;
-        for (int r = lane; r < n; r += 64) { m1 = fmaxf(m1, s1[r]); m2 = fmaxf(m2, s2[r]); }
-        m1 = wave_max(m1);
-        m2 = wave_max(m2);
-        float z1 = 0.f, z2 = 0.f;
-        if (m1 != -INFINITY) {   // the split holds at least one visible key of query t (both maps alike)
-            for (int r = lane; r < n; r += 64) {
-                const float p1 = __builtin_amdgcn_exp2f(s1[r] - m1), p2 = __builtin_amdgcn_exp2f(s2[r] - m2);
-                s1[r] = p1;
-                s2[r] = p2;
-                z1 += p1;
-                z2 += p2;
-            }
-        }
-        z1 = wave_sum(z1);
-        z2 = wave_sum(z2);
-        if (lane == 0) {
-            stat[t][0] = m1;
-            stat[t][1] = z1;
-            stat[t][2] = m2;
-            stat[t][3] = z2;
+
+    // Cache row index of absolute row r of this sequence.  Paged caches read the page index from the split's staged
+    // table (LDS), so no global load stands between the loop's direct loads.
+    int pg0 = 0;
+    if constexpr (PAGED) {
+        pg0 = j0 >> pg.log2_page;
+        const int b = bh / H;
+        for (int i = lane; i < PT_MAX; i += 64) {
+            const int idx = min(pg0 + i, pg.max_pages - 1);
+            ptab[i] = min(max(pg.table[(size_t)b * pg.max_pages + idx], 0), pg.num_pages - 1);
         }
     }
-    // Phase 3: partial outputs per query; lane takes channels 8 (lane % 16) .. + 7 of row slot lane / 16.
-    const int vc = lane & 15, slot = lane >> 4;
-    for (int t = wave; t < T; t += 4) {
-        float* dst = dst0 + ((size_t)t * splits + sp) * PART_FLOATS;
-        const float m1 = stat[t][0];   // written by this wave above
-        float a1[8], a2[8];
+    const int hh = bh % H;
+    auto row_index = [&](int r) __attribute__((always_inline)) -> size_t {
+        if constexpr (!PAGED) {
+            return (size_t)bh * L + r;
+        } else {
+            const int page = ptab[(r >> pg.log2_page) - pg0];
+            return (((size_t)page * H + hh) << pg.log2_page) + (r & ((1 << pg.log2_page) - 1));
+        }
+    };
+
+    // Tile loads (rows past the split's end repeat its last row and are masked).  K1 and K2: 4 pieces each of 8
+    // rows x 128 bytes; lane L of piece p writes LDS position 16 L, i.e. row 8 p + L / 8, stored chunk L % 8 =
+    // logical chunk ^ ((row >> 1) & 7).  V: 8 pieces of 4 rows x 256 bytes; lane L of piece p writes row
+    // 4 p + L / 16, stored chunk L % 16 = logical chunk ^ (2 (row & 3)).
+    const int n_tiles = (n + MT - 1) / MT;
+    auto load_tile = [&](int tile, unsigned char* kslot, unsigned char* vslot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) { a1[k] = 0.f; a2[k] = 0.f; }
-        if (m1 != -INFINITY) {
-            const float* p1s = &sc[0][t * split_keys];
-            const float* p2s = &sc[1][t * split_keys];
-            for (int r = slot; r < n; r += 4) {
-                const u32x4 w = *(const u32x4*)(gv + cache_row<PAGED>(pg, bh, H, L, j0 + r) * DV + vc * 8);
-                const float p1 = p1s[r], p2 = p2s[r];
+        for (int p = 0; p < 4; ++p) {
+            const int rr = 8 * p + (lane >> 3);
+            const int r = min(tile * MT + rr, n - 1);
+            const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
+            const size_t row = row_index(j0 + r);
+            dma16(gk1 + row * D + 8 * chunk, lds_u32(kslot + 1024 * p));
+            dma16(gk2 + row * D + 8 * chunk, lds_u32(kslot + MK_TILE + 1024 * p));
+        }
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float lo = bf_lo(w[k]), hi = bf_hi(w[k]);
-                    a1[2 * k] = __builtin_fmaf(p1, lo, a1[2 * k]);
-                    a1[2 * k + 1] = __builtin_fmaf(p1, hi, a1[2 * k + 1]);
-                    a2[2 * k] = __builtin_fmaf(p2, lo, a2[2 * k]);
-                    a2[2 * k + 1] = __builtin_fmaf(p2, hi, a2[2 * k + 1]);
-                }
+        for (int p = 0; p < 8; ++p) {
+            const int rr = 4 * p + (lane >> 4);
+            const int r = min(tile * MT + rr, n - 1);
+            const int chunk = (lane & 15) ^ ((rr & 3) << 1);
+            dma16(gv + row_index(j0 + r) * DV + 8 * chunk, lds_u32(vslot + 1024 * p));
+        }
+    };
+    constexpr int LOADS_PER_TILE = 8 + 8;   // K1 + K2 pieces, V pieces
+    // K A-operand of key block kb and feature half kh: row 16 kb + l16, chunk 4 kh + g; the row swizzle does not
+    // depend on kb, so mk_off(16 kb + l16, 4 kh + g) = (k_rd0 ^ (64 kh)) + 2048 kb.
+    const int k_rd0 = mk_off(l16, g);
+
+    // V^T operand offsets: lane 4 jj + qq of 16-lane group g supplies row 4 g + jj (then 16 + 4 g + jj), channels
+    // 16 cb + 4 qq .. + 3, and receives channel 16 cb + l16 of those 4 keys; cb XORs 32 cb into the offset.
+    const int jj = (lane >> 2) & 3, qq = lane & 3;
+    const int v_rd0 = mv_off(4 * g + jj, qq >> 1) + 8 * (qq & 1);
+    auto v_frag = [&](const unsigned char* slot, int cb) __attribute__((always_inline)) {
+        const unsigned char* p = slot + (v_rd0 ^ (32 * cb));
+        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * 256));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
+    f32x4 o1[8], o2[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { o1[cb][i] = 0.f; o2[cb][i] = 0.f; }
+    MultiMap st1 = {-__FLT_MAX__, 0.f}, st2 = st1;
+
+    load_tile(0, ks0, vs0);
+    // Q must have landed before the loop: the compiler waits for it here (and with it for tile 0's loads, issued
+    // after it), so it places no wait for Q inside the loop.
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) asm volatile("" ::"v"(qa[kh]), "v"(qb[kh]));
+    // PREFETCH: issue the next tile's loads first (the caller guarantees it exists), then wait for this tile's.
+    // Both are compile-time, so the loop has no branch around the loads and the compiler's own waits stay exact.
+    auto step = [&](auto S, auto PREFETCH, int tile) __attribute__((always_inline)) {
+        constexpr int s0 = decltype(S)::value;
+        unsigned char* cur = s0 ? vs1 : vs0;
+        unsigned char* nxt = s0 ? vs0 : vs1;
+        const unsigned char* kcur = s0 ? ks1 : ks0;
+        unsigned char* knxt = s0 ? ks0 : ks1;
+        // The scheduling barriers keep this tile's matrix work after the wait (the compiler would otherwise hoist it
+        // and add waits of its own that also cover the prefetch).
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(PREFETCH)::value) {
+            load_tile(tile + 1, knxt, nxt);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS_PER_TILE));   // tile `tile` has landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 s1[2], s2[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { s1[kb][i] = 0.f; s2[kb][i] = 0.f; }
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const int off = (k_rd0 ^ (64 * kh)) + 2048 * kb;
+                s1[kb] = mfma16(*(const bf16x8*)(kcur + off), qa[kh], s1[kb]);
+                s2[kb] = mfma16(*(const bf16x8*)(kcur + MK_TILE + off), qb[kh], s2[kb]);
             }
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            a1[k] += __shfl_xor(a1[k], 16);
-            a1[k] += __shfl_xor(a1[k], 32);
-            a2[k] += __shfl_xor(a2[k], 16);
-            a2[k] += __shfl_xor(a2[k], 32);
-        }
-        if (lane < 16) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                dst[4 + vc * 8 + k] = a1[k];
-                dst[4 + DV + vc * 8 + k] = a2[k];
+            for (int i = 0; i < 4; ++i) {
+                const int r = tile * MT + 16 * kb + 4 * g + i;
+                const bool vis = t_ok && r < n && j0 + r <= pos0 + t_col;
+                s1[kb][i] = vis ? s1[kb][i] * c : -INFINITY;
+                s2[kb][i] = vis ? s2[kb][i] * c : -INFINITY;
             }
+        const bf16x8 p1 = multi_softmax(s1, st1, o1);
+        const bf16x8 p2 = multi_softmax(s2, st2, o2);
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+            const bf16x8 va = v_frag(cur, cb);
+            o1[cb] = mfma16(va, p1, o1[cb]);
+            o2[cb] = mfma16(va, p2, o2[cb]);
         }
-        if (lane == 0) {
-            dst[0] = stat[t][0];
-            dst[1] = stat[t][1];
-            dst[2] = stat[t][2];
-            dst[3] = stat[t][3];
+        // This tile's LDS reads are done before the next step's direct loads overwrite its slots.
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+    };
+    int tile = 0;
+    for (; tile + 2 < n_tiles; tile += 2) {
+        step(Slot2<0>{}, Slot2<1>{}, tile);
+        step(Slot2<1>{}, Slot2<1>{}, tile + 1);
+    }
+    if (tile + 1 < n_tiles) {
+        step(Slot2<0>{}, Slot2<1>{}, tile);
+        step(Slot2<1>{}, Slot2<0>{}, tile + 1);
+    } else {
+        step(Slot2<0>{}, Slot2<0>{}, tile);
+    }
+
+    // The split's state per query column: offsets, sums over the column's four lanes, and O (lane holds channels
+    // 16 cb + 4 g + i of its column).
+    const float l1 = col_sum(st1.l), l2 = col_sum(st2.l);
+    if (t_ok) {
+        float* dst = dst0 + ((size_t)t_col * splits + sp) * PART_FLOATS;
+        if (g == 0) {
+            dst[0] = l1 > 0.f ? st1.m : -INFINITY;
+            dst[1] = l1;
+            dst[2] = l2 > 0.f ? st2.m : -INFINITY;
+            dst[3] = l2;
+        }
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+            *(f32x4*)(dst + 4 + 16 * cb + 4 * g) = o1[cb];
+            *(f32x4*)(dst + 4 + DV + 16 * cb + 4 * g) = o2[cb];
         }
     }
 }
 
-// Split plan of a call: the single-token plan, with splits shortened for T > 1 so that T x split keys fit in LDS.
+// Split plan of a call (the same for every T).
 SplitPlan plan_call(int64_t BH, int64_t L, int T) {
-    SplitPlan p = plan_splits(BH, L);
-    if (T > 1) {
-        int cap = (MULTI_SCORES / T) & ~31;
-        if (p.split_keys > cap) {
-            p.split_keys = cap;
-            p.splits = (int)((L + cap - 1) / cap);
-        }
-    }
-    return p;
+    (void)T;   // the multi-token kernel keeps no per-key state, so every T shares the single-token plan
+    return plan_splits(BH, L);
 }
 
 }  // namespace
@@ -440,11 +622,11 @@ hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const 
                                q2, k2, v, ws, (int)L, p.splits, p.split_keys, lens, (int)H, pg);
     } else {
         if (pages)
-            hipLaunchKernelGGL(decode_multi_split_kernel<true>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1,
-                               k1, q2, k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg);
+            hipLaunchKernelGGL(decode_multi_mfma_kernel<true>, dim3((unsigned)blocks), dim3(64), 0, stream, q1, k1,
+                               q2, k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg);
         else
-            hipLaunchKernelGGL(decode_multi_split_kernel<false>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1,
-                               k1, q2, k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg);
+            hipLaunchKernelGGL(decode_multi_mfma_kernel<false>, dim3((unsigned)blocks), dim3(64), 0, stream, q1, k1,
+                               q2, k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
