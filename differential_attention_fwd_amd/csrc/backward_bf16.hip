@@ -73,50 +73,82 @@ template <int S, class T> __device__ __forceinline__ T* pick4(T* a, T* b, T* c, 
     else return d;
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-    return x;
-}
-
 __device__ __forceinline__ unsigned pack_bf16_bits(float a, float b) { return pack2(a, b); }
 
 // ---------------------------------------------------------------------------------------------------------------
-// 1. Preprocess: one wave per row; lane holds channels 2 lane, 2 lane + 1.
+// 1. Preprocess: 16 lanes per row (4 rows per wave); lane q of a row holds channels 8 q .. 8 q + 7, so every load and
+//    store is 16 bytes wide and each dot product needs a 4-step reduction over the row's 16 lanes.
 // ---------------------------------------------------------------------------------------------------------------
+constexpr int PRE_ROWS = 4 * WAVES;   // rows per workgroup
+
+__device__ __forceinline__ float row16_sum(float x) {
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) x += __shfl_xor(x, m, 16);
+    return x;
+}
+
 __global__ __launch_bounds__(THREADS) void bwd_pre_kernel(const uint16_t* __restrict__ dy, const float* __restrict__ saved,
                                                           uint16_t* __restrict__ dO, float* __restrict__ stats,
                                                           float* __restrict__ dl_rows, int64_t rows, int N, Epilogue ep) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    const int q = threadIdx.x & 15;
+    const int64_t row_u = (int64_t)blockIdx.x * PRE_ROWS + (threadIdx.x >> 4);
+    const bool live = row_u < rows;
+    const int64_t row = live ? row_u : rows - 1;   // tail lanes redo the last row and store nothing
     const int bh = (int)(row / N);
     const float lam = lambda_of(ep, bh);
     const float* srow = saved + row * SAVED_FLOATS;
-    const unsigned dyb = *(const unsigned*)(dy + row * DV + 2 * lane);
-    const float dy0 = __uint_as_float(dyb << 16), dy1 = __uint_as_float(dyb & 0xffff0000u);
-    const f32x2 o1 = *(const f32x2*)(srow + SAVED_O1 + 2 * lane);
-    const f32x2 o2 = *(const f32x2*)(srow + SAVED_O2 + 2 * lane);
-    const float oc0 = o1[0] - lam * o2[0], oc1 = o1[1] - lam * o2[1];
-    float d0 = dy0, d1 = dy1;
+    const u32x4 dyw = *(const u32x4*)(dy + row * DV + 8 * q);
+    const f32x4 o1a = *(const f32x4*)(srow + SAVED_O1 + 8 * q), o1b = *(const f32x4*)(srow + SAVED_O1 + 8 * q + 4);
+    const f32x4 o2a = *(const f32x4*)(srow + SAVED_O2 + 8 * q), o2b = *(const f32x4*)(srow + SAVED_O2 + 8 * q + 4);
+    const f32x4 hdr = *(const f32x4*)srow;   // lse1, lse2, r, unused
+    float y[8], o1[8], o2[8], oc[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const unsigned w = dyw[k];
+        y[2 * k] = __uint_as_float(w << 16);
+        y[2 * k + 1] = __uint_as_float(w & 0xffff0000u);
+        o1[k] = o1a[k];
+        o1[4 + k] = o1b[k];
+        o2[k] = o2a[k];
+        o2[4 + k] = o2b[k];
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) oc[c] = o1[c] - lam * o2[c];
+    float d[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) d[c] = y[c];
     if (ep.normalise) {
-        const float rr = srow[2];
-        const float dyo = wave_sum(dy0 * oc0 + dy1 * oc1);
+        const float rr = hdr[2];
+        float t = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) t += y[c] * oc[c];
+        const float dyo = row16_sum(t);
         const float g = ep.out_scale;
         const float k = g * rr * rr * rr * dyo * (1.f / DV);
-        d0 = g * rr * dy0 - k * oc0;
-        d1 = g * rr * dy1 - k * oc1;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) d[c] = g * rr * y[c] - k * oc[c];
     }
     // dO is used in bf16 by the matrix products; E1 and E2 use the same rounded values.
-    const unsigned db = pack_bf16_bits(d0, d1);
-    *(unsigned*)(dO + row * DV + 2 * lane) = db;
-    const float r0 = __uint_as_float(db << 16), r1 = __uint_as_float(db & 0xffff0000u);
-    const float e1 = wave_sum(r0 * o1[0] + r1 * o1[1]);
-    const float e2 = wave_sum(r0 * o2[0] + r1 * o2[1]);
+    u32x4 db;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) db[k] = pack_bf16_bits(d[2 * k], d[2 * k + 1]);
+    if (live) *(u32x4*)(dO + row * DV + 8 * q) = db;
+    float e1 = 0.f, e2 = 0.f, dl = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const unsigned w = db[k];
+        const float r0 = __uint_as_float(w << 16), r1 = __uint_as_float(w & 0xffff0000u);
+        e1 += r0 * o1[2 * k] + r1 * o1[2 * k + 1];
+        e2 += r0 * o2[2 * k] + r1 * o2[2 * k + 1];
+    }
     // dlambda is a sum over rows with much cancellation: it uses the unrounded dO.
-    const float dl = wave_sum(d0 * o2[0] + d1 * o2[1]);
-    if (lane == 0) {
-        *(f32x4*)(stats + row * STAT_FLOATS) = f32x4{srow[0], srow[1], e1, e2};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) dl += d[c] * o2[c];
+    e1 = row16_sum(e1);
+    e2 = row16_sum(e2);
+    dl = row16_sum(dl);
+    if (live && q == 0) {
+        *(f32x4*)(stats + row * STAT_FLOATS) = f32x4{hdr[0], hdr[1], e1, e2};
         dl_rows[row] = -dl;
     }
 }
@@ -609,7 +641,7 @@ hipError_t launch_bwd_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uin
     uint16_t* dO = (uint16_t*)ws;
     float* stats = (float*)(ws + up((size_t)rows * DV * 2));
     float* dl_rows = (float*)(ws + up((size_t)rows * DV * 2) + up((size_t)rows * STAT_FLOATS * 4));
-    const int64_t pre_blocks = (rows + WAVES - 1) / WAVES;
+    const int64_t pre_blocks = (rows + PRE_ROWS - 1) / PRE_ROWS;
     const int n_blocks = (int)((N + BLOCK - 1) / BLOCK);
     const int64_t grid = (int64_t)n_blocks * BH;
     const int64_t kv_grid = (int64_t)((N + KBLK - 1) / KBLK) * BH;
