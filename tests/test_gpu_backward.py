@@ -110,3 +110,28 @@ def test_backward_deterministic():
     _, g2, _, _ = run_case(1, 2, 257, True, 2, 0.6, seed=530)
     for k in ("dq1", "dk1", "dq2", "dk2", "dv", "dlambda"):
         assert torch.equal(g1[k], g2[k]), k
+
+
+def test_backward_full_size_sampled_heads():
+    """The backward workload bench.py times (B4 H12 N4096, causal, layer 12, lambda = lambda_init(12), outlier query
+    rows, synthetic N(0,1) output gradient) run on the GPU in full, in bench.py's launch configuration; heads 0 and
+    H - 1 (every batch entry) checked against the oracle.  Heads are independent under a scalar lambda, so the oracle
+    runs on those heads' slices, and dlambda of a head sums over its batch entries only."""
+    torch = torch_mod()
+    B, H, N, layer, seed = 4, 12, 4096, 12, 3
+    lam = float(np.float32(da.diffattn_lambda_init(layer)))
+    say(f"case: backward full size B{B} H{H} N{N} causal layer {layer}, heads 0 and {H - 1} vs oracle")
+    inp = di.prefill_bf16(B, H, N, 64, seed=seed, outliers=True)
+    dy_bits = di.output_grad_bf16(B, H, N, 64, seed=seed)
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    dy = dev_bf16(dy_bits)
+    out, saved = da.diffattn_fwd_train(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], lam, layer, True)
+    g = da.diffattn_bwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], dy, saved, lam, layer, True)
+    torch.cuda.synchronize()
+    heads = [0, H - 1]
+    f = {k: di.bf16_bits_to_f32(v[:, heads]) for k, v in inp.items()}
+    ref = oracle.diffattn_bwd(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], di.bf16_bits_to_f32(dy_bits[:, heads]),
+                              lam, layer, True)
+    sub = {k: g[k][:, heads].contiguous() for k in ("dq1", "dk1", "dq2", "dk2", "dv")}
+    sub["dlambda"] = g["dlambda"][heads].contiguous()
+    check_grads(sub, ref, "backward B4 H12 N4096 heads 0, 11")
