@@ -164,7 +164,7 @@ def bench_decode_paged(da, stream, q1, k1, q2, k2, v, Dc, steps, ref_out, nbytes
     def pool(x):
         w = x.shape[-1]
         pages = x.view(B, H, max_pages, P, w).permute(0, 2, 1, 3, 4).reshape(B * max_pages, H, P, w)
-        out = torch.empty_like(pages)
+        out = torch.empty(pages.shape, dtype=pages.dtype, device=pages.device)   # contiguous
         out[perm] = pages
         return out
 

@@ -565,3 +565,78 @@ def test_decode_paged_per_head_lambda():
     torch.cuda.synchronize()
     ref = varlen_reference(widen(cont), T, L, lens, LAM_HEADS.astype(np.float64), 1)
     check_bf16(host_bf16(out), ref, "decode paged per-head")
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Maximum cache length (DIFFATTN_MAX_LEN = 2^23 rows): a closed-form case of the definition
+# ---------------------------------------------------------------------------------------------------------------
+
+MAX_L = 1 << 23
+
+
+def needle_caches(H, T, needles, seed):
+    """Caches of MAX_L rows on the GPU: K1 = K2 = 0 except row j* of head h, which is a bf16 copy of alpha * q (per
+    map) with the score q.k / sqrt(d) = 40 for every query of the head (its queries are equal), and V = 0 except rows
+    j* - 1, j*, j* + 1 (seeded N(0,1)).  Every other key scores 0, so both maps give row j* the weight
+    1 / (1 + (L - 1) e^-40) = 1 - 3.6e-11 and the output is (1 - lambda) V[j*] to within that (then normalised for
+    layer >= 1)."""
+    torch = torch_mod()
+    qd = di.decode_bf16(1, H, 4, 64, seed=seed)
+    q1 = dev_bf16(qd["q1"]).view(1, H, 1, 64).expand(1, H, T, 64).contiguous()
+    q2 = dev_bf16(qd["q2"]).view(1, H, 1, 64).expand(1, H, T, 64).contiguous()
+    rows = dev_bf16(qd["v"][0, :, :3])                  # [H][3][128]: the V rows around each needle
+    k1 = torch.zeros(1, H, MAX_L, 64, dtype=torch.bfloat16, device="cuda:0")
+    k2 = torch.zeros_like(k1)
+    v = torch.zeros(1, H, MAX_L, 128, dtype=torch.bfloat16, device="cuda:0")
+    for h, j in enumerate(needles):
+        for kk, qq in ((k1, q1), (k2, q2)):
+            qf = qq[0, h, 0].float()
+            kk[0, h, j] = (qf * (320.0 / float((qf * qf).sum()))).to(torch.bfloat16)
+        v[0, h, j - 1:j + 2] = rows[h]
+    torch.cuda.synchronize()
+    return q1, k1, q2, k2, v
+
+
+def needle_reference(v, needles, T, lam, layer):
+    out = np.zeros((1, len(needles), T, 128))
+    for h, j in enumerate(needles):
+        o = (1.0 - lam) * host_bf16(v[0, h, j])
+        if layer >= 1:
+            o = o / np.sqrt((o * o).mean() + 1e-5) * (1.0 - oracle.lambda_init(layer))
+        out[0, h, :] = o
+    return out
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_decode_max_length_needle(layer):
+    """Decode and paged decode at the largest supported cache length: one head's V is 2 GiB, the edge of the 32-bit
+    buffer offsets; the paged pools (64-row pages in a shuffled order, V pool 6 GiB) need 64-bit addresses."""
+    torch = torch_mod()
+    H, lam = 3, 0.5
+    needles = [100, (1 << 22) + 7, MAX_L - 2]   # every needle is visible to both queries when T = 2
+    say(f"case: decode max length L=2^23 needles {needles} layer {layer}")
+    q1, k1, q2, k2, v = needle_caches(H, 2, needles, seed=880)
+    out = da.diffattn_decode(q1[:, :, 0].contiguous(), k1, q2[:, :, 0].contiguous(), k2, v, lam, layer)
+    torch.cuda.synchronize()
+    ref1 = needle_reference(v, needles, 1, lam, layer)
+    check_bf16(host_bf16(out)[:, :, None], ref1, f"decode L=2^23 layer {layer}")
+    # The same caches in shuffled 64-row pages.
+    P, max_pages = 64, MAX_L // 64
+    perm = torch.randperm(max_pages, generator=torch.Generator().manual_seed(881)).to("cuda:0")
+
+    def pool(x):
+        pages = x.view(1, H, max_pages, P, x.shape[-1]).permute(0, 2, 1, 3, 4).reshape(max_pages, H, P, x.shape[-1])
+        dst = torch.empty(pages.shape, dtype=pages.dtype, device=pages.device)   # contiguous
+        dst[perm] = pages
+        return dst
+
+    k1p, k2p = pool(k1), pool(k2)
+    del k1, k2
+    vp = pool(v)
+    table = perm.to(torch.int32).view(1, max_pages)
+    torch.cuda.synchronize()
+    for T in (1, 2):
+        outp = da.diffattn_decode_paged(q1[:, :, :T].contiguous(), k1p, q2[:, :, :T].contiguous(), k2p, vp, table,
+                                        lam, layer)
+        torch.cuda.synchronize()
+        check_bf16(host_bf16(outp), needle_reference(v, needles, T, lam, layer), f"paged decode L=2^23 T{T}")
