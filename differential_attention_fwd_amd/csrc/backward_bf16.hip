@@ -44,16 +44,26 @@ constexpr int STAT_FLOATS = 4;    // per row in the workspace: lse1, lse2, E1, E
 // ---------------------------------------------------------------------------------------------------------------
 // LDS tile layouts and helpers shared by the dQ and dK/dV kernels.
 // ---------------------------------------------------------------------------------------------------------------
-// Q tile: row r (query) of 128 bytes; chunk c at c ^ q_sw(r).  Rows r and r + 2 (same LDS bank half) differ in
-// bit 1 of the swizzle, so a transposing read's 4 rows x 32 bytes and a 16-row read of one chunk both hit distinct
-// bank quads.
+// The LDS has 64 banks of 4 bytes.  A 64-bit read (the transposing ones included) is served in two windows of 32
+// consecutive lanes; a 128-bit read in four windows of 16 lanes: within each half wave, the 4-lane groups
+// q = (lane >> 2) & 7 of even bit parity form one window and those of odd parity the other (measured on gfx950
+// with pairs of active lanes).  A read takes one pass per window when the window's lanes touch distinct banks.
+//
+// Q tile (and the dQ kernel's K tiles): row r of 128 bytes; chunk c at c ^ q_sw(r), q_sw linear over GF(2) in
+// x = (r >> 1) & 7.  Found by exhaustive search over such maps: free of conflicts for the 16-row 128-bit reads (dK/dV:
+// 16 rows x 4 chunks; dQ: 32 rows x 2 chunks) and the 32-lane transposing reads (dK/dV: 8 rows x 2 adjacent chunks;
+// dQ: 4 rows x 4 chunks).
 __device__ __forceinline__ int q_sw(int r) {
     const int x = (r >> 1) & 7;
-    return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
+    return ((x & 1) << 2) ^ (((x >> 1) & 1) * 3) ^ (((x >> 2) & 1) << 1);
 }
 __device__ __forceinline__ int q_off(int r, int c) { return r * 128 + ((c ^ q_sw(r)) << 4); }
-// dO tile: row r of 256 bytes; chunk c at c ^ do_sw(r), a bijection of r % 16 onto the 16 chunk positions.
-__device__ __forceinline__ int do_sw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+// dO tile (and the dQ kernel's V tiles): row r of 256 bytes; chunk c at c ^ do_sw(r), linear in the bits of r % 16,
+// found the same way for the 16-row 128-bit reads (dK/dV: 16 rows x 4 chunks; dQ: 32 rows x 2 chunks) and the
+// 32-lane transposing reads of 8 rows x 2 adjacent chunks.
+__device__ __forceinline__ int do_sw(int r) {
+    return ((r & 1) << 3) ^ (((r >> 1) & 1) << 2) ^ (((r >> 2) & 1) * 3) ^ (((r >> 3) & 1) << 1);
+}
 __device__ __forceinline__ int do_off(int r, int c) { return r * 256 + ((c ^ do_sw(r)) << 4); }
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
