@@ -321,9 +321,13 @@ __device__ __forceinline__ float col_sum(float x) {
     auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
-// Raw V tile in LDS: row r (key) of 256 bytes, chunk c at c ^ (2 (r & 3)): the 4 rows x 32 bytes of a transposing
-// read hit 8 distinct bank quads.
-__device__ __forceinline__ int mv_off(int row, int chunk) { return row * 256 + ((chunk ^ ((row & 3) << 1)) << 4); }
+// Raw V tile in LDS: row r (key) of 256 bytes, chunk c at c ^ mv_sw(r).  A transposing (64-bit) read is served in
+// windows of 32 consecutive lanes, here 8 rows x 2 adjacent chunks; mv_sw, linear over GF(2) in the bits of r % 16
+// (found by exhaustive search over such maps), puts those 16 chunks on 16 distinct bank quads.
+__device__ __forceinline__ int mv_sw(int r) {
+    return ((r & 1) << 3) ^ (((r >> 1) & 1) << 2) ^ (((r >> 2) & 1) * 3) ^ (((r >> 3) & 1) << 1);
+}
+__device__ __forceinline__ int mv_off(int row, int chunk) { return row * 256 + ((chunk ^ mv_sw(row)) << 4); }
 // K tile in LDS: row r of 128 bytes, chunk c at c ^ ((r >> 1) & 7): the 16 rows of one chunk read by a 16-lane group
 // hit 16 distinct bank quads.
 __device__ __forceinline__ int mk_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
@@ -460,7 +464,7 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
     // Tile loads (rows past the split's end repeat its last row and are masked).  K1 and K2: 4 pieces each of 8
     // rows x 128 bytes; lane L of piece p writes LDS position 16 L, i.e. row 8 p + L / 8, stored chunk L % 8 =
     // logical chunk ^ ((row >> 1) & 7).  V: 8 pieces of 4 rows x 256 bytes; lane L of piece p writes row
-    // 4 p + L / 16, stored chunk L % 16 = logical chunk ^ (2 (row & 3)).
+    // 4 p + L / 16, stored chunk L % 16 = logical chunk ^ mv_sw(row).
     const int n_tiles = (n + MT - 1) / MT;
     auto load_tile = [&](int tile, unsigned char* kslot, unsigned char* vslot) __attribute__((always_inline)) {
 #pragma unroll
@@ -476,7 +480,7 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
         for (int p = 0; p < 8; ++p) {
             const int rr = 4 * p + (lane >> 4);
             const int r = min(tile * MT + rr, n - 1);
-            const int chunk = (lane & 15) ^ ((rr & 3) << 1);
+            const int chunk = (lane & 15) ^ mv_sw(rr);
             dma16(gv + row_index(j0 + r) * DV + 8 * chunk, lds_u32(vslot + 1024 * p));
         }
     };
