@@ -18,7 +18,8 @@
 //     16x16x32 MFMA tiles: scores K Q^T and outputs V^T P^T on the matrix cores, an online softmax per query in
 //     between (see the kernel).
 //   * Paged caches (template flag PAGED): a sequence's rows live in fixed-size pages of a pool shared by all
-//     sequences, found through a per-sequence block table; every row address goes through cache_row.
+//     sequences, found through a per-sequence block table.  A split first copies its page indices into LDS
+//     (stage_pages); every row address then goes through staged_row.
 #include "launch.h"
 
 namespace diffattn {
@@ -32,6 +33,8 @@ constexpr int D = 64;
 constexpr int DV = 128;
 constexpr int THREADS = 256;
 constexpr int MAX_SPLIT_KEYS = 1024;          // keys per split (scores of both maps fit in 8 KiB of LDS)
+constexpr int PT_MAX = 128;                   // page-table entries staged per split
+static_assert(MAX_SPLIT_KEYS / 16 + 2 <= PT_MAX, "a split spans at most keys / 16 + 2 pages of the smallest size");
 constexpr int PART_FLOATS = 4 + 2 * DV;       // m1, l1, m2, l2, O1[128], O2[128]
 constexpr int MAX_T = 16;                     // new tokens per sequence in multi-token decode
 constexpr float LOG2E = 1.4426950408889634f;
@@ -80,17 +83,33 @@ __host__ __device__ inline SplitPlan plan_splits(int64_t BH, int64_t L) {
     return SplitPlan{(int)s, (int)keys};
 }
 
-// Index of cache row r (logical position in its sequence) of head bh, in rows of the cache tensors: contiguous
-// [B][H][L][w], or paged pools [num_pages][H][page][w] through the block table (entries clamped to the pool).
+// Paged caches: copy the block-table entries of the pages that hold rows [j0, j0 + MAX_SPLIT_KEYS) of sequence b
+// into ptab (clamped to the pool; positions past the table repeat its last entry), so that a row's page is an LDS
+// read rather than a dependent global load.  Returns the first staged page.  The caller makes the writes visible
+// (a barrier, or the same wave's later reads).
 template <bool PAGED>
-__device__ __forceinline__ size_t cache_row(const DecodePages& pg, int bh, int H, int L, int r) {
+__device__ __forceinline__ int stage_pages(const DecodePages& pg, int b, int j0, int* ptab, int tid, int nthreads) {
+    if constexpr (!PAGED) {
+        return 0;
+    } else {
+        const int pg0 = j0 >> pg.log2_page;
+        for (int i = tid; i < PT_MAX; i += nthreads) {
+            const int idx = min(pg0 + i, pg.max_pages - 1);
+            ptab[i] = min(max(pg.table[(size_t)b * pg.max_pages + idx], 0), pg.num_pages - 1);
+        }
+        return pg0;
+    }
+}
+// Index of cache row r (logical position in its sequence) of head bh (head hh of its sequence), in rows of the cache
+// tensors: contiguous [B][H][L][w], or paged pools [num_pages][H][page][w] through the staged page indices.
+template <bool PAGED>
+__device__ __forceinline__ size_t staged_row(const DecodePages& pg, const int* ptab, int pg0, int bh, int hh, int H,
+                                             int L, int r) {
     if constexpr (!PAGED) {
         return (size_t)bh * L + r;
     } else {
-        const int b = bh / H, h = bh - b * H;
-        int page = pg.table[(size_t)b * pg.max_pages + (r >> pg.log2_page)];
-        page = min(max(page, 0), pg.num_pages - 1);
-        return (((size_t)page * H + h) << pg.log2_page) + (r & ((1 << pg.log2_page) - 1));
+        const int page = ptab[(r >> pg.log2_page) - pg0];
+        return (((size_t)page * H + hh) << pg.log2_page) + (r & ((1 << pg.log2_page) - 1));
     }
 }
 
@@ -121,6 +140,7 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     __shared__ float sc1[MAX_SPLIT_KEYS], sc2[MAX_SPLIT_KEYS];
     __shared__ float red[4][8];
     __shared__ float part[4][2 * DV];
+    __shared__ int ptab[PAGED ? PT_MAX : 1];   // paged caches: the split's page indices
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x / splits;
@@ -132,6 +152,9 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
         return;
     }
     const float c = LOG2E * 0.125f;  // log2(e) / sqrt(64)
+    const int hh = bh % H;
+    const int pg0 = stage_pages<PAGED>(pg, bh / H, j0, ptab, tid, THREADS);
+    if constexpr (PAGED) __syncthreads();
 
     // Phase 1: scores.  Lane handles 16-byte chunk (lane % 8) of row (lane / 8) of an 8-row group; the workgroup
     // covers 32 rows per step.
@@ -143,7 +166,7 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     for (int r0 = 0; r0 < n; r0 += 32) {
         const int r = r0 + r_in;
         const int rr = min(r, n - 1);
-        const size_t kr = cache_row<PAGED>(pg, bh, H, L, j0 + rr);
+        const size_t kr = staged_row<PAGED>(pg, ptab, pg0, bh, hh, H, L, j0 + rr);
         const u32x4 ka = *(const u32x4*)(gk1 + kr * D + ch * 8);
         const u32x4 kb = *(const u32x4*)(gk2 + kr * D + ch * 8);
         float s1 = dot8(qa, ka, 0.f), s2 = dot8(qb, kb, 0.f);
@@ -190,7 +213,7 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     for (int r0 = 0; r0 < n; r0 += 16) {
         const int r = r0 + vr_in;
         if (r < n) {
-            const u32x4 w = *(const u32x4*)(gv + cache_row<PAGED>(pg, bh, H, L, j0 + r) * DV + vc * 8);
+            const u32x4 w = *(const u32x4*)(gv + staged_row<PAGED>(pg, ptab, pg0, bh, hh, H, L, j0 + r) * DV + vc * 8);
             const float p1 = sc1[r], p2 = sc2[r];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -292,7 +315,6 @@ constexpr int MQ = 16;                 // query columns of the tile
 constexpr int MT = 32;                 // keys per tile
 constexpr int MV_TILE = MT * DV * 2;   // 8 KiB
 constexpr int MK_TILE = MT * D * 2;    // 4 KiB
-constexpr int PT_MAX = 128;            // page-table entries staged per split (split keys / 16 + 2 <= 66 needed)
 constexpr float MULTI_RESCALE = 8.0f;  // log2 units
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -394,7 +416,7 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
                                                                DecodePages pg) {
     __shared__ __attribute__((aligned(16))) unsigned char vs0[MV_TILE], vs1[MV_TILE];
     __shared__ __attribute__((aligned(16))) unsigned char ks0[2 * MK_TILE], ks1[2 * MK_TILE];   // K1 | K2
-    __shared__ int ptab[PT_MAX];   // paged caches: the split's page indices, clamped to the pool
+    __shared__ int ptab[PAGED ? PT_MAX : 1];   // paged caches: the split's page indices
 
     const int lane = threadIdx.x;
     const int g = lane >> 4, l16 = lane & 15;
@@ -442,23 +464,10 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
 
     // Cache row index of absolute row r of this sequence.  Paged caches read the page index from the split's staged
     // table (LDS), so no global load stands between the loop's direct loads.
-    int pg0 = 0;
-    if constexpr (PAGED) {
-        pg0 = j0 >> pg.log2_page;
-        const int b = bh / H;
-        for (int i = lane; i < PT_MAX; i += 64) {
-            const int idx = min(pg0 + i, pg.max_pages - 1);
-            ptab[i] = min(max(pg.table[(size_t)b * pg.max_pages + idx], 0), pg.num_pages - 1);
-        }
-    }
+    const int pg0 = stage_pages<PAGED>(pg, bh / H, j0, ptab, lane, 64);   // one wave: its own later reads see them
     const int hh = bh % H;
     auto row_index = [&](int r) __attribute__((always_inline)) -> size_t {
-        if constexpr (!PAGED) {
-            return (size_t)bh * L + r;
-        } else {
-            const int page = ptab[(r >> pg.log2_page) - pg0];
-            return (((size_t)page * H + hh) << pg.log2_page) + (r & ((1 << pg.log2_page) - 1));
-        }
+        return staged_row<PAGED>(pg, ptab, pg0, bh, hh, H, L, r);
     };
 
     // Tile loads (rows past the split's end repeat its last row and are masked).  K1 and K2: 4 pieces each of 8
