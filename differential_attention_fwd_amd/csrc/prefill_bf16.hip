@@ -10,15 +10,15 @@
 //     workgroups share a CU, so each SIMD runs two independent waves and the matrix cores of one overlap the
 //     softmax of the other.  Key tiles are 32 keys.
 //   * Loads go straight from global memory to LDS (buffer_load ... lds, no registers) through 4-slot rings, three
-//     tiles ahead: K1, K2 and V tiles, all row-major (one key per row).  Ring slots are separate __shared__ arrays
-//     and the loop is unrolled by four, so the compiler can tell reads of one slot from loads still landing in
-//     another.  One workgroup barrier per tile.
+//     tiles ahead: K1, K2 and V tiles, laid out in LDS so that every operand read is free of bank conflicts.
+//     Ring slots are separate __shared__ arrays and the loop is unrolled by four, so the compiler can tell reads
+//     of one slot from loads still landing in another.  One workgroup barrier per tile.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held in
 //     registers).  In the accumulator layout every lane owns ONE query row (lane % 32) and 16 of the 32 keys, so
 //     row statistics need only the lane pair (l, l ^ 32), exchanged with v_permlane32_swap.
 //   * P^T stays in registers and feeds O^T = V^T P^T directly as the MFMA B operand.  The k-order of that product
-//     is the accumulator's key order.  The A operand (V^T: one channel, 8 keys per lane) comes from the row-major
-//     V tile through two transposing reads (ds_read_b64_tr_b16, 4 keys each) that pick the keys in that order;
+//     is the accumulator's key order.  The A operand (V^T: one channel, 8 keys per lane) comes from the
+//     key-by-key V tile through two transposing reads (ds_read_b64_tr_b16, 4 keys each) that pick the keys in that order;
 //     each fragment is shared by the two maps.  O^T's layout gives each lane one query row again, so the
 //     online-softmax rescale of O is lane-local.
 //   * Two online softmaxes run side by side (running offset and sum per map, two O accumulators).  Probabilities
@@ -190,7 +190,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     const int n_tiles = causal ? (q_last / BN + 1) : (N + BN - 1) / BN;
 
     // Direct loads: each wave moves one 1 KiB piece per tile and tensor role.  K1 and K2 tiles (4 KiB each) are 8
-    // pieces, the raw V tile (8 KiB) another 8; piece x of a tile covers its bytes [1024 x, 1024 x + 1024) and lane L
+    // pieces, the V tile (8 KiB) another 8; piece x of a tile covers its bytes [1024 x, 1024 x + 1024) and lane L
     // writes position 16 L of it.  Loads are issued unconditionally, also for tiles past the end: those buffer loads
     // are out of range and read zeros, and they land in ring slots no wave reads again.  The number of vector-memory
     // operations per iteration is therefore fixed, which makes the waits below exact.
@@ -202,18 +202,21 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     for (int j = 0; j < K_PIECES_PER_WAVE; ++j) {
         const int piece = wave + WAVES * j;        // 0..3: K1, 4..7: K2
         const unsigned rb = piece < 4 ? k1rb : k2rb;
-        // K tile row 8 (piece % 4) + L / 8, stored chunk L % 8 = logical chunk ^ ((row >> 1) & 7) (see k_off).
-        const int row = 8 * (piece & 3) + (lane >> 3);
-        kd_voff[j] = (unsigned)row * rb + ((((lane & 7) ^ ((row >> 1) & 7))) << 4);
+        // Piece kc = piece % 4 of a K tile holds 16-byte chunks 2 kc and 2 kc + 1 of all 32 rows: chunk 2 kc + e of
+        // row r at position 2 r + (e ^ ((r >> 3) & 1)), so lane L brings row L / 2, chunk 2 kc + ((L & 1) ^ ...).
+        const int row = lane >> 1, kc = piece & 3;
+        kd_voff[j] = (unsigned)row * rb + ((2 * kc + ((lane & 1) ^ ((row >> 3) & 1))) << 4);
         kd_step[j] = (unsigned)BN * rb;            // bytes per tile
         kd_lds[j] = (piece >> 2) * K_TILE_BYTES + 1024 * (piece & 3);
     }
 #pragma unroll
     for (int j = 0; j < V_PIECES_PER_WAVE; ++j) {
-        // Raw V: position p holds row p / 256 and stored chunk (p / 16) % 16 = logical chunk ^ (2 (row & 3)).
-        const int p = 1024 * (wave + WAVES * j) + 16 * lane;
-        const int row = p >> 8, pchunk = (p >> 4) & 15;
-        vd_voff[j] = (unsigned)row * vrb + ((pchunk ^ ((row & 3) << 1)) << 4);
+        // V tile as [channel block][key][32 channels] (2 KiB per block of 32 channels): piece x holds channels
+        // 32 (x / 2) .. + 31 of keys 16 (x % 2) .. + 15, 64 bytes per key, so lane L brings key 16 (x % 2) + L / 4,
+        // bytes 16 (L % 4) .. + 15 of that channel block.
+        const int x = wave + WAVES * j;
+        const int row = 16 * (x & 1) + (lane >> 2);
+        vd_voff[j] = (unsigned)row * vrb + 64 * (x >> 1) + 16 * (lane & 3);
     }
     const unsigned vd_step = (unsigned)BN * vrb;
     auto issue_k = [&](auto S, int t) {   // S = t % 4
@@ -235,18 +238,20 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(slot + 1024 * (wave + WAVES * j)), 16,
                                                      (int)(vd_voff[j] + (unsigned)t * vd_step), 0, 0, 0);
     };
-    // Per-lane read offsets.  K A-operand: row l32, chunk 2 kc + h; k_off(l32, 2 kc + h) = k_rd0 ^ (32 kc), the
-    // chunk swizzle being an XOR on bits 4..6 of the offset.
+    // Per-lane read offsets.  The LDS serves a 128-bit read in four windows of 16 lanes (within each half wave, the
+    // 4-lane groups (lane >> 2) & 7 of even and of odd bit parity) and a 64-bit read in two windows of 32
+    // consecutive lanes; both layouts give every window distinct banks, and every fragment a constant offset.
+    // K A-operand: row l32, chunk 2 kc + h, at 1024 kc + 16 (2 l32 + (h ^ ((l32 >> 3) & 1))).
     // V^T A-operand of channel block cb and key half ks: lane (h, l32) needs channel 32 cb + l32 of the keys at
     // accumulator positions 16 ks + 8 h .. + 7, i.e. keys 16 ks + 4 h + 0..3, then 16 ks + 8 + 4 h + 0..3.  Each
     // comes from one ds_read_b64_tr_b16: the lane's 16-lane group reads a block of 4 keys x 16 channels, lane
     // 4 jj + q of the group supplying key jj, channels 4 q .. 4 q + 3 of the block, and lane i of the group
-    // receiving channel i of the 4 keys.  The 4-key blocks sit at multiples of 4 rows, so the raw-tile swizzle
-    // depends only on jj; moving to channel block cb XORs 64 cb into the offset, moving by 8 keys adds 2 KiB.
-    const int k_rd0 = k_off(l32, h);
+    // receiving channel i of the 4 keys.  A 32-lane window reads 4 whole 64-byte key rows of a channel block
+    // (256 contiguous bytes); channel block cb adds 2 KiB, 16 keys 1 KiB, 8 keys 512 bytes.
+    const int k_rd0 = 16 * (2 * l32 + (h ^ ((l32 >> 3) & 1)));
     const int trl = lane & 15;
     const int tr_ch = 16 * ((lane >> 4) & 1) + 4 * (trl & 3);   // first channel this lane supplies (block cb = 0)
-    const int v_rd0 = vr_off(4 * h + (trl >> 2), tr_ch >> 3) + (tr_ch & 7) * 2;
+    const int v_rd0 = 64 * (4 * h + (trl >> 2)) + 2 * tr_ch;
 
     f32x16 o1[4], o2[4];
 #pragma unroll
@@ -271,7 +276,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     // Two transposing reads make one V^T fragment (the 8 keys of one accumulator position block).
     auto v_frag = [&](const unsigned char* p) __attribute__((always_inline)) {
         const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * 256));
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * 64));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     auto step = [&](auto S, int t) {   // S = t % 4
@@ -290,7 +295,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
             for (int i = 0; i < 16; ++i) { s1[i] = 0.f; s2[i] = 0.f; }
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
-                const int kro = k_rd0 ^ (32 * kc);
+                const int kro = k_rd0 + 1024 * kc;
                 const bf16x8 ka = *(const bf16x8*)(kb_ + kro);
                 const bf16x8 kb = *(const bf16x8*)(kb_ + K_TILE_BYTES + kro);
                 s1 = mfma(ka, qa[kc], s1);
@@ -312,12 +317,12 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
             __builtin_amdgcn_s_setprio(1);
             bf16x8 va[4][2];
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) va[cb][0] = v_frag(vb_ + (v_rd0 ^ (64 * cb)));
+            for (int cb = 0; cb < 4; ++cb) va[cb][0] = v_frag(vb_ + v_rd0 + 2048 * cb);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o1[cb] = mfma(va[cb][0], p1[0], o1[cb]);
             const float part2 = softmax_tile(s2, st2, o2, c, p2[0], p2[1]);
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) va[cb][1] = v_frag(vb_ + (v_rd0 ^ (64 * cb)) + 16 * 256);
+            for (int cb = 0; cb < 4; ++cb) va[cb][1] = v_frag(vb_ + v_rd0 + 2048 * cb + 1024);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o2[cb] = mfma(va[cb][0], p2[0], o2[cb]);
 #pragma unroll

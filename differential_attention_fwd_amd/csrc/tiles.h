@@ -3,10 +3,9 @@
 // MFMA v_mfma_f32_32x32x16_bf16 operand layouts (lane l, h = l / 32, r = l % 32):
 //   A (32 x 16): lane holds A[m = r][k = 8 h + j], j = 0..7      B (16 x 32): lane holds B[k = 8 h + j][n = r]
 //   D (32 x 32): lane holds D[m = 8 (i / 4) + 4 h + i % 4][n = r], i = 0..15
-// A row-major tile feeds A operands with one 16-byte read per lane; a k-dimension that runs along the tile's rows
-// (keys or queries) needs the tile transposed ("T" tiles below).  When such a product consumes an accumulator of
-// another product as its B operand, the k order is the accumulator's row order: position 8 h + j of a 16-slot
-// k step holds row 8 (j / 4) + 4 h + j % 4, i.e. bits 2 and 3 of the row index swapped (key_pos).
+// When a product consumes an accumulator of another product as its B operand, the k order is the accumulator's row
+// order: position 8 h + j of a 16-slot k step holds row 8 (j / 4) + 4 h + j % 4.  The kernels read the matching A
+// operands with transposing LDS reads (ds_read_b64_tr_b16) that pick rows in that order.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -25,26 +24,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float LOG2E = 1.4426950408889634f;
-
-// K tile: row r (key) of 128 bytes = 8 chunks of 16 bytes; chunk c lives at position c ^ ((r >> 1) & 7).  A wave's
-// 16-lane read group (16 rows, one chunk) and the contiguous direct loads both touch 16 distinct bank quads.
-__device__ __forceinline__ int k_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
-
-// Transposed tile (V^T, and any [32 rows][W] tile transposed): W channel rows of 64 bytes (32 keys or queries).  Keys are stored in the accumulator's key order:
-// key 16s + 8a + 4h + j sits at position 16s + 8h + 4a + j (bits 2 and 3 swapped).  Channel c occupies physical
-// row (c & ~3) | ((c & 3) ^ ((c >> 4) & 1)) and its 16-byte chunk q sits at q ^ ((c >> 2) & 3): the 16
-// consecutive channels of a 128-bit read group hit 16 distinct bank quads, and a transposing write group
-// (4 key groups x 8 channel groups) at most 2-way shares one.  The swizzle uses only channel bits 0..4, so the
-// four 32-channel blocks of a read differ by a constant offset.
-__device__ __forceinline__ int vt_off(int c, int chunk) {
-    const int prow = (c & ~3) | ((c & 3) ^ ((c >> 4) & 1));
-    return prow * 64 + ((chunk ^ ((c >> 2) & 3)) << 4);
-}
-__device__ __forceinline__ int key_pos(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
-
-// Raw V tile as loaded: row r (key) of 256 bytes = 16 chunks of 16 bytes; chunk c lives at c ^ (2 (r & 3)), so the
-// 4 rows x 32 bytes read by each 16-lane group of a transposing read hit 8 distinct bank quads.
-__device__ __forceinline__ int vr_off(int row, int chunk) { return row * 256 + ((chunk ^ ((row & 3) << 1)) << 4); }
 
 // Combine a per-lane value with the value of lane (l ^ 32).
 __device__ __forceinline__ float pair_max(float x) {
