@@ -17,6 +17,8 @@ events recorded on the stream it is launched on.  Prints ONE JSON line.
             synthetic output gradient, timed separately: 1792 FLOP per unmasked pair on the matrix cores (the
             dQ kernel recomputes both score maps and dP: 768; the dK/dV kernel recomputes them and forms dV, dK1,
             dK2: 1024)
+Every roofline's "traffic" is the HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+(profiles/hbm_traffic.txt), used only while the kernel source still matches the hash recorded there, else null.
 """
 from __future__ import annotations
 
@@ -148,7 +150,7 @@ def bench_decode_multi(da, stream, k1, k2, v, Dc, steps, T=4):
                         f"(seeded uniform in [{L // 2}, {L}]), d64 dv128", "steps": steps, "ms": round(ms, 4),
             "bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": read_traffic("decode_multi")}}
 
 
 def bench_decode_paged(da, stream, q1, k1, q2, k2, v, Dc, steps, ref_out, nbytes, P=64):
@@ -196,7 +198,7 @@ def bench_decode_paged(da, stream, q1, k1, q2, k2, v, Dc, steps, ref_out, nbytes
     return {"workload": f"decode B{B} H{H} L{L} d64 dv128 in {P}-row pages (shuffled pool, block table)",
             "steps": steps, "ms": round(ms, 4), "bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": read_traffic("decode_paged")}}
 
 
 def bench_backward(da, di, stream, p_bits, q1, k1, q2, k2, v, lam, steps):
@@ -241,7 +243,7 @@ def bench_backward(da, di, stream, p_bits, q1, k1, q2, k2, v, lam, steps):
             "steps": steps, "fwd_train_ms": round(f_ms, 4), "ms": round(b_ms, 4), "flops_exec": flops,
             "tflops_exec": round(tf, 2),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
-                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic("backward")}}
 
 
 def main():
