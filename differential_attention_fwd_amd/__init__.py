@@ -20,7 +20,7 @@ STATUS = {0: "DIFFATTN_OK", -1: "DIFFATTN_ERR_NULL", -2: "DIFFATTN_ERR_SHAPE", -
           -7: "DIFFATTN_ERR_WORKSPACE", -8: "DIFFATTN_ERR_ALIAS", -9: "DIFFATTN_ERR_HIP"}
 EXPORTS = ["diffattn_fwd", "diffattn_fwd_heads", "diffattn_fwd_strided", "diffattn_decode", "diffattn_decode_heads",
            "diffattn_decode_workspace_bytes", "diffattn_decode_varlen_workspace_bytes", "diffattn_decode_varlen",
-           "diffattn_decode_paged_workspace_bytes", "diffattn_decode_paged",
+           "diffattn_decode_paged_workspace_bytes", "diffattn_decode_paged", "diffattn_decode_strided",
            "diffattn_train_saved_bytes", "diffattn_fwd_train",
            "diffattn_bwd_workspace_bytes", "diffattn_bwd", "diffattn_lambda_init", "diffattn_status_str",
            "diffattn_abi_version"]
@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
     L.diffattn_decode_varlen.argtypes = [P, P, P, P, P, P, i64, i64, i64, i64, P, c_int, c_int, c_float, P, c_int, P,
                                          ctypes.c_size_t, P]
     L.diffattn_decode_varlen.restype = c_int
+    L.diffattn_decode_strided.argtypes = [P, P, P, P, P, P, i64, i64, i64, i64, P, P, c_int, c_int, c_float, P, c_int,
+                                          P, ctypes.c_size_t, P]
+    L.diffattn_decode_strided.restype = c_int
     L.diffattn_decode_paged_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, c_int]
     L.diffattn_decode_paged_workspace_bytes.restype = ctypes.c_size_t
     L.diffattn_decode_paged.argtypes = [P, P, P, P, P, P, i64, i64, i64, P, i64, i64, i64, P, c_int, c_int, c_float, P,
@@ -340,6 +343,44 @@ def diffattn_decode_paged(q1, k1_pages, q2, k2_pages, v_pages, block_table, lam,
                                      _stream_handle(stream, q1.device))
     if st != 0:
         raise DiffAttnError(st, "diffattn_decode_paged")
+    return out
+
+
+def diffattn_decode_strided(q1, k1, q2, k2, v, lam, layer: int, lens=None, out=None, workspace=None, stream=None):
+    """Decode (bf16, d = 64) with strided caches: k1, k2 [B][H][L][d] and v [B][H][L][2d] may be any GPU views whose
+    last dimension is contiguous (e.g. permuted token-major caches, or slices of one packed buffer); q1, q2
+    [B][H][T][d] and out are contiguous.  lens as for diffattn_decode_varlen.  Returns out [B][H][T][2d]."""
+    import torch
+    _check_tensors((q1, q2))
+    B, H, T, d = q1.shape
+    L = k1.shape[2]
+    if out is None:
+        out = torch.empty((B, H, T, 2 * d), dtype=q1.dtype, device=q1.device)
+    _check_tensors((out,))
+    if tuple(q2.shape) != (B, H, T, d) or q2.dtype != q1.dtype or tuple(out.shape) != (B, H, T, 2 * d):
+        raise ValueError("q1, q2 must be [B][H][T][d] and out [B][H][T][2d], contiguous, of one dtype")
+    caches = (k1, k2, v)
+    for t, w in zip(caches, (d, d, 2 * d)):
+        if not t.is_cuda or t.dtype != q1.dtype or tuple(t.shape) != (B, H, L, w) or t.stride(-1) != 1:
+            raise ValueError("strided caches must be [B][H][L][w] GPU views of the queries' dtype with a contiguous "
+                             "last dimension")
+    if lens is not None:
+        if lens.dtype != torch.int32 or tuple(lens.shape) != (B,) or lens.device != q1.device:
+            raise ValueError(f"lens must be an int32 tensor of shape ({B},) on {q1.device}")
+        _check_tensors((lens,))
+    strides = (ctypes.c_int64 * 9)(*[int(x) for t in caches for x in t.stride()[:3]])
+    need = diffattn_decode_varlen_workspace_bytes(B, H, T, L, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q1.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lam_f, lam_p = _lambda_args(lam, H, q1.device)
+    st = lib().diffattn_decode_strided(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
+                                       out.data_ptr(), B, H, T, L, lens.data_ptr() if lens is not None else None,
+                                       strides, d, _dtype_code(q1), lam_f, lam_p, int(layer), ws_ptr, ws_bytes,
+                                       _stream_handle(stream, q1.device))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_decode_strided")
     return out
 
 

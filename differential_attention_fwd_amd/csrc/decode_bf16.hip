@@ -19,7 +19,9 @@
 //     between (see the kernel).
 //   * Paged caches (template flag PAGED): a sequence's rows live in fixed-size pages of a pool shared by all
 //     sequences, found through a per-sequence block table.  A split first copies its page indices into LDS
-//     (stage_pages); every row address then goes through staged_row.
+//     (stage_pages); every row address then goes through cache_elem.
+//   * Padded caches are addressed through per-tensor batch, head and row strides (dense ones included), so K1, K2
+//     and V may be views of token-major or packed buffers.
 #include "launch.h"
 
 namespace diffattn {
@@ -100,16 +102,17 @@ __device__ __forceinline__ int stage_pages(const DecodePages& pg, int b, int j0,
         return pg0;
     }
 }
-// Index of cache row r (logical position in its sequence) of head bh (head hh of its sequence), in rows of the cache
-// tensors: contiguous [B][H][L][w], or paged pools [num_pages][H][page][w] through the staged page indices.
+// Element offset of cache row r (logical position in its sequence) of head hh of sequence b in cache tensor t (width
+// elements per row): padded caches through their strides, paged pools [num_pages][H][page][width] through the
+// staged page indices.
 template <bool PAGED>
-__device__ __forceinline__ size_t staged_row(const DecodePages& pg, const int* ptab, int pg0, int bh, int hh, int H,
-                                             int L, int r) {
+__device__ __forceinline__ int64_t cache_elem(const DecodePages& pg, const CacheStrides& cs, const int* ptab, int pg0,
+                                              int b, int hh, int H, int r, int t, int width) {
     if constexpr (!PAGED) {
-        return (size_t)bh * L + r;
+        return b * cs.b[t] + hh * cs.h[t] + (int64_t)r * cs.n[t];
     } else {
         const int page = ptab[(r >> pg.log2_page) - pg0];
-        return (((size_t)page * H + hh) << pg.log2_page) + (r & ((1 << pg.log2_page) - 1));
+        return (int64_t)((((size_t)page * H + hh) << pg.log2_page) + (r & ((1 << pg.log2_page) - 1))) * width;
     }
 }
 
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
                                                                const uint16_t* __restrict__ gv,
                                                                float* __restrict__ ws, int L, int splits,
                                                                int split_keys, const int* __restrict__ lens, int H,
-                                                               DecodePages pg) {
+                                                               DecodePages pg, CacheStrides cs) {
     __shared__ float sc1[MAX_SPLIT_KEYS], sc2[MAX_SPLIT_KEYS];
     __shared__ float red[4][8];
     __shared__ float part[4][2 * DV];
@@ -152,8 +155,8 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
         return;
     }
     const float c = LOG2E * 0.125f;  // log2(e) / sqrt(64)
-    const int hh = bh % H;
-    const int pg0 = stage_pages<PAGED>(pg, bh / H, j0, ptab, tid, THREADS);
+    const int hh = bh % H, bb = bh / H;
+    const int pg0 = stage_pages<PAGED>(pg, bb, j0, ptab, tid, THREADS);
     if constexpr (PAGED) __syncthreads();
 
     // Phase 1: scores.  Lane handles 16-byte chunk (lane % 8) of row (lane / 8) of an 8-row group; the workgroup
@@ -166,9 +169,8 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     for (int r0 = 0; r0 < n; r0 += 32) {
         const int r = r0 + r_in;
         const int rr = min(r, n - 1);
-        const size_t kr = staged_row<PAGED>(pg, ptab, pg0, bh, hh, H, L, j0 + rr);
-        const u32x4 ka = *(const u32x4*)(gk1 + kr * D + ch * 8);
-        const u32x4 kb = *(const u32x4*)(gk2 + kr * D + ch * 8);
+        const u32x4 ka = *(const u32x4*)(gk1 + cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, j0 + rr, C_K1, D) + ch * 8);
+        const u32x4 kb = *(const u32x4*)(gk2 + cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, j0 + rr, C_K2, D) + ch * 8);
         float s1 = dot8(qa, ka, 0.f), s2 = dot8(qb, kb, 0.f);
         s1 += __shfl_xor(s1, 1); s2 += __shfl_xor(s2, 1);
         s1 += __shfl_xor(s1, 2); s2 += __shfl_xor(s2, 2);
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     for (int r0 = 0; r0 < n; r0 += 16) {
         const int r = r0 + vr_in;
         if (r < n) {
-            const u32x4 w = *(const u32x4*)(gv + staged_row<PAGED>(pg, ptab, pg0, bh, hh, H, L, j0 + r) * DV + vc * 8);
+            const u32x4 w = *(const u32x4*)(gv + cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, j0 + r, C_V, DV) + vc * 8);
             const float p1 = sc1[r], p2 = sc2[r];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
                                                                const uint16_t* __restrict__ gv,
                                                                float* __restrict__ ws, int L, int T, int splits,
                                                                int split_keys, const int* __restrict__ lens, int H,
-                                                               DecodePages pg) {
+                                                               DecodePages pg, CacheStrides cs) {
     __shared__ __attribute__((aligned(16))) unsigned char vs0[MV_TILE], vs1[MV_TILE];
     __shared__ __attribute__((aligned(16))) unsigned char ks0[2 * MK_TILE], ks1[2 * MK_TILE];   // K1 | K2
     __shared__ int ptab[PAGED ? PT_MAX : 1];   // paged caches: the split's page indices
@@ -464,10 +466,10 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
 
     // Cache row index of absolute row r of this sequence.  Paged caches read the page index from the split's staged
     // table (LDS), so no global load stands between the loop's direct loads.
-    const int pg0 = stage_pages<PAGED>(pg, bh / H, j0, ptab, lane, 64);   // one wave: its own later reads see them
-    const int hh = bh % H;
-    auto row_index = [&](int r) __attribute__((always_inline)) -> size_t {
-        return staged_row<PAGED>(pg, ptab, pg0, bh, hh, H, L, r);
+    const int hh = bh % H, bb = bh / H;
+    const int pg0 = stage_pages<PAGED>(pg, bb, j0, ptab, lane, 64);   // one wave: its own later reads see them
+    auto elem = [&](int r, int t, int width) __attribute__((always_inline)) -> int64_t {
+        return cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, r, t, width);
     };
 
     // Tile loads (rows past the split's end repeat its last row and are masked).  K1 and K2: 4 pieces each of 8
@@ -481,16 +483,15 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
             const int rr = 8 * p + (lane >> 3);
             const int r = min(tile * MT + rr, n - 1);
             const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
-            const size_t row = row_index(j0 + r);
-            dma16(gk1 + row * D + 8 * chunk, lds_u32(kslot + 1024 * p));
-            dma16(gk2 + row * D + 8 * chunk, lds_u32(kslot + MK_TILE + 1024 * p));
+            dma16(gk1 + elem(j0 + r, C_K1, D) + 8 * chunk, lds_u32(kslot + 1024 * p));
+            dma16(gk2 + elem(j0 + r, C_K2, D) + 8 * chunk, lds_u32(kslot + MK_TILE + 1024 * p));
         }
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
             const int rr = 4 * p + (lane >> 4);
             const int r = min(tile * MT + rr, n - 1);
             const int chunk = (lane & 15) ^ mv_sw(rr);
-            dma16(gv + row_index(j0 + r) * DV + 8 * chunk, lds_u32(vslot + 1024 * p));
+            dma16(gv + elem(j0 + r, C_V, DV) + 8 * chunk, lds_u32(vslot + 1024 * p));
         }
     };
     constexpr int LOADS_PER_TILE = 8 + 8;   // K1 + K2 pieces, V pieces
@@ -618,8 +619,8 @@ size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L, int T) {
 
 hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
                                   const uint16_t* v, uint16_t* out, int64_t BH, int64_t H, int64_t L, int T,
-                                  const int* lens, const DecodePages* pages, Epilogue ep, void* workspace,
-                                  hipStream_t stream) {
+                                  const int* lens, const DecodePages* pages, const CacheStrides& cs, Epilogue ep,
+                                  void* workspace, hipStream_t stream) {
     const SplitPlan p = plan_call(BH, L, T);
     const int64_t blocks = BH * (int64_t)p.splits;
     if (blocks > 0x7fffffff || BH * T > 0x7fffffff || T < 1 || T > MAX_T) return hipErrorInvalidValue;
@@ -629,17 +630,17 @@ hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const 
     if (T == 1) {
         if (pages)
             hipLaunchKernelGGL(decode_split_kernel<true>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1, q2,
-                               k2, v, ws, (int)L, p.splits, p.split_keys, lens, (int)H, pg);
+                               k2, v, ws, (int)L, p.splits, p.split_keys, lens, (int)H, pg, cs);
         else
             hipLaunchKernelGGL(decode_split_kernel<false>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1,
-                               q2, k2, v, ws, (int)L, p.splits, p.split_keys, lens, (int)H, pg);
+                               q2, k2, v, ws, (int)L, p.splits, p.split_keys, lens, (int)H, pg, cs);
     } else {
         if (pages)
             hipLaunchKernelGGL(decode_multi_mfma_kernel<true>, dim3((unsigned)blocks), dim3(64), 0, stream, q1, k1,
-                               q2, k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg);
+                               q2, k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg, cs);
         else
             hipLaunchKernelGGL(decode_multi_mfma_kernel<false>, dim3((unsigned)blocks), dim3(64), 0, stream, q1, k1,
-                               q2, k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg);
+                               q2, k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg, cs);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -219,10 +219,12 @@ size_t diffattn_decode_varlen_workspace_bytes(int64_t B, int64_t H, int64_t T, i
 
 namespace {
 
+// strided: the caches are addressed through cache_strides, 9 host values (k1, k2, v: batch, head, row; elements);
+// otherwise they are dense [B][H][L][w].
 int decode_impl(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out, int64_t B,
                 int64_t H, int64_t T, int64_t L, const int32_t* lens, bool varlen, int d, int dtype, float lambda,
                 const float* lambda_heads, bool per_head, int layer, void* workspace, size_t workspace_bytes,
-                void* stream) {
+                void* stream, bool strided = false, const int64_t* cache_strides = nullptr) {
     if (B < 0 || H < 0 || L < 0 || T < 1) return DIFFATTN_ERR_SHAPE;
     if (L == 0 || L > DIFFATTN_MAX_LEN || T > DIFFATTN_MAX_NEW_TOKENS || L < T) return DIFFATTN_ERR_SHAPE;
     int st = check_dtype_d(dtype, d);
@@ -237,15 +239,34 @@ int decode_impl(const void* q1, const void* k1, const void* q2, const void* k2, 
         return DIFFATTN_ERR_SHAPE;
     if (BH == 0) return DIFFATTN_OK;
     if (!q1 || !k1 || !q2 || !k2 || !v || !out) return DIFFATTN_ERR_NULL;
+    if (strided && !cache_strides) return DIFFATTN_ERR_NULL;
     if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2) || !aligned16(v) || !aligned16(out))
         return DIFFATTN_ERR_ALIGN;
     const size_t eb = elem_bytes(dtype);
+    diffattn::CacheStrides cs = diffattn::dense_cache_strides(H, L, d);
+    Span cache_span[3] = {{(uintptr_t)k1, (uintptr_t)k1 + (size_t)k_elems * eb},
+                          {(uintptr_t)k2, (uintptr_t)k2 + (size_t)k_elems * eb},
+                          {(uintptr_t)v, (uintptr_t)v + (size_t)v_elems * eb}};
+    if (strided) {
+        if (dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
+        const void* cp[3] = {k1, k2, v};
+        for (int k = 0; k < 3; ++k) {
+            cs.b[k] = cache_strides[3 * k];
+            cs.h[k] = cache_strides[3 * k + 1];
+            cs.n[k] = cache_strides[3 * k + 2];
+            const int64_t w = k == diffattn::C_V ? 2 * (int64_t)d : d;
+            if (cs.b[k] < 0 || cs.h[k] < 0 || cs.n[k] < w) return DIFFATTN_ERR_SHAPE;
+            if ((cs.b[k] | cs.h[k] | cs.n[k]) & 7) return DIFFATTN_ERR_ALIGN;   // 16-byte aligned rows
+            int64_t t1, t2, t3;
+            if (!mul_ok(B - 1, cs.b[k], &t1) || !mul_ok(H - 1, cs.h[k], &t2) || !mul_ok(L - 1, cs.n[k], &t3) ||
+                t1 > INT64_MAX / 4 || t2 > INT64_MAX / 4 || t3 > INT64_MAX / 4)
+                return DIFFATTN_ERR_SHAPE;
+            cache_span[k] = Span{(uintptr_t)cp[k], (uintptr_t)cp[k] + (uintptr_t)(t1 + t2 + t3 + w) * eb};
+        }
+    }
     const Span o{(uintptr_t)out, (uintptr_t)out + (size_t)q_elems * 2 * eb};
-    const Span ins[5] = {{(uintptr_t)q1, (uintptr_t)q1 + (size_t)q_elems * eb},
-                         {(uintptr_t)k1, (uintptr_t)k1 + (size_t)k_elems * eb},
-                         {(uintptr_t)q2, (uintptr_t)q2 + (size_t)q_elems * eb},
-                         {(uintptr_t)k2, (uintptr_t)k2 + (size_t)k_elems * eb},
-                         {(uintptr_t)v, (uintptr_t)v + (size_t)v_elems * eb}};
+    const Span ins[5] = {{(uintptr_t)q1, (uintptr_t)q1 + (size_t)q_elems * eb}, cache_span[0],
+                         {(uintptr_t)q2, (uintptr_t)q2 + (size_t)q_elems * eb}, cache_span[1], cache_span[2]};
     for (const Span& s : ins)
         if (overlaps(o, s)) return DIFFATTN_ERR_ALIAS;
     if (per_head) {
@@ -278,7 +299,7 @@ int decode_impl(const void* q1, const void* k1, const void* q2, const void* k2, 
     if (lens && overlaps(w, ls)) return DIFFATTN_ERR_ALIAS;
     return hip_status(diffattn::launch_decode_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
                                                        (const uint16_t*)k2, (const uint16_t*)v, (uint16_t*)out, BH, H,
-                                                       L, (int)T, lens, nullptr, ep, workspace, s));
+                                                       L, (int)T, lens, nullptr, cs, ep, workspace, s));
 }
 
 }  // namespace
@@ -375,7 +396,8 @@ int diffattn_decode_paged(const void* q1, const void* k1_pages, const void* q2, 
     const diffattn::DecodePages pg{block_table, (int)max_pages, lp, (int)num_pages};
     return hip_status(diffattn::launch_decode_bf16_d64(
         (const uint16_t*)q1, (const uint16_t*)k1_pages, (const uint16_t*)q2, (const uint16_t*)k2_pages,
-        (const uint16_t*)v_pages, (uint16_t*)out, BH, H, L, (int)T, lens, &pg, ep, workspace, (hipStream_t)stream));
+        (const uint16_t*)v_pages, (uint16_t*)out, BH, H, L, (int)T, lens, &pg, diffattn::dense_cache_strides(H, L, d), ep,
+        workspace, (hipStream_t)stream));
 }
 
 int diffattn_decode_varlen(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
@@ -384,6 +406,15 @@ int diffattn_decode_varlen(const void* q1, const void* k1, const void* q2, const
                            size_t workspace_bytes, void* stream) {
     return decode_impl(q1, k1, q2, k2, v, out, B, H, T, L, lens, true, d, dtype, lambda_heads ? 0.0f : lambda,
                        lambda_heads, lambda_heads != nullptr, layer, workspace, workspace_bytes, stream);
+}
+
+int diffattn_decode_strided(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
+                            int64_t B, int64_t H, int64_t T, int64_t L, const int32_t* lens,
+                            const int64_t* cache_strides, int d, int dtype, float lambda, const float* lambda_heads,
+                            int layer, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(q1, k1, q2, k2, v, out, B, H, T, L, lens, true, d, dtype, lambda_heads ? 0.0f : lambda,
+                       lambda_heads, lambda_heads != nullptr, layer, workspace, workspace_bytes, stream, true,
+                       cache_strides);
 }
 
 

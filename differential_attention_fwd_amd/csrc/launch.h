@@ -80,11 +80,31 @@ struct DecodePages {
     int max_pages, log2_page, num_pages;
 };
 
+// Element strides of the three padded decode caches, indexed k1, k2, v: batch, head and row.  The feature dimension
+// is contiguous.  Paged caches ignore them.
+struct CacheStrides {
+    int64_t b[3], h[3], n[3];
+};
+enum { C_K1 = 0, C_K2 = 1, C_V = 2 };
+
+// Dense [B][H][L][d] (and [B][H][L][2d] for v) strides.
+inline CacheStrides dense_cache_strides(int64_t H, int64_t L, int64_t d) {
+    CacheStrides s;
+    for (int k = 0; k < 3; ++k) {
+        const int64_t w = k == C_V ? 2 * d : d;
+        s.b[k] = H * L * w;
+        s.h[k] = L * w;
+        s.n[k] = w;
+    }
+    return s;
+}
+
 size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L, int T);
-// pages == nullptr: contiguous caches [B][H][L][w].
+// pages == nullptr: padded caches addressed through cs (cache row r of head (b, h) of tensor t at element
+// b cs.b[t] + h cs.h[t] + r cs.n[t]); otherwise the page pools.
 hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
                                   const uint16_t* v, uint16_t* out, int64_t BH, int64_t H, int64_t L, int T,
-                                  const int* lens, const DecodePages* pages, Epilogue ep, void* workspace,
-                                  hipStream_t stream);
+                                  const int* lens, const DecodePages* pages, const CacheStrides& cs, Epilogue ep,
+                                  void* workspace, hipStream_t stream);
 
 }  // namespace diffattn

@@ -150,6 +150,28 @@ int diffattn_decode_varlen(const void *q1, const void *k1, const void *q2, const
                            size_t workspace_bytes, void *stream);
 
 /*
+ * Strided decode caches (bf16, d = 64): diffattn_decode_varlen with K1, K2 and V read through batch, head and row
+ * strides, so a cache kept token-major ([B][L][H][w]) or the key halves and values packed in one buffer (for
+ * example [B][L][H][d + d + 2d] straight from a fused projection) is read in place.  The computation is that of
+ * diffattn_decode_varlen ([U] worked example: the two query/key halves and the values); only the addressing of
+ * cache rows differs.
+ *   cache_strides: HOST array of 9 int64 values, for k1, k2, v in that order: the batch, head and row strides in
+ *                  elements.  Row r of head h of sequence b of tensor t starts at
+ *                  base_t + b*cache_strides[3t] + h*cache_strides[3t+1] + r*cache_strides[3t+2]; its d (or 2d)
+ *                  features are contiguous.  Every stride must be >= 0 and a multiple of 8 (16-byte rows; else
+ *                  DIFFATTN_ERR_ALIGN), a row stride at least the row width (else DIFFATTN_ERR_SHAPE).
+ *   q1, q2, out, T, L, lens, lambda, lambda_heads, layer, workspace: as for diffattn_decode_varlen (q1, q2 and out
+ *   contiguous; the workspace size is diffattn_decode_varlen_workspace_bytes(B, H, T, L, d)).
+ * Errors as for diffattn_decode_varlen; cache_strides NULL is DIFFATTN_ERR_NULL; out or the workspace overlapping
+ * any cache's address range (its bounding box) is DIFFATTN_ERR_ALIAS; the caches may overlap each other.  Dense
+ * strides give diffattn_decode_varlen's result bit for bit.
+ */
+int diffattn_decode_strided(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
+                            int64_t B, int64_t H, int64_t T, int64_t L, const int32_t *lens,
+                            const int64_t *cache_strides, int d, int dtype, float lambda, const float *lambda_heads,
+                            int layer, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Paged decode (bf16, d = 64): diffattn_decode_varlen over caches kept in fixed-size pages of a pool shared by all
  * sequences, the layout of a serving cache that grows a page at a time.  The method is the same (the pages fix the
  * computation, not where the cache rows live); only the addressing of cache rows differs.

@@ -289,3 +289,49 @@ def test_paged_workspace_sizes(lib):
 ])
 def test_decode_paged_validation(lib, case, expect):
     assert dec_paged(lib, **case) == expect
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Strided decode caches: validation only (every case fails before any HIP call, or has no work)
+# ---------------------------------------------------------------------------------------------------------------
+def token_major(B, H, L, d):
+    """Strides of [B][L][H][w] caches viewed as [B][H][L][w]: k1, k2 (w = d) and v (w = 2d)."""
+    out = []
+    for w in (d, d, 2 * d):
+        out += [L * H * w, w, H * w]
+    return out
+
+
+def dec_strided(lib, strides="token", B=2, H=2, T=2, L=64, k1=A[1], k2=A[3], v=A[4], out=A[5], ws=G[2],
+                ws_bytes=None, lens=None, d=64, dtype=BF16, lam=0.8, layer=1):
+    if isinstance(strides, str):
+        strides = token_major(B, H, L, d)
+    arr = None if strides is None else (ctypes.c_int64 * 9)(*strides)
+    if ws_bytes is None:
+        ws_bytes = lib.diffattn_decode_varlen_workspace_bytes(max(B, 0), max(H, 0), max(T, 1), L, 64)
+    return lib.diffattn_decode_strided(A[0], k1, A[2], k2, v, out, B, H, T, L, lens, arr, d, dtype, lam, None, layer,
+                                       ws, ws_bytes, None)
+
+
+def with_stride(i, val):
+    s = token_major(2, 2, 64, 64)
+    s[i] = val
+    return s
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(strides=None), E_NULL), (dict(strides=None, B=0), OK),
+    (dict(strides=with_stride(2, 32)), E_SHAPE),            # k1 row stride below d
+    (dict(strides=with_stride(8, 64)), E_SHAPE),            # v row stride below 2d
+    (dict(strides=with_stride(0, -8)), E_SHAPE),            # negative batch stride
+    (dict(strides=with_stride(1, 4)), E_ALIGN),             # rows not 16-byte aligned
+    (dict(strides=with_stride(3, 1 << 62)), E_SHAPE),       # offsets overflow
+    (dict(out=A[1] + 2 * 64 * 2 * 64 * 2 - 256), E_ALIAS),  # out ends inside k1's token-major span
+    (dict(ws=A[4] + 1024), E_ALIAS),                        # workspace inside v's span
+    (dict(dtype=F32), E_UNSUP), (dict(d=8), E_UNSUP), (dict(T=0), E_SHAPE), (dict(T=17), E_SHAPE),
+    (dict(layer=-1), E_LAYER), (dict(lam=float("nan")), E_LAMBDA), (dict(lens=G[1] + 2), E_ALIGN),
+    # K1, K2 and V packed in one buffer may overlap each other: validation reaches the workspace check.
+    (dict(k2=A[1] + 128, v=A[1] + 256, strides=[64 * 2 * 256, 256, 2 * 256] * 3, ws=None), E_WS),
+])
+def test_decode_strided_validation(lib, case, expect):
+    assert dec_strided(lib, **case) == expect

@@ -405,6 +405,57 @@ def test_decode_varlen_per_head_lambda():
     check_bf16(host_bf16(out), ref, "decode varlen per-head")
 
 
+def strided_caches(dev, layout):
+    """Views of the same cache rows in another memory layout: 'token' = each cache token-major ([B][L][H][w]);
+    'packed' = K1, K2 and V of a row side by side in one [B][L][H][d + d + 2d] buffer."""
+    torch = torch_mod()
+    k1, k2, v = dev["k1"], dev["k2"], dev["v"]
+    if layout == "token":
+        return tuple(t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in (k1, k2, v))
+    B, H, L, d = k1.shape
+    buf = torch.empty(B, L, H, 4 * d, dtype=k1.dtype, device=k1.device)
+    buf[..., :d] = k1.permute(0, 2, 1, 3)
+    buf[..., d:2 * d] = k2.permute(0, 2, 1, 3)
+    buf[..., 2 * d:] = v.permute(0, 2, 1, 3)
+    return tuple(x.permute(0, 2, 1, 3) for x in (buf[..., :d], buf[..., d:2 * d], buf[..., 2 * d:]))
+
+
+@pytest.mark.parametrize("layout,B,H,T,L,lens", [
+    ("token", 2, 3, 1, 2000, [2000, 777]),
+    ("token", 2, 2, 4, 1500, None),
+    ("packed", 3, 2, 1, 1100, None),
+    ("packed", 2, 2, 5, 4100, [4100, 31]),
+])
+def test_decode_strided_equals_contiguous(layout, B, H, T, L, lens):
+    """Strided caches read in place give the contiguous call's bits (same kernels, same split plan)."""
+    torch = torch_mod()
+    inp = varlen_inputs(B, H, T, L, seed=900 + T + L)
+    say(f"case: decode strided {layout} B{B} H{H} T{T} L{L} lens={lens}")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    ldev = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda:0")
+    k1s, k2s, vs = strided_caches(dev, layout)
+    assert not k1s.is_contiguous()
+    a = da.diffattn_decode_varlen(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.8, 1, lens=ldev)
+    b = da.diffattn_decode_strided(dev["q1"], k1s, dev["q2"], k2s, vs, 0.8, 1, lens=ldev)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_decode_strided_vs_oracle():
+    torch = torch_mod()
+    B, H, T, L, lens = 2, 2, 3, 900, [900, 77]
+    inp = varlen_inputs(B, H, T, L, seed=950)
+    say(f"case: decode strided packed vs oracle B{B} H{H} T{T} L{L} lens={lens}, per-head lambda")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    ldev = torch.tensor(lens, dtype=torch.int32, device="cuda:0")
+    k1s, k2s, vs = strided_caches(dev, "packed")
+    lam = LAM_HEADS[:H]
+    out = da.diffattn_decode_strided(dev["q1"], k1s, dev["q2"], k2s, vs, dev_lam(lam), 2, lens=ldev)
+    torch.cuda.synchronize()
+    ref = varlen_reference(widen(inp), T, L, lens, lam.astype(np.float64), 2)
+    check_bf16(host_bf16(out), ref, "decode strided packed")
+
+
 def test_decode_varlen_single_token_equals_decode():
     """T = 1 without lengths runs the decode kernels: bit-identical to diffattn_decode."""
     torch = torch_mod()
