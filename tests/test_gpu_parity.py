@@ -222,6 +222,27 @@ def test_prefill_lambda_zero_and_layer_ratio():
     assert np.median(rel) < 1e-2 and rel.max() < 5e-2
 
 
+@pytest.mark.parametrize("causal,layer", [(True, 1), (False, 0)])
+def test_prefill_growing_scores(causal, layer):
+    """Map-1 scores that grow by half a nat per key (about 216 in log2 units over 300 keys) in head 0: the
+    probabilities at the first tile's offset would overflow, so the rows are recomputed at their final offsets.
+    Head 1 and map 2 keep ordinary N(0,1) scores."""
+    B, H, N = 1, 2, 300
+    inp = di.prefill_bf16(B, H, N, 64, seed=11)
+    q1 = di.bf16_bits_to_f32(inp["q1"]).copy()
+    k1 = di.bf16_bits_to_f32(inp["k1"]).copy()
+    q1[0, 0, :, 0] = 64.0                                   # s_ij = q1_i . k1_j / 8 = j / 2 + noise
+    k1[0, 0, :, 0] = np.arange(N, dtype=np.float32) / 16.0
+    inp["q1"] = di.f32_to_bf16_bits(q1)
+    inp["k1"] = di.f32_to_bf16_bits(k1)
+    lam = 0.8 if layer == 0 else lam_of(("lambda_init", layer))
+    say(f"case: prefill growing scores N{N} causal={causal} layer={layer}")
+    got = run_prefill_bf16(inp, lam, layer, causal)
+    f = widen(inp)
+    ref = oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam, layer, causal)
+    check_bf16(got, ref, "growing scores")
+
+
 def test_prefill_deterministic():
     torch = torch_mod()
     inp = di.prefill_bf16(2, 3, 700, 64, seed=10)
