@@ -121,6 +121,9 @@ __device__ __forceinline__ int seq_len(const int* lens, int b, int lo, int L) {
     return lens ? min(max(lens[b], lo), L) : L;
 }
 
+// 16-byte nontemporal load (cache policy "nt": streamed data that will not be read again).
+__device__ __forceinline__ u32x4 ldnt(const uint16_t* p) { return __builtin_nontemporal_load((const u32x4*)p); }
+
 __device__ __forceinline__ void write_empty(float* dst, int tid) {
     if (tid == 0) {
         dst[0] = -INFINITY;
@@ -169,8 +172,9 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     for (int r0 = 0; r0 < n; r0 += 32) {
         const int r = r0 + r_in;
         const int rr = min(r, n - 1);
-        const u32x4 ka = *(const u32x4*)(gk1 + cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, j0 + rr, C_K1, D) + ch * 8);
-        const u32x4 kb = *(const u32x4*)(gk2 + cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, j0 + rr, C_K2, D) + ch * 8);
+        // Cache rows are read once: nontemporal loads stream them without displacing other data in the caches.
+        const u32x4 ka = ldnt(gk1 + cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, j0 + rr, C_K1, D) + ch * 8);
+        const u32x4 kb = ldnt(gk2 + cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, j0 + rr, C_K2, D) + ch * 8);
         float s1 = dot8(qa, ka, 0.f), s2 = dot8(qb, kb, 0.f);
         s1 += __shfl_xor(s1, 1); s2 += __shfl_xor(s2, 1);
         s1 += __shfl_xor(s1, 2); s2 += __shfl_xor(s2, 2);
@@ -215,7 +219,7 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     for (int r0 = 0; r0 < n; r0 += 16) {
         const int r = r0 + vr_in;
         if (r < n) {
-            const u32x4 w = *(const u32x4*)(gv + cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, j0 + r, C_V, DV) + vc * 8);
+            const u32x4 w = ldnt(gv + cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, j0 + r, C_V, DV) + vc * 8);
             const float p1 = sc1[r], p2 = sc2[r];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -357,12 +361,12 @@ __device__ __forceinline__ int mv_off(int row, int chunk) { return row * 256 + (
 __device__ __forceinline__ int mk_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 // One 16-byte-per-lane direct load from global memory to LDS: lane L writes LDS [lds + 16 L, lds + 16 L + 16) with
-// the 16 bytes at src.  The s_nop is the wait state an LDS DMA needs after an SALU write of M0 (the compiler cannot
+// the 16 bytes at src, nontemporal (each cache row is read once).  The s_nop is the wait state an LDS DMA needs after an SALU write of M0 (the compiler cannot
 // insert it inside the asm); nothing else in this kernel keeps a value in M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* src, unsigned lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds)
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
