@@ -533,6 +533,42 @@ def test_prefill_strided_packed_projection():
     check_bf16(host_bf16(oview.contiguous()), ref, "strided prefill")
 
 
+def test_prefill_strided_at_offset_limit():
+    """K1 | K2 | V packed in rows of 8192 elements (16 KiB).  N = 261887 is the largest N whose per-head buffer
+    range for the direct loads, (N + 256) rows of that stride plus one row of V, fits 32-bit offsets: bit-identical
+    to the contiguous call, sampled rows (the last ones read the highest offsets) within tolerance of the oracle,
+    and N + 1 rejected as a shape error before any launch."""
+    torch = torch_mod()
+    N, RS, layer = 261887, 8192, 3
+    assert (N + 256) * RS * 2 + 256 <= 2**32 - 1 < (N + 257) * RS * 2 + 256
+    say(f"case: strided prefill at the 32-bit offset limit, N{N} row stride {RS} causal layer {layer}")
+    g = torch.Generator(device="cuda:0").manual_seed(900)
+    buf = torch.empty((N + 1, RS), dtype=torch.bfloat16, device="cuda:0")
+    buf[:, :256] = torch.randn((N + 1, 256), generator=g, device="cuda:0").to(torch.bfloat16)
+    q = torch.randn((2, 1, 1, N, 64), generator=g, device="cuda:0").to(torch.bfloat16)
+    lam = lam_of(("lambda_init", layer))
+
+    def views(n):
+        part = lambda lo, w: buf[:n, lo:lo + w].unsqueeze(0).unsqueeze(0)   # [1][1][n][w], row stride RS
+        return part(0, 64), part(64, 64), part(128, 128)
+
+    k1v, k2v, vv = views(N)
+    got = da.diffattn_fwd_strided(q[0], k1v, q[1], k2v, vv, lam, layer, True)
+    ref_dev = da.diffattn_fwd(q[0], k1v.contiguous(), q[1], k2v.contiguous(), vv.contiguous(), lam, layer, True)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref_dev.view(torch.int16))
+    rows = np.array([0, 1, 127, 128, 4096, N // 2, N - 257, N - 256, N - 33, N - 32, N - 1]
+                    + [int(x) for x in np.random.default_rng(900).integers(0, N, 21)], dtype=np.int64)
+    host = lambda t: t.float().cpu().numpy()
+    ref = oracle.diffattn(host(q[0]), host(k1v), host(q[1]), host(k2v), host(vv), lam, layer, True, rows=rows)
+    check_bf16(host_bf16(got).reshape(N, 128)[rows], ref, "strided prefill at the offset limit")
+    q_big = torch.zeros((1, 1, N + 1, 64), dtype=torch.bfloat16, device="cuda:0")
+    k1b, k2b, vb = views(N + 1)
+    with pytest.raises(da.DiffAttnError) as e:
+        da.diffattn_fwd_strided(q_big, k1b, q_big, k2b, vb, lam, layer, True)
+    assert e.value.status == -2
+
+
 def test_prefill_strided_interleaved_heads():
     """Q and K with the two halves interleaved per head ([B][N][2H][64], half 1 at even, half 2 at odd heads),
     non-causal, per-head lambda: bit-identical to the contiguous call."""
