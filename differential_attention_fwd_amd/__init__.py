@@ -21,8 +21,9 @@ STATUS = {0: "DIFFATTN_OK", -1: "DIFFATTN_ERR_NULL", -2: "DIFFATTN_ERR_SHAPE", -
 EXPORTS = ["diffattn_fwd", "diffattn_fwd_heads", "diffattn_fwd_strided", "diffattn_decode", "diffattn_decode_heads",
            "diffattn_decode_workspace_bytes", "diffattn_decode_varlen_workspace_bytes", "diffattn_decode_varlen",
            "diffattn_decode_paged_workspace_bytes", "diffattn_decode_paged", "diffattn_decode_strided",
-           "diffattn_train_saved_bytes", "diffattn_fwd_train",
-           "diffattn_bwd_workspace_bytes", "diffattn_bwd", "diffattn_lambda_init", "diffattn_status_str",
+           "diffattn_train_saved_bytes", "diffattn_fwd_train", "diffattn_fwd_train_strided",
+           "diffattn_bwd_workspace_bytes", "diffattn_bwd", "diffattn_bwd_strided", "diffattn_lambda_init",
+           "diffattn_status_str",
            "diffattn_abi_version"]
 
 _lib = None
@@ -78,6 +79,12 @@ def lib() -> ctypes.CDLL:
     L.diffattn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, P, c_int,
                                c_int, P, ctypes.c_size_t, P]
     L.diffattn_bwd.restype = c_int
+    L.diffattn_fwd_train_strided.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, P, c_int, c_int,
+                                             P, P, ctypes.c_size_t, P]
+    L.diffattn_fwd_train_strided.restype = c_int
+    L.diffattn_bwd_strided.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, P,
+                                       c_int, c_int, P, P, ctypes.c_size_t, P]
+    L.diffattn_bwd_strided.restype = c_int
     L.diffattn_decode_workspace_bytes.argtypes = [i64, i64, i64, c_int]
     L.diffattn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.diffattn_lambda_init.argtypes = [c_int]
@@ -403,3 +410,61 @@ def diffattn_fwd_strided(q1, k1, q2, k2, v, lam, layer: int, causal: bool, out=N
     if st != 0:
         raise DiffAttnError(st, "diffattn_fwd_strided")
     return out
+
+
+def _strided_views(ts, widths, shape4, what):
+    B, H, N = shape4
+    for t, w in zip(ts, widths):
+        if not t.is_cuda or t.dtype != ts[0].dtype or tuple(t.shape) != (B, H, N, w) or t.stride(-1) != 1:
+            raise ValueError(f"{what} needs [B][H][N][w] GPU views of one dtype with a contiguous last dimension")
+    return (ctypes.c_int64 * (3 * len(ts)))(*[int(x) for t in ts for x in t.stride()[:3]])
+
+
+def diffattn_fwd_train_strided(q1, k1, q2, k2, v, lam, layer: int, causal: bool, out=None, saved=None, stream=None):
+    """Training forward (bf16, d = 64) on strided [B][H][N][.] views (e.g. slices of packed projection outputs);
+    out may be a strided view too.  Returns (out, saved) as diffattn_fwd_train."""
+    import torch
+    B, H, N, d = q1.shape
+    if out is None:
+        out = torch.empty((B, H, N, 2 * d), dtype=q1.dtype, device=q1.device)
+    if saved is None:
+        saved = torch.empty(max(diffattn_train_saved_bytes(B, H, N, d), 16), dtype=torch.uint8, device=q1.device)
+    _check_tensors((saved,))
+    strides = _strided_views((q1, k1, q2, k2, v, out), (d, d, d, d, 2 * d, 2 * d), (B, H, N),
+                             "strided training forward")
+    lam_f, lam_p = _lambda_args(lam, H, q1.device)
+    st = lib().diffattn_fwd_train_strided(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
+                                          out.data_ptr(), B, H, N, d, _dtype_code(q1), lam_f, lam_p, int(layer),
+                                          int(bool(causal)), strides, saved.data_ptr(),
+                                          saved.numel() * saved.element_size(), _stream_handle(stream, q1.device))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_fwd_train_strided")
+    return out, saved
+
+
+def diffattn_bwd_strided(q1, k1, q2, k2, v, dy, saved, lam, layer: int, causal: bool, grads, workspace=None,
+                         stream=None):
+    """Backward (bf16, d = 64) on strided views: q1, k1, q2, k2, v, dy and the gradients grads["dq1"], ["dk1"],
+    ["dq2"], ["dk2"], ["dv"] are [B][H][N][.] GPU views with a contiguous last dimension (e.g. column slices of one
+    packed projection buffer and of its gradient buffer); grads["dlambda"] is a float32 tensor of H values.
+    Returns grads."""
+    import torch
+    B, H, N, d = q1.shape
+    g = grads
+    _check_tensors((saved, g["dlambda"]))
+    strides = _strided_views((q1, k1, q2, k2, v, dy, g["dq1"], g["dk1"], g["dq2"], g["dk2"], g["dv"]),
+                             (d, d, d, d, 2 * d, 2 * d, d, d, d, d, 2 * d), (B, H, N), "strided backward")
+    need = diffattn_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q1.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lam_f, lam_p = _lambda_args(lam, H, q1.device)
+    st = lib().diffattn_bwd_strided(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
+                                    dy.data_ptr(), saved.data_ptr(), g["dq1"].data_ptr(), g["dk1"].data_ptr(),
+                                    g["dq2"].data_ptr(), g["dk2"].data_ptr(), g["dv"].data_ptr(),
+                                    g["dlambda"].data_ptr(), B, H, N, d, _dtype_code(q1), lam_f, lam_p, int(layer),
+                                    int(bool(causal)), strides, ws_ptr, ws_bytes, _stream_handle(stream, q1.device))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_bwd_strided")
+    return grads

@@ -99,7 +99,8 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 __global__ __launch_bounds__(THREADS) void bwd_pre_kernel(const uint16_t* __restrict__ dy, const float* __restrict__ saved,
                                                           uint16_t* __restrict__ dO, float* __restrict__ stats,
-                                                          float* __restrict__ dl_rows, int64_t rows, int N, Epilogue ep) {
+                                                          float* __restrict__ dl_rows, int64_t rows, int N, int H,
+                                                          BwdStrides gs, Epilogue ep) {
     const int q = threadIdx.x & 15;
     const int64_t row_u = (int64_t)blockIdx.x * PRE_ROWS + (threadIdx.x >> 4);
     const bool live = row_u < rows;
@@ -107,7 +108,8 @@ __global__ __launch_bounds__(THREADS) void bwd_pre_kernel(const uint16_t* __rest
     const int bh = (int)(row / N);
     const float lam = lambda_of(ep, bh);
     const float* srow = saved + row * SAVED_FLOATS;
-    const u32x4 dyw = *(const u32x4*)(dy + row * DV + 8 * q);
+    const int64_t i = row - (int64_t)bh * N;
+    const u32x4 dyw = *(const u32x4*)(dy + (bh / H) * gs.b[G_DY] + (bh % H) * gs.h[G_DY] + i * gs.n[G_DY] + 8 * q);
     const f32x4 o1a = *(const f32x4*)(srow + SAVED_O1 + 8 * q), o1b = *(const f32x4*)(srow + SAVED_O1 + 8 * q + 4);
     const f32x4 o2a = *(const f32x4*)(srow + SAVED_O2 + 8 * q), o2b = *(const f32x4*)(srow + SAVED_O2 + 8 * q + 4);
     const f32x4 hdr = *(const f32x4*)srow;   // lse1, lse2, r, unused
@@ -175,7 +177,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict_
                    const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
                    const uint16_t* __restrict__ gv, const uint16_t* __restrict__ gdo,
                    const float* __restrict__ stats, uint16_t* __restrict__ dq1, uint16_t* __restrict__ dq2,
-                   int BH, int N, int n_blocks, int causal, Epilogue ep) {
+                   int BH, int N, int n_blocks, int causal, int H, BwdStrides gs, Epilogue ep) {
     constexpr int K_TILE = TILE * D * 2, V_TILE = TILE * DV * 2;
     __shared__ __attribute__((aligned(16))) unsigned char kr0[2 * K_TILE], kr1[2 * K_TILE], kr2[2 * K_TILE],
         kr3[2 * K_TILE];
@@ -188,38 +190,48 @@ void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict_
     const int qb = causal ? (n_blocks - 1 - bid / BH) : bid / BH;   // heaviest query blocks first
     const int bh = bid % BH;
     const int q0 = qb * BLOCK, q0w = q0 + TILE * wave;
-    const size_t hqk = (size_t)bh * N * D, hv = (size_t)bh * N * DV;
+    const size_t hv = (size_t)bh * N * DV;   // the workspace's dO rows
+    const int64_t b_ = bh / H, h_ = bh % H;
+    auto gbase = [&](int k) { return b_ * gs.b[k] + h_ * gs.h[k]; };   // head's first element of caller tensor k
     const int q = q0w + l32, qc = min(q, N - 1);
     const float c = LOG2E * 0.125f;
 
-    // Per-head buffer resources: rows at or beyond N read as zero.  N is at most 2^23, so the offsets fit.
-    const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc((void*)(gk1 + hqk), (short)0, N * (D * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rk2 = __builtin_amdgcn_make_buffer_rsrc((void*)(gk2 + hqk), (short)0, N * (D * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(gv + hv), (short)0, N * (DV * 2), 0x00020000);
+    // Per-head buffer resources over the head's rows (row strides in bytes): rows at or beyond N read as zero.  The
+    // caller checked that N + 256 rows fit the unsigned 32-bit offsets.
+    const unsigned rbk1 = (unsigned)gs.n[G_K1] * 2u, rbk2 = (unsigned)gs.n[G_K2] * 2u, rbv = (unsigned)gs.n[G_V] * 2u;
+    const unsigned n1 = (unsigned)(N - 1);
+    const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc((void*)(gk1 + gbase(G_K1)), (short)0,
+                                                                         (int)(n1 * rbk1 + D * 2u), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk2 = __builtin_amdgcn_make_buffer_rsrc((void*)(gk2 + gbase(G_K2)), (short)0,
+                                                                         (int)(n1 * rbk2 + D * 2u), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(gv + gbase(G_V)), (short)0,
+                                                                        (int)(n1 * rbv + DV * 2u), 0x00020000);
 
     // Direct loads per wave and tile: K1 rows 8 wave .. + 7, K2 the same, V rows 4 p .. 4 p + 3 for pieces
     // p = wave and wave + 4 (lane L writes position 16 L of a 1 KiB piece).  Issued unconditionally, also past the
     // end (out of range: zeros), so every iteration issues the same number.
     const int krow = 8 * wave + (lane >> 3);
-    const unsigned k_voff = (unsigned)krow * (D * 2) + ((((lane & 7) ^ q_sw(krow))) << 4);
+    const unsigned k_chunk = (((lane & 7) ^ q_sw(krow))) << 4;
+    const unsigned k1_voff = (unsigned)krow * rbk1 + k_chunk, k2_voff = (unsigned)krow * rbk2 + k_chunk;
+    const unsigned k1_step = TILE * rbk1, k2_step = TILE * rbk2, v_step = TILE * rbv;   // bytes per tile
     unsigned v_voff[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int r = 4 * (wave + WAVES * j) + (lane >> 4);
-        v_voff[j] = (unsigned)r * (DV * 2) + ((((lane & 15) ^ do_sw(r))) << 4);
+        v_voff[j] = (unsigned)r * rbv + ((((lane & 15) ^ do_sw(r))) << 4);
     }
     auto issue = [&](auto S, int t) __attribute__((always_inline)) {
         constexpr int s0 = decltype(S)::value;
         unsigned char* ks = pick4<s0>(kr0, kr1, kr2, kr3);
         unsigned char* vs = pick4<s0>(vr0, vr1, vr2, vr3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk1, (lds_void*)(ks + 1024 * wave), 16,
-                                                 (int)(k_voff + (unsigned)t * K_TILE), 0, 0, 0);
+                                                 (int)(k1_voff + (unsigned)t * k1_step), 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk2, (lds_void*)(ks + K_TILE + 1024 * wave), 16,
-                                                 (int)(k_voff + (unsigned)t * K_TILE), 0, 0, 0);
+                                                 (int)(k2_voff + (unsigned)t * k2_step), 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vs + 1024 * (wave + WAVES * j)), 16,
-                                                     (int)(v_voff[j] + (unsigned)t * V_TILE), 0, 0, 0);
+                                                     (int)(v_voff[j] + (unsigned)t * v_step), 0, 0, 0);
     };
     constexpr int DQ_LOADS = 4;
 
@@ -235,8 +247,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict_
     bf16x8 qa[4], qbf[4], dob[8];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-        qa[kc] = *(const bf16x8*)(gq1 + hqk + (size_t)qc * D + 16 * kc + 8 * h);
-        qbf[kc] = *(const bf16x8*)(gq2 + hqk + (size_t)qc * D + 16 * kc + 8 * h);
+        qa[kc] = *(const bf16x8*)(gq1 + gbase(G_Q1) + qc * gs.n[G_Q1] + 16 * kc + 8 * h);
+        qbf[kc] = *(const bf16x8*)(gq2 + gbase(G_Q2) + qc * gs.n[G_Q2] + 16 * kc + 8 * h);
     }
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) dob[kc] = *(const bf16x8*)(gdo + hv + (size_t)qc * DV + 16 * kc + 8 * h);
@@ -348,8 +360,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict_
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     if (q >= N) return;
     const float sc1 = 0.125f, sc2 = -lambda_of(ep, bh) * 0.125f;
-    uint16_t* r1 = dq1 + hqk + (size_t)q * D + 4 * h;
-    uint16_t* r2 = dq2 + hqk + (size_t)q * D + 4 * h;
+    uint16_t* r1 = dq1 + gbase(G_DQ1) + q * gs.n[G_DQ1] + 4 * h;
+    uint16_t* r2 = dq2 + gbase(G_DQ2) + q * gs.n[G_DQ2] + 4 * h;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -392,7 +404,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
                      const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
                      const uint16_t* __restrict__ gv, const uint16_t* __restrict__ gdo,
                      const float* __restrict__ stats, uint16_t* __restrict__ dk1, uint16_t* __restrict__ dk2,
-                     uint16_t* __restrict__ dv, int BH, int N, int causal, Epilogue ep) {
+                     uint16_t* __restrict__ dv, int BH, int N, int causal, int H, BwdStrides gs, Epilogue ep) {
     __shared__ __attribute__((aligned(16))) unsigned char sl0[SLOT_BYTES], sl1[SLOT_BYTES], sl2[SLOT_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -402,15 +414,21 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
     const int kb = bid / BH;   // key blocks in order: the first ones see the most queries under the causal mask
     const int bh = bid % BH;
     const int k0 = kb * KBLK, k0w = k0 + KW * wave;
-    const size_t hqk = (size_t)bh * N * D, hv = (size_t)bh * N * DV;
+    const size_t hv = (size_t)bh * N * DV;   // the workspace's dO rows
+    const int64_t b_ = bh / H, h_ = bh % H;
+    auto gbase = [&](int k) { return b_ * gs.b[k] + h_ * gs.h[k]; };   // head's first element of caller tensor k
     const int key = k0w + l16, kc_row = min(key, N - 1);
     const float c = LOG2E * 0.125f;
     const float lam = lambda_of(ep, bh);
 
-    // Per-head buffer resources: rows at or beyond N read as zero.  Offsets are unsigned 32-bit; N is at most 2^23,
-    // so (N + 96) rows of 256 bytes fit.
-    const __amdgpu_buffer_rsrc_t rq1 = __builtin_amdgcn_make_buffer_rsrc((void*)(gq1 + hqk), (short)0, N * (D * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rq2 = __builtin_amdgcn_make_buffer_rsrc((void*)(gq2 + hqk), (short)0, N * (D * 2), 0x00020000);
+    // Per-head buffer resources: rows at or beyond N read as zero.  Offsets are unsigned 32-bit: the caller checked
+    // that N + 256 rows of Q1 and Q2 fit, and the workspace's dO rows (256 bytes each, N at most 2^23) do.
+    const unsigned rbq1 = (unsigned)gs.n[G_Q1] * 2u, rbq2 = (unsigned)gs.n[G_Q2] * 2u;
+    const unsigned n1 = (unsigned)(N - 1);
+    const __amdgpu_buffer_rsrc_t rq1 = __builtin_amdgcn_make_buffer_rsrc((void*)(gq1 + gbase(G_Q1)), (short)0,
+                                                                         (int)(n1 * rbq1 + D * 2u), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq2 = __builtin_amdgcn_make_buffer_rsrc((void*)(gq2 + gbase(G_Q2)), (short)0,
+                                                                         (int)(n1 * rbq2 + D * 2u), 0x00020000);
     const __amdgpu_buffer_rsrc_t rdo = __builtin_amdgcn_make_buffer_rsrc((void*)(gdo + hv), (short)0, N * (DV * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc((void*)(stats + (size_t)bh * N * STAT_FLOATS),
                                                                          (short)0, N * (STAT_FLOATS * 4), 0x00020000);
@@ -420,7 +438,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
     // (lanes 0..31, 4 bytes each, so the stats land as [stat][query]).  Loads are issued unconditionally, also for
     // tiles past the end (out of range: zeros), so every iteration issues the same number.
     const int qrow = 8 * wave + (lane >> 3);
-    const unsigned q_voff = (unsigned)qrow * (D * 2) + ((((lane & 7) ^ q_sw(qrow))) << 4);
+    const unsigned q_chunk = (((lane & 7) ^ q_sw(qrow))) << 4;
+    const unsigned q1_voff = (unsigned)qrow * rbq1 + q_chunk, q2_voff = (unsigned)qrow * rbq2 + q_chunk;
+    const unsigned q1_step = TILE * rbq1, q2_step = TILE * rbq2;   // bytes per tile
     unsigned do_voff[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -431,9 +451,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
     auto issue = [&](auto S, int u) __attribute__((always_inline)) {
         unsigned char* s = pick3<decltype(S)::value>(sl0, sl1, sl2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rq1, (lds_void*)(s + 1024 * wave), 16,
-                                                 (int)(q_voff + (unsigned)u * (TILE * D * 2)), 0, 0, 0);
+                                                 (int)(q1_voff + (unsigned)u * q1_step), 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rq2, (lds_void*)(s + Q_TILE_BYTES + 1024 * wave), 16,
-                                                 (int)(q_voff + (unsigned)u * (TILE * D * 2)), 0, 0, 0);
+                                                 (int)(q2_voff + (unsigned)u * q2_step), 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rdo, (lds_void*)(s + 2 * Q_TILE_BYTES + 1024 * (wave + WAVES * j)),
@@ -455,11 +475,11 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
     bf16x8 kb1[2], kb2[2], vb[4];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-        kb1[kh] = *(const bf16x8*)(gk1 + hqk + (size_t)kc_row * D + 32 * kh + 8 * g);
-        kb2[kh] = *(const bf16x8*)(gk2 + hqk + (size_t)kc_row * D + 32 * kh + 8 * g);
+        kb1[kh] = *(const bf16x8*)(gk1 + gbase(G_K1) + kc_row * gs.n[G_K1] + 32 * kh + 8 * g);
+        kb2[kh] = *(const bf16x8*)(gk2 + gbase(G_K2) + kc_row * gs.n[G_K2] + 32 * kh + 8 * g);
     }
 #pragma unroll
-    for (int kh = 0; kh < 4; ++kh) vb[kh] = *(const bf16x8*)(gv + hv + (size_t)kc_row * DV + 32 * kh + 8 * g);
+    for (int kh = 0; kh < 4; ++kh) vb[kh] = *(const bf16x8*)(gv + gbase(G_V) + kc_row * gs.n[G_V] + 32 * kh + 8 * g);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) asm volatile("" ::"v"(kb1[kh]), "v"(kb2[kh]));
 #pragma unroll
@@ -578,9 +598,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     if (key >= N) return;
     const float sc1 = 0.125f, sc2 = -lam * 0.125f;
-    uint16_t* r1 = dk1 + hqk + (size_t)key * D + 4 * g;
-    uint16_t* r2 = dk2 + hqk + (size_t)key * D + 4 * g;
-    uint16_t* rvv = dv + hv + (size_t)key * DV + 4 * g;
+    uint16_t* r1 = dk1 + gbase(G_DK1) + key * gs.n[G_DK1] + 4 * g;
+    uint16_t* r2 = dk2 + gbase(G_DK2) + key * gs.n[G_DK2] + 4 * g;
+    uint16_t* rvv = dv + gbase(G_DV) + key * gs.n[G_DV] + 4 * g;
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
         u32x2 w1, w2;
@@ -644,7 +664,8 @@ size_t bwd_bf16_workspace_bytes(int64_t BH, int64_t N) {
 hipError_t launch_bwd_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
                                const uint16_t* v, const uint16_t* dy, const float* saved, uint16_t* dq1,
                                uint16_t* dk1, uint16_t* dq2, uint16_t* dk2, uint16_t* dv, float* dlambda, int64_t B,
-                               int64_t H, int64_t N, int causal, Epilogue ep, void* workspace, hipStream_t stream) {
+                               int64_t H, int64_t N, int causal, Epilogue ep, const BwdStrides& gs, void* workspace,
+                               hipStream_t stream) {
     const int64_t BH = B * H, rows = BH * N;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     unsigned char* ws = (unsigned char*)workspace;
@@ -662,11 +683,11 @@ hipError_t launch_bwd_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uin
         return hipGetLastError();
     }
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)pre_blocks), dim3(THREADS), 0, stream, dy, saved, dO, stats,
-                       dl_rows, rows, (int)N, ep);
+                       dl_rows, rows, (int)N, (int)H, gs, ep);
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)grid), dim3(THREADS), 0, stream, q1, k1, q2, k2, v, dO, stats,
-                       dq1, dq2, (int)BH, (int)N, n_blocks, causal ? 1 : 0, ep);
+                       dq1, dq2, (int)BH, (int)N, n_blocks, causal ? 1 : 0, (int)H, gs, ep);
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_grid), dim3(THREADS), 0, stream, q1, k1, q2, k2, v, dO,
-                       stats, dk1, dk2, dv, (int)BH, (int)N, causal ? 1 : 0, ep);
+                       stats, dk1, dk2, dv, (int)BH, (int)N, causal ? 1 : 0, (int)H, gs, ep);
     hipLaunchKernelGGL(bwd_dlambda_kernel, dim3((unsigned)H), dim3(DL_THREADS), 0, stream, dl_rows, dlambda, (int)B,
                        (int)H, (int)N);
     return hipGetLastError();

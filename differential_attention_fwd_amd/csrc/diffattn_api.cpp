@@ -490,7 +490,8 @@ int diffattn_bwd(const void* q1, const void* k1, const void* q2, const void* k2,
     if (rows == 0)   // no rows: dlambda is zero (written by a kernel, so the call stays capturable in a graph)
         return hip_status(diffattn::launch_bwd_bf16_d64(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                                          nullptr, nullptr, nullptr, nullptr, nullptr, dlambda, B, H, 0,
-                                                         causal, ep, nullptr, (hipStream_t)stream));
+                                                         causal, ep, diffattn::dense_bwd_strides(H, 0, d), nullptr,
+                                                         (hipStream_t)stream));
     if (!q1 || !k1 || !q2 || !k2 || !v || !dy || !saved || !dq1 || !dk1 || !dq2 || !dk2 || !dv) return DIFFATTN_ERR_NULL;
     const void* a16[] = {q1, k1, q2, k2, v, dy, saved, dq1, dk1, dq2, dk2, dv};
     for (const void* p : a16)
@@ -526,7 +527,180 @@ int diffattn_bwd(const void* q1, const void* k1, const void* q2, const void* k2,
     return hip_status(diffattn::launch_bwd_bf16_d64(
         (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2, (const uint16_t*)k2, (const uint16_t*)v,
         (const uint16_t*)dy, (const float*)saved, (uint16_t*)dq1, (uint16_t*)dk1, (uint16_t*)dq2, (uint16_t*)dk2,
-        (uint16_t*)dv, dlambda, B, H, N, causal, ep, workspace, (hipStream_t)stream));
+        (uint16_t*)dv, dlambda, B, H, N, causal, ep, diffattn::dense_bwd_strides(H, N, d), workspace,
+        (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Byte footprint of one strided bf16 tensor [B][H][N][w] for overlap checks: its bounding box, the byte strides of
+// its dimensions of extent > 1 (0 for the others) and its row width in bytes.
+struct Footprint {
+    uintptr_t lo, hi;
+    int64_t sb, sh, sn, wb;
+};
+
+Footprint dense_footprint(const void* p, size_t bytes) {
+    return Footprint{(uintptr_t)p, (uintptr_t)p + bytes, 0, 0, 0, (int64_t)bytes};
+}
+
+// Validates one strided tensor (element strides s[0..2] for batch, head and row; rows of w contiguous elements) and
+// returns its footprint.  `buffered` tensors are read through 32-bit buffer offsets: one head's N + 256 rows must
+// span less than 4 GiB.
+int strided_tensor(const void* p, int64_t B, int64_t H, int64_t N, int64_t w, const int64_t* s, bool buffered,
+                   Footprint* f) {
+    const int64_t sb = s[0], sh = s[1], sn = s[2];
+    if (sb < 0 || sh < 0 || sn < w) return DIFFATTN_ERR_SHAPE;
+    if ((sb | sh | sn) & 7) return DIFFATTN_ERR_ALIGN;   // 16-byte aligned rows
+    int64_t t1, t2, t3;
+    if (!mul_ok(B - 1, sb, &t1) || !mul_ok(H - 1, sh, &t2) || !mul_ok(N - 1, sn, &t3) || t1 > INT64_MAX / 4 ||
+        t2 > INT64_MAX / 4 || t3 > INT64_MAX / 4)
+        return DIFFATTN_ERR_SHAPE;
+    if (buffered) {
+        int64_t range;
+        if (!mul_ok(N + 256, sn * 2, &range) || range + w * 2 > (int64_t)UINT32_MAX) return DIFFATTN_ERR_SHAPE;
+    }
+    *f = Footprint{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(t1 + t2 + t3 + w) * 2, B > 1 ? 2 * sb : 0,
+                   H > 1 ? 2 * sh : 0, N > 1 ? 2 * sn : 0, 2 * w};
+    return DIFFATTN_OK;
+}
+
+int64_t gcd64(int64_t a, int64_t b) {
+    while (b) {
+        const int64_t t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+// True when two footprints provably share no byte: their bounding boxes are disjoint, or every byte of each lies at
+// its base plus a multiple of m = gcd(all their strides) plus a column offset below its row width, and the two
+// resulting arcs of residues modulo m do not meet (interleaved rows of one packed buffer).
+bool disjoint(const Footprint& a, const Footprint& b) {
+    if (!overlaps(Span{a.lo, a.hi}, Span{b.lo, b.hi})) return true;
+    int64_t m = 0;
+    for (int64_t x : {a.sb, a.sh, a.sn, b.sb, b.sh, b.sn}) m = gcd64(m, x);
+    if (m == 0 || a.wb + b.wb > m) return false;
+    const int64_t ra = (int64_t)(a.lo % (uint64_t)m), rb = (int64_t)(b.lo % (uint64_t)m);
+    return ((rb - ra) % m + m) % m >= a.wb && ((ra - rb) % m + m) % m >= b.wb;
+}
+
+}  // namespace
+
+extern "C" {
+
+int diffattn_fwd_train_strided(const void* q1, const void* k1, const void* q2, const void* k2, const void* v,
+                               void* out, int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda,
+                               const float* lambda_heads, int layer, int causal, const int64_t* strides, void* saved,
+                               size_t saved_bytes, void* stream) {
+    if (B < 0 || H < 0 || N < 0 || N > DIFFATTN_MAX_LEN) return DIFFATTN_ERR_SHAPE;
+    if (dtype != DIFFATTN_BF16 || d != 64) return DIFFATTN_ERR_UNSUPPORTED;
+    Epilogue ep;
+    int st = make_epilogue(lambda_heads ? 0.0f : lambda, layer, &ep);
+    if (st) return st;
+    int64_t BH, rows;
+    if (!mul_ok(B, H, &BH) || BH > INT32_MAX || !mul_ok(BH, N, &rows)) return DIFFATTN_ERR_SHAPE;
+    if (rows == 0) return DIFFATTN_OK;
+    if (!strides || !q1 || !k1 || !q2 || !k2 || !v || !out || !saved) return DIFFATTN_ERR_NULL;
+    const void* ptr[6] = {q1, k1, q2, k2, v, out};
+    for (const void* p : ptr)
+        if (!aligned16(p)) return DIFFATTN_ERR_ALIGN;
+    if (!aligned16(saved)) return DIFFATTN_ERR_ALIGN;
+    const size_t need = diffattn_train_saved_bytes(B, H, N, d);
+    if (saved_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+    Footprint f[6];
+    diffattn::Strides S;
+    for (int k = 0; k < 6; ++k) {
+        const bool wide = k == diffattn::S_V || k == diffattn::S_OUT;
+        const bool buffered = k == diffattn::S_K1 || k == diffattn::S_K2 || k == diffattn::S_V;
+        st = strided_tensor(ptr[k], B, H, N, wide ? 128 : 64, strides + 3 * k, buffered, &f[k]);
+        if (st) return st;
+        S.b[k] = strides[3 * k];
+        S.h[k] = strides[3 * k + 1];
+        S.n[k] = strides[3 * k + 2];
+    }
+    const Footprint sv = dense_footprint(saved, need);
+    if (!disjoint(f[diffattn::S_OUT], sv)) return DIFFATTN_ERR_ALIAS;
+    for (int k = 0; k < 5; ++k)
+        if (!disjoint(f[diffattn::S_OUT], f[k]) || !disjoint(sv, f[k])) return DIFFATTN_ERR_ALIAS;
+    if (lambda_heads) {
+        if (((uintptr_t)lambda_heads & 3u) != 0) return DIFFATTN_ERR_ALIGN;
+        const Footprint l = dense_footprint(lambda_heads, (size_t)H * sizeof(float));
+        if (!disjoint(l, f[diffattn::S_OUT]) || !disjoint(l, sv)) return DIFFATTN_ERR_ALIAS;
+        ep.lambda_heads = lambda_heads;
+        ep.heads = (int)H;
+    }
+    return hip_status(diffattn::launch_prefill_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
+                                                        (const uint16_t*)k2, (const uint16_t*)v, (uint16_t*)out, B, H,
+                                                        N, causal, S, ep, (float*)saved, (hipStream_t)stream));
+}
+
+int diffattn_bwd_strided(const void* q1, const void* k1, const void* q2, const void* k2, const void* v,
+                         const void* dy, const void* saved, void* dq1, void* dk1, void* dq2, void* dk2, void* dv,
+                         float* dlambda, int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda,
+                         const float* lambda_heads, int layer, int causal, const int64_t* strides, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (B < 0 || H < 0 || N < 0 || N > DIFFATTN_MAX_LEN) return DIFFATTN_ERR_SHAPE;
+    if (dtype != DIFFATTN_BF16 || d != 64) return DIFFATTN_ERR_UNSUPPORTED;
+    Epilogue ep;
+    int st = make_epilogue(lambda_heads ? 0.0f : lambda, layer, &ep);
+    if (st) return st;
+    int64_t BH, rows;
+    if (!mul_ok(B, H, &BH) || BH > INT32_MAX || !mul_ok(BH, N, &rows)) return DIFFATTN_ERR_SHAPE;
+    if (BH == 0) return DIFFATTN_OK;
+    if (!dlambda) return DIFFATTN_ERR_NULL;
+    if (((uintptr_t)dlambda & 3u) != 0) return DIFFATTN_ERR_ALIGN;
+    if (rows == 0)   // no rows: dlambda is zero, as for diffattn_bwd
+        return diffattn_bwd(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                            nullptr, nullptr, dlambda, B, H, N, d, dtype, lambda, lambda_heads, layer, causal, nullptr,
+                            0, stream);
+    if (!strides || !q1 || !k1 || !q2 || !k2 || !v || !dy || !saved || !dq1 || !dk1 || !dq2 || !dk2 || !dv)
+        return DIFFATTN_ERR_NULL;
+    const void* ptr[diffattn::BWD_TENSORS] = {q1, k1, q2, k2, v, dy, dq1, dk1, dq2, dk2, dv};
+    for (const void* p : ptr)
+        if (!aligned16(p)) return DIFFATTN_ERR_ALIGN;
+    if (!aligned16(saved)) return DIFFATTN_ERR_ALIGN;
+    const size_t need = diffattn_bwd_workspace_bytes(B, H, N, d);
+    if (!workspace || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return DIFFATTN_ERR_ALIGN;
+    Footprint f[diffattn::BWD_TENSORS];
+    diffattn::BwdStrides G;
+    for (int k = 0; k < diffattn::BWD_TENSORS; ++k) {
+        const bool wide = k == diffattn::G_V || k == diffattn::G_DY || k == diffattn::G_DV;
+        const bool buffered = k <= diffattn::G_V;   // q1, k1, q2, k2, v are read through buffer offsets
+        st = strided_tensor(ptr[k], B, H, N, wide ? 128 : 64, strides + 3 * k, buffered, &f[k]);
+        if (st) return st;
+        G.b[k] = strides[3 * k];
+        G.h[k] = strides[3 * k + 1];
+        G.n[k] = strides[3 * k + 2];
+    }
+    // Inputs: q1, k1, q2, k2, v, dy and saved (may overlap one another).  Outputs: the five gradients, dlambda and
+    // the workspace (must not overlap one another or any input).
+    const Footprint ins[7] = {f[0], f[1], f[2], f[3], f[4], f[5],
+                              dense_footprint(saved, diffattn_train_saved_bytes(B, H, N, d))};
+    const Footprint outs[7] = {f[6], f[7], f[8], f[9], f[10], dense_footprint(dlambda, (size_t)H * sizeof(float)),
+                               dense_footprint(workspace, need)};
+    for (int i = 0; i < 7; ++i) {
+        for (const Footprint& in : ins)
+            if (!disjoint(outs[i], in)) return DIFFATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 7; ++j)
+            if (!disjoint(outs[i], outs[j])) return DIFFATTN_ERR_ALIAS;
+    }
+    if (lambda_heads) {
+        if (((uintptr_t)lambda_heads & 3u) != 0) return DIFFATTN_ERR_ALIGN;
+        const Footprint l = dense_footprint(lambda_heads, (size_t)H * sizeof(float));
+        for (const Footprint& o : outs)
+            if (!disjoint(l, o)) return DIFFATTN_ERR_ALIAS;
+        ep.lambda_heads = lambda_heads;
+        ep.heads = (int)H;
+    }
+    return hip_status(diffattn::launch_bwd_bf16_d64(
+        (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2, (const uint16_t*)k2, (const uint16_t*)v,
+        (const uint16_t*)dy, (const float*)saved, (uint16_t*)dq1, (uint16_t*)dk1, (uint16_t*)dq2, (uint16_t*)dk2,
+        (uint16_t*)dv, dlambda, B, H, N, causal, ep, G, workspace, (hipStream_t)stream));
 }
 
 }  // extern "C"

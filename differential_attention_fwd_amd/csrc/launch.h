@@ -55,14 +55,36 @@ hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const
                                    const uint16_t* v, uint16_t* out, int64_t B, int64_t H, int64_t N, int causal,
                                    const Strides& st, Epilogue ep, float* saved, hipStream_t stream);
 
+// Element strides of the backward's caller tensors, indexed q1, k1, q2, k2, v, dy, dq1, dk1, dq2, dk2, dv: batch,
+// head and row.  The feature dimension is contiguous.
+constexpr int BWD_TENSORS = 11;
+struct BwdStrides {
+    int64_t b[BWD_TENSORS], h[BWD_TENSORS], n[BWD_TENSORS];
+};
+enum { G_Q1 = 0, G_K1, G_Q2, G_K2, G_V, G_DY, G_DQ1, G_DK1, G_DQ2, G_DK2, G_DV };
+
+// Dense [B][H][N][d] (and [B][H][N][2d] for v, dy and dv) strides.
+inline BwdStrides dense_bwd_strides(int64_t H, int64_t N, int64_t d) {
+    BwdStrides s;
+    for (int k = 0; k < BWD_TENSORS; ++k) {
+        const int64_t w = (k == G_V || k == G_DY || k == G_DV) ? 2 * d : d;
+        s.b[k] = H * N * w;
+        s.h[k] = N * w;
+        s.n[k] = w;
+    }
+    return s;
+}
+
 // bf16 backward, d = 64: preprocess, dQ, dK/dV and dlambda kernels (see backward_bf16.hip).  `saved` is the
 // training forward's [BH][N][SAVED_FLOATS]; `workspace` holds bwd_bf16_workspace_bytes(BH, N) bytes (256-byte
-// aligned); dlambda receives H floats (per head, summed over the batch).
+// aligned); dlambda receives H floats (per head, summed over the batch).  Caller tensors are addressed through `gs`;
+// the caller has checked that every head's Q1, K1, Q2, K2 and V rows, N + 256 of them, span less than 4 GiB.
 size_t bwd_bf16_workspace_bytes(int64_t BH, int64_t N);
 hipError_t launch_bwd_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
                                const uint16_t* v, const uint16_t* dy, const float* saved, uint16_t* dq1,
                                uint16_t* dk1, uint16_t* dq2, uint16_t* dk2, uint16_t* dv, float* dlambda, int64_t B,
-                               int64_t H, int64_t N, int causal, Epilogue ep, void* workspace, hipStream_t stream);
+                               int64_t H, int64_t N, int causal, Epilogue ep, const BwdStrides& gs, void* workspace,
+                               hipStream_t stream);
 
 // fp32 path (d = 8 or 64), general Nq <= Nk with end-aligned causal mask; exact three-pass softmax per row.
 hipError_t launch_attn_f32(const float* q1, const float* k1, const float* q2, const float* k2, const float* v,

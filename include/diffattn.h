@@ -229,6 +229,33 @@ int diffattn_bwd(const void *q1, const void *k1, const void *q2, const void *k2,
                  int64_t H, int64_t N, int d, int dtype, float lambda, const float *lambda_heads, int layer,
                  int causal, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Strided training (bf16, d = 64): diffattn_fwd_train and diffattn_bwd with every caller tensor addressed through
+ * element strides, so that q1, k1, q2, k2 and v are read straight out of packed projection outputs (as for
+ * diffattn_fwd_strided) and the five gradients written straight into the matching packed gradient buffer.  `saved`,
+ * the workspace and dlambda keep the dense layouts of the unstrided calls.
+ *   diffattn_fwd_train_strided: strides is a HOST array of 18 int64 values for q1, k1, q2, k2, v, out, laid out and
+ *     checked as for diffattn_fwd_strided; writes the same out and `saved` as diffattn_fwd_train on dense copies.
+ *   diffattn_bwd_strided: strides is a HOST array of 33 int64 values for q1, k1, q2, k2, v, dy, dq1, dk1, dq2, dk2,
+ *     dv in that order (batch, head and row strides in elements per tensor; rows of d or 2d contiguous elements).
+ *     Every stride must be >= 0 and a multiple of 8 (else DIFFATTN_ERR_ALIGN) and each row stride at least the row
+ *     width; one head's q1, k1, q2, k2 and v rows, N + 256 of them, must span less than 4 GiB (else
+ *     DIFFATTN_ERR_SHAPE).  Gives diffattn_bwd's results on dense copies bit for bit.
+ *   Aliasing: outputs (and, for the backward, the gradients, dlambda and the workspace among themselves) must not
+ *   share a byte with each other or with any input.  Two strided tensors count as disjoint when their bounding boxes
+ *   are, or when their rows fall in different residue classes modulo the gcd of all their byte strides (for example
+ *   the column slices of one packed buffer); anything else that overlaps is DIFFATTN_ERR_ALIAS.
+ */
+int diffattn_fwd_train_strided(const void *q1, const void *k1, const void *q2, const void *k2, const void *v,
+                               void *out, int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda,
+                               const float *lambda_heads, int layer, int causal, const int64_t *strides, void *saved,
+                               size_t saved_bytes, void *stream);
+int diffattn_bwd_strided(const void *q1, const void *k1, const void *q2, const void *k2, const void *v,
+                         const void *dy, const void *saved, void *dq1, void *dk1, void *dq2, void *dk2, void *dv,
+                         float *dlambda, int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda,
+                         const float *lambda_heads, int layer, int causal, const int64_t *strides, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 /* lambda_init(layer) = 0.8 - 0.6 exp(-0.3 (layer - 1)) in double, for layer >= 1 ([U]); NaN for layer < 1. */
 double diffattn_lambda_init(int layer);
 

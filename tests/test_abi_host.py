@@ -335,3 +335,76 @@ def with_stride(i, val):
 ])
 def test_decode_strided_validation(lib, case, expect):
     assert dec_strided(lib, **case) == expect
+
+
+# Strided training: a packed projection [B][N][H][6][64] (q1 | k1 | q2 | k2 | v) at A[0] and its packed gradient
+# buffer at G[0]; dy dense at A[7].  Every case changes the default (which itself would pass validation and is never
+# called) so that validation fails.
+def packed_strides(B, H, N, col, w):
+    del w
+    return [N * H * 384, 384, H * 384], col
+
+
+def train_strided_layout(B=1, H=2, N=64):
+    s_in, s_g = [], []
+    ptr_in, ptr_g = [], []
+    for col, w in ((0, 64), (64, 64), (128, 64), (192, 64), (256, 128)):
+        st, c = packed_strides(B, H, N, col, w)
+        s_in += st
+        ptr_in.append(A[0] + 2 * c)
+        s_g += st
+        ptr_g.append(G[0] + 2 * c)
+    dy = [H * N * 128, N * 128, 128]
+    return ptr_in, ptr_g, s_in, dy, s_g
+
+
+def bwd_strided(lib, edit=None, ptr_edit=None, B=1, H=2, N=64, dtype=BF16, strides_none=False):
+    ptr_in, ptr_g, s_in, s_dy, s_g = train_strided_layout(B, H, N)
+    strides = s_in + s_dy + s_g
+    ptrs = ptr_in + [A[7]] + ptr_g
+    if edit:
+        for i, v in edit.items():
+            strides[i] = v
+    if ptr_edit:
+        for i, v in ptr_edit.items():
+            ptrs[i] = v
+    arr = None if strides_none else (ctypes.c_int64 * 33)(*strides)
+    ws_bytes = lib.diffattn_bwd_workspace_bytes(B, H, N, 64)
+    return lib.diffattn_bwd_strided(*ptrs[:6], A[6], *ptrs[6:], G[5], B, H, N, 64, dtype, 0.5, None, 1, 1, arr,
+                                    G[6], ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(strides_none=True), E_NULL),
+    (dict(edit={2: 772}), E_ALIGN),                        # q1 row stride not a multiple of 8
+    (dict(edit={14: 120}), E_SHAPE),                       # v row stride below its 128-element row
+    (dict(edit={4: -384}), E_SHAPE),                       # negative head stride
+    (dict(edit={5: 1 << 24}), E_SHAPE),                    # k1's N + 256 rows past 4 GiB of buffer offsets
+    (dict(ptr_edit={6: A[0]}), E_ALIAS),                   # dq1 written over q1
+    (dict(ptr_edit={7: G[0] + 64}), E_ALIAS),              # dk1 overlapping dq1 inside each packed row
+    (dict(ptr_edit={10: G[0] + 2 * 320}), E_ALIAS),        # dv (128 wide) running into the next head's dq1
+    (dict(ptr_edit={5: G[0] + 2 * 64}), E_ALIAS),          # dy read from where dk1 is written
+    (dict(dtype=F32), E_UNSUP), (dict(B=0), OK),
+])
+def test_bwd_strided_validation(lib, case, expect):
+    assert bwd_strided(lib, **case) == expect
+
+
+def fwd_train_strided(lib, strides_none=False, out=None, saved=A[6], edit=None, N=64):
+    ptr_in, _, s_in, _, _ = train_strided_layout(N=N)
+    s = s_in + [2 * N * 128, N * 128, 128]
+    if edit:
+        for i, v in edit.items():
+            s[i] = v
+    arr = None if strides_none else (ctypes.c_int64 * 18)(*s)
+    need = lib.diffattn_train_saved_bytes(1, 2, N, 64)
+    return lib.diffattn_fwd_train_strided(*ptr_in, A[5] if out is None else out, 1, 2, N, 64, BF16, 0.5, None, 1, 1,
+                                          arr, saved, need, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(strides_none=True), E_NULL), (dict(out=A[0] + 2 * 64), E_ALIAS), (dict(saved=A[0]), E_ALIAS),
+    (dict(saved=A[6] + 8), E_ALIGN), (dict(edit={17: 64}), E_SHAPE), (dict(N=0), OK),
+])
+def test_fwd_train_strided_validation(lib, case, expect):
+    assert fwd_train_strided(lib, **case) == expect

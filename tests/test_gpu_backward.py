@@ -135,3 +135,42 @@ def test_backward_full_size_sampled_heads():
     sub = {k: g[k][:, heads].contiguous() for k in ("dq1", "dk1", "dq2", "dk2", "dv")}
     sub["dlambda"] = g["dlambda"][heads].contiguous()
     check_grads(sub, ref, "backward B4 H12 N4096 heads 0, 11")
+
+
+@pytest.mark.parametrize("causal,per_head", [(True, False), (False, True)])
+def test_strided_training_packed_projection(causal, per_head):
+    """q1 | k1 | q2 | k2 | v read as column slices of one packed projection [B][N][H][6][64], dy a token-major view,
+    out into a [B][N][H][128] buffer and the five gradients into the packed gradient buffer: out, saved, every
+    gradient and dlambda bit-identical to the dense entry points on contiguous copies."""
+    torch = torch_mod()
+    B, H, N, layer = 2, 3, 333, 2
+    say(f"case: strided training from a packed projection, B{B} H{H} N{N} causal={causal} per-head={per_head}")
+    inp = di.prefill_bf16(B, H, N, 64, seed=800)
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    dy = dev_bf16(di.output_grad_bf16(B, H, N, 64, seed=800))
+    lam = torch.tensor([0.3, 0.55, 0.7], device="cuda:0") if per_head else 0.6
+    proj = torch.empty((B, N, H, 6, 64), dtype=torch.bfloat16, device="cuda:0")
+    for i, k in enumerate(("q1", "k1", "q2", "k2")):
+        proj[:, :, :, i] = dev[k].permute(0, 2, 1, 3)
+    proj[:, :, :, 4:6] = dev["v"].permute(0, 2, 1, 3).reshape(B, N, H, 2, 64)
+    views = [proj[:, :, :, i].permute(0, 2, 1, 3) for i in range(4)]
+    vview = proj[:, :, :, 4:6].reshape(B, N, H, 128).permute(0, 2, 1, 3)
+    dy_tok = dy.permute(0, 2, 1, 3).contiguous()                       # [B][N][H][128]
+    dyview = dy_tok.permute(0, 2, 1, 3)
+    obuf = torch.zeros((B, N, H, 128), dtype=torch.bfloat16, device="cuda:0")
+    out, saved = da.diffattn_fwd_train_strided(views[0], views[1], views[2], views[3], vview, lam, layer, causal,
+                                               out=obuf.permute(0, 2, 1, 3))
+    gbuf = torch.zeros((B, N, H, 6, 64), dtype=torch.bfloat16, device="cuda:0")
+    grads = {k: gbuf[:, :, :, i].permute(0, 2, 1, 3) for i, k in enumerate(("dq1", "dk1", "dq2", "dk2"))}
+    grads["dv"] = gbuf[:, :, :, 4:6].reshape(B, N, H, 128).permute(0, 2, 1, 3)
+    grads["dlambda"] = torch.empty(H, dtype=torch.float32, device="cuda:0")
+    da.diffattn_bwd_strided(views[0], views[1], views[2], views[3], vview, dyview, saved, lam, layer, causal, grads)
+    ref_out, ref_saved = da.diffattn_fwd_train(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], lam, layer,
+                                               causal)
+    ref = da.diffattn_bwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], dy, ref_saved, lam, layer, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out.contiguous().view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(saved, ref_saved)
+    for k in ("dq1", "dk1", "dq2", "dk2", "dv"):
+        assert torch.equal(grads[k].contiguous().view(torch.int16), ref[k].view(torch.int16)), k
+    assert torch.equal(grads["dlambda"], ref["dlambda"])
