@@ -24,8 +24,9 @@
 //   * Two online softmaxes run side by side (running offset and sum per map, two O accumulators).  Probabilities
 //     are taken at the running offset first; only when a lane's 16 of them sum to more than 2^8 (a wave-uniform
 //     decision) is the row max taken and O rescaled, so neither the max nor the rescale is on the common path.
-//     Exponents use exp2 with log2(e)/sqrt(d) folded into one FMA; sums add the bf16-rounded probabilities
-//     pairwise with v_dot2_f32_bf16.  Map 2's exponentials are issued between map 1's value MFMAs.
+//     Exponents use exp2 with log2(e)/sqrt(d) folded into one FMA; the row sums add the probabilities in fp32 with
+//     plain VALU adds (v_dot2 would run on the matrix pipe and wait behind the MFMAs).  Map 2's exponentials are
+//     issued between map 1's value MFMAs.
 //   * Epilogue: O1/l1 - lambda O2/l2, RMS over the 128 channels (pair-reduced), scale, bf16 round-to-nearest-even.
 //   * Causal: row tiles are launched heaviest first; tiles wholly above a wave's rows are skipped by that wave,
 //     and only diagonal or ragged-tail tiles pay for masking.
@@ -78,8 +79,9 @@ struct MapState {
     float ms, ml, l;
 };
 
-// p = exp2(s * c - ml) for the lane's 16 keys, packed as P^T: two bf16x8 B operands.
-__device__ __forceinline__ void exp_pack(const f32x16& s, float ml, float c, bf16x8& lo, bf16x8& hi) {
+// p = exp2(s * c - ml) for the lane's 16 keys, packed as P^T: two bf16x8 B operands.  Returns the sum of the 16
+// probabilities in fp32.
+__device__ __forceinline__ float exp_pack(const f32x16& s, float ml, float c, bf16x8& lo, bf16x8& hi) {
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -ml));
@@ -91,21 +93,10 @@ __device__ __forceinline__ void exp_pack(const f32x16& s, float ml, float c, bf1
     }
     lo = __builtin_bit_cast(bf16x8, a);
     hi = __builtin_bit_cast(bf16x8, b);
-}
-
-// Sum of the lane's 16 packed probabilities: pairwise bf16 dot products with (1, 1), so the sum is of the same
-// bf16-rounded values that multiply V.
-__device__ __forceinline__ float sum_packed(const bf16x8& lo, const bf16x8& hi) {
-    const u32x4 a = __builtin_bit_cast(u32x4, lo), b = __builtin_bit_cast(u32x4, hi);
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    float t0 = 0.f, t1 = 0.f;
+    float t[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const unsigned ak = a[k], bk = b[k];   // scalar copies: bit_cast of a vector element misreads it
-        t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ak), one, t0, false);
-        t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, bk), one, t1, false);
-    }
-    return t0 + t1;
+    for (int k = 0; k < 8; ++k) t[k] = p[2 * k] + p[2 * k + 1];
+    return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
 }
 
 // Probabilities of one map for the lane's 16 scores of a tile, packed as P^T (lo, hi), and their sum.  They are
@@ -115,8 +106,7 @@ __device__ __forceinline__ float sum_packed(const bf16x8& lo, const bf16x8& hi) 
 // never needed.
 __device__ __forceinline__ float softmax_tile(const f32x16& s, MapState& st, f32x16 (&o)[4], float c, bf16x8& lo,
                                               bf16x8& hi) {
-    exp_pack(s, st.ml, c, lo, hi);
-    float part = sum_packed(lo, hi);
+    float part = exp_pack(s, st.ml, c, lo, hi);
     if (__any(__float_as_uint(part) > P_SUM_LIMIT_BITS)) {
         const float ms = fmaxf(st.ms, pair_max(max16(s)));
         const float ml = ms * c;
@@ -128,8 +118,7 @@ __device__ __forceinline__ float softmax_tile(const f32x16& s, MapState& st, f32
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
-        exp_pack(s, ml, c, lo, hi);
-        part = sum_packed(lo, hi);
+        part = exp_pack(s, ml, c, lo, hi);
     }
     return part;
 }
