@@ -399,16 +399,10 @@ __device__ __forceinline__ bf16x8 multi_softmax(const f32x4 (&s)[2], MultiMap& s
     u32x4 w;
 #pragma unroll
     for (int k = 0; k < 4; ++k) w[k] = pack_bf16(p[2 * k], p[2 * k + 1]);
-    const bf16x8 pk = __builtin_bit_cast(bf16x8, w);
-    // The sum is of the bf16-rounded probabilities that multiply V.
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    const unsigned w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
-    float t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), one, 0.f, false);
-    float t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), one, 0.f, false);
-    t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), one, t0, false);
-    t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), one, t1, false);
-    st.l += t0 + t1;
-    return pk;
+    // The sum is taken in fp32 with plain VALU adds: v_dot2 on the packed values would run on the matrix pipe,
+    // behind the value MFMAs.
+    st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    return __builtin_bit_cast(bf16x8, w);
 }
 
 template <bool PAGED>
