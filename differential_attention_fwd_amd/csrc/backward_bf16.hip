@@ -429,7 +429,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
                                                                          (int)(n1 * rbq1 + D * 2u), 0x00020000);
     const __amdgpu_buffer_rsrc_t rq2 = __builtin_amdgcn_make_buffer_rsrc((void*)(gq2 + gbase(G_Q2)), (short)0,
                                                                          (int)(n1 * rbq2 + D * 2u), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rdo = __builtin_amdgcn_make_buffer_rsrc((void*)(gdo + hv), (short)0, N * (DV * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rdo = __builtin_amdgcn_make_buffer_rsrc((void*)(gdo + hv), (short)0,
+                                                                         (int)((unsigned)N * (DV * 2u)), 0x00020000);
     const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc((void*)(stats + (size_t)bh * N * STAT_FLOATS),
                                                                          (short)0, N * (STAT_FLOATS * 4), 0x00020000);
 

@@ -29,6 +29,31 @@ bool mul_ok(int64_t a, int64_t b, int64_t* r) {
     return true;
 }
 
+// True when the strided [B][H][N][w] layout with element strides (sb, sh, sn) (feature stride 1) gives every element
+// its own address, proven by ordering the dimensions of extent > 1 by stride: each stride must be at least the
+// previous one times its extent (the first at least 1).  Outputs must pass: a layout that folds two elements onto one
+// address would have several workgroups write it at once.  (Some exotic one-to-one layouts fail the test too; they
+// are rejected rather than risked.)
+bool one_to_one(int64_t B, int64_t H, int64_t N, int64_t w, int64_t sb, int64_t sh, int64_t sn) {
+    int64_t st[4] = {1, sn, sh, sb}, ex[4] = {w, N, H, B};
+    int n = 0;
+    int64_t ds[4], de[4];
+    for (int k = 0; k < 4; ++k)
+        if (ex[k] > 1) { ds[n] = st[k]; de[n] = ex[k]; ++n; }
+    for (int i = 1; i < n; ++i)   // insertion sort by stride
+        for (int j = i; j > 0 && ds[j] < ds[j - 1]; --j) {
+            const int64_t a = ds[j], e = de[j];
+            ds[j] = ds[j - 1]; de[j] = de[j - 1];
+            ds[j - 1] = a; de[j - 1] = e;
+        }
+    int64_t need = 1;
+    for (int i = 0; i < n; ++i) {
+        if (ds[i] < need) return false;
+        if (!mul_ok(ds[i], de[i], &need)) return false;
+    }
+    return true;
+}
+
 int check_dtype_d(int dtype, int d) {
     if (dtype == DIFFATTN_BF16) return d == 64 ? DIFFATTN_OK : DIFFATTN_ERR_UNSUPPORTED;
     if (dtype == DIFFATTN_F32) return (d == 8 || d == 64) ? DIFFATTN_OK : DIFFATTN_ERR_UNSUPPORTED;
@@ -187,6 +212,8 @@ int diffattn_fwd_strided(const void* q1, const void* k1, const void* q2, const v
         }
         span[k] = Span{(uintptr_t)ptr[k], (uintptr_t)ptr[k] + (uintptr_t)last * 2};
     }
+    if (!one_to_one(B, H, N, 128, S.b[diffattn::S_OUT], S.h[diffattn::S_OUT], S.n[diffattn::S_OUT]))
+        return DIFFATTN_ERR_ALIAS;
     for (int k = 0; k < 5; ++k)
         if (overlaps(span[diffattn::S_OUT], span[k])) return DIFFATTN_ERR_ALIAS;
     if (lambda_heads) {
@@ -622,6 +649,8 @@ int diffattn_fwd_train_strided(const void* q1, const void* k1, const void* q2, c
         S.h[k] = strides[3 * k + 1];
         S.n[k] = strides[3 * k + 2];
     }
+    if (!one_to_one(B, H, N, 128, S.b[diffattn::S_OUT], S.h[diffattn::S_OUT], S.n[diffattn::S_OUT]))
+        return DIFFATTN_ERR_ALIAS;
     const Footprint sv = dense_footprint(saved, need);
     if (!disjoint(f[diffattn::S_OUT], sv)) return DIFFATTN_ERR_ALIAS;
     for (int k = 0; k < 5; ++k)
@@ -677,6 +706,8 @@ int diffattn_bwd_strided(const void* q1, const void* k1, const void* q2, const v
         G.h[k] = strides[3 * k + 1];
         G.n[k] = strides[3 * k + 2];
     }
+    for (int k = diffattn::G_DQ1; k <= diffattn::G_DV; ++k)
+        if (!one_to_one(B, H, N, k == diffattn::G_DV ? 128 : 64, G.b[k], G.h[k], G.n[k])) return DIFFATTN_ERR_ALIAS;
     // Inputs: q1, k1, q2, k2, v, dy and saved (may overlap one another).  Outputs: the five gradients, dlambda and
     // the workspace (must not overlap one another or any input).
     const Footprint ins[7] = {f[0], f[1], f[2], f[3], f[4], f[5],

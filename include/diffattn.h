@@ -123,7 +123,10 @@ int diffattn_decode_heads(const void *q1, const void *k1, const void *q2, const 
  *            (b, h, n, c) of tensor t is at base_t + b*strides[3t] + h*strides[3t+1] + n*strides[3t+2] + c.
  *   Every stride must be >= 0, a multiple of 8 (16-byte rows; else DIFFATTN_ERR_ALIGN), and a row stride at least
  *   the row width.  One head's K1, K2 and V rows, N + 256 of them, must span less than 4 GiB
- *   (else DIFFATTN_ERR_SHAPE).  Outputs must not overlap the inputs' address ranges (bounding boxes).
+ *   (else DIFFATTN_ERR_SHAPE).  Outputs must not overlap the inputs' address ranges (bounding boxes), and out's
+ *   strides must give every element its own address: ordered by stride, the dimensions of extent > 1 (the row of
+ *   2d elements first, stride 1) must each have a stride of at least the previous stride times the previous
+ *   extent; otherwise DIFFATTN_ERR_ALIAS (several workgroups would write one element).
  *   lambda / lambda_heads as for diffattn_fwd_train.  Contiguous strides give diffattn_fwd's result bit for bit.
  */
 int diffattn_fwd_strided(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
@@ -244,7 +247,9 @@ int diffattn_bwd(const void *q1, const void *k1, const void *q2, const void *k2,
  *   Aliasing: outputs (and, for the backward, the gradients, dlambda and the workspace among themselves) must not
  *   share a byte with each other or with any input.  Two strided tensors count as disjoint when their bounding boxes
  *   are, or when their rows fall in different residue classes modulo the gcd of all their byte strides (for example
- *   the column slices of one packed buffer); anything else that overlaps is DIFFATTN_ERR_ALIAS.
+ *   the column slices of one packed buffer); anything else that overlaps is DIFFATTN_ERR_ALIAS.  Each output (out,
+ *   and each gradient) must also give every one of its own elements a distinct address, by the rule stated for
+ *   diffattn_fwd_strided's out; otherwise DIFFATTN_ERR_ALIAS.
  */
 int diffattn_fwd_train_strided(const void *q1, const void *k1, const void *q2, const void *k2, const void *v,
                                void *out, int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda,

@@ -50,21 +50,28 @@ def pin_worked_example_printed(mutant=0):
 
 
 def pin_worked_example_library(mutant=0):
-    """[U] worked example evaluated with the library softmax it uses, in float64: map and output."""
+    """[U] worked example, map and output, from library routines in float64: both maps come from one batched
+    torch.softmax over the stacked [2][n][n] score tensor (scores scaled by 1/sqrt(d), d the query/key width), which
+    an explicit exp-and-normalise must reproduce; then w = map1 - lambda map2 and o = w V."""
     ex = di.worked_example()
-    q1, k1, q2, k2, v = (_t64(ex[k][0, 0]) for k in ("q1", "k1", "q2", "k2", "v"))
-    d, lam = ex["d"], ex["lambda"]
-    map1 = torch.softmax(q1 @ k1.T / d ** 0.5, dim=-1)
-    map2 = torch.softmax(q2 @ k2.T / d ** 0.5, dim=-1)
-    ref_w = (map1 - lam * map2).numpy()
-    ref_o = (map1 - lam * map2) @ v
-    out, diff = oracle.diffattn(ex["q1"], ex["k1"], ex["q2"], ex["k2"], ex["v"], lam, 0, False, want_diff=True,
-                                mutant=mutant)
+    q = np.stack([ex["q1"][0, 0], ex["q2"][0, 0]]).astype(np.float64)   # [map][n][d]
+    k = np.stack([ex["k1"][0, 0], ex["k2"][0, 0]]).astype(np.float64)
+    v = ex["v"][0, 0].astype(np.float64)
+    lam = float(ex["lambda"])
+    scores = np.einsum("mid,mjd->mij", q, k) / math.sqrt(ex["d"])
+    maps = torch.softmax(torch.from_numpy(scores), dim=-1).numpy()
+    e = np.exp(scores - scores.max(axis=-1, keepdims=True))
     fails = []
+    if np.abs(maps - e / e.sum(axis=-1, keepdims=True)).max() > 1e-15:
+        fails.append("library softmax disagrees with exp-and-normalise")
+    ref_w = maps[0] - lam * maps[1]
+    ref_o = ref_w @ v
+    out, diff = oracle.diffattn(ex["q1"], ex["k1"], ex["q2"], ex["k2"], ex["v"], ex["lambda"], 0, False,
+                                want_diff=True, mutant=mutant)
     if np.abs(diff[0, 0] - ref_w).max() > 1e-12:
         fails.append(f"map differs by {np.abs(diff[0, 0] - ref_w).max():.3g}")
-    if np.abs(out[0, 0] - ref_o.numpy()).max() > 1e-12:
-        fails.append(f"output differs by {np.abs(out[0, 0] - ref_o.numpy()).max():.3g}")
+    if np.abs(out[0, 0] - ref_o).max() > 1e-12:
+        fails.append(f"output differs by {np.abs(out[0, 0] - ref_o).max():.3g}")
     return fails
 
 

@@ -256,6 +256,10 @@ def _with(idx, val, B=1, H=2, N=64):
     (dict(strides=None), E_NULL), (dict(strides=_with(2, 68)), E_ALIGN), (dict(strides=_with(14, 64)), E_SHAPE),
     (dict(strides=_with(1, -8)), E_SHAPE), (dict(strides=_with(5, 1 << 26)), E_SHAPE), (dict(out=A[0]), E_ALIAS),
     (dict(dtype=F32), E_UNSUP), (dict(N=0), OK), (dict(strides=_with(11, 64 * 2 * 64 * 4096)), E_SHAPE),
+    # outputs that would write one element from several workgroups: the two heads' rows on the same addresses, or
+    # overlapping by half a row; both batch entries on the same addresses
+    (dict(strides=_with(16, 0)), E_ALIAS), (dict(strides=_with(16, 64)), E_ALIAS),
+    (dict(strides=_with(15, 0, B=2), B=2), E_ALIAS),
 ])
 def test_fwd_strided_validation(lib, case, expect):
     assert fwd_strided(lib, **case) == expect
@@ -384,6 +388,10 @@ def bwd_strided(lib, edit=None, ptr_edit=None, B=1, H=2, N=64, dtype=BF16, strid
     (dict(ptr_edit={7: G[0] + 64}), E_ALIAS),              # dk1 overlapping dq1 inside each packed row
     (dict(ptr_edit={10: G[0] + 2 * 320}), E_ALIAS),        # dv (128 wide) running into the next head's dq1
     (dict(ptr_edit={5: G[0] + 2 * 64}), E_ALIAS),          # dy read from where dk1 is written
+    (dict(edit={19: 0}), E_ALIAS),                         # dq1 of both heads on the same addresses
+    (dict(edit={31: 64}), E_ALIAS),                        # dv heads 64 elements apart, rows 128 wide
+    # dq1 alone in a buffer of its own, dense 64-element rows, but head 1 starting at head 0's row 32 (N = 64)
+    (dict(ptr_edit={6: 0x900000000}, edit={20: 64, 19: 32 * 64}), E_ALIAS),
     (dict(dtype=F32), E_UNSUP), (dict(B=0), OK),
 ])
 def test_bwd_strided_validation(lib, case, expect):
@@ -405,6 +413,7 @@ def fwd_train_strided(lib, strides_none=False, out=None, saved=A[6], edit=None, 
 @pytest.mark.parametrize("case,expect", [
     (dict(strides_none=True), E_NULL), (dict(out=A[0] + 2 * 64), E_ALIAS), (dict(saved=A[0]), E_ALIAS),
     (dict(saved=A[6] + 8), E_ALIGN), (dict(edit={17: 64}), E_SHAPE), (dict(N=0), OK),
+    (dict(edit={16: 0}), E_ALIAS), (dict(edit={16: 64}), E_ALIAS),   # out heads folded onto each other
 ])
 def test_fwd_train_strided_validation(lib, case, expect):
     assert fwd_train_strided(lib, **case) == expect

@@ -2,13 +2,15 @@
 
 The backward oracle is the chain rule of the forward definition in double precision, pinned by finite differences
 of the forward oracle (tests/test_oracle_bwd.py).  The GPU path computes in bf16 with fp32 accumulation: probabilities
-and ds are rounded to bf16 before the matrix products (relative error 2^-9 each), dO is rounded to bf16, and the
-gradients are stored as bf16 (2^-9).  Over the key or query sums these errors partly cancel, so each gradient tensor
-is checked relative to its own scale: max |got - ref| <= 2.5e-2 max |ref| and mean |got - ref| <= 4e-3 max |ref|;
-dlambda within 2e-2 of the largest head's |dlambda|: it is a sum over rows of terms of both signs, each
-carrying the forward's bf16-probability error (2^-9 relative) in o2, and the cancellation enlarges the relative
-error of the total.  The scale has an absolute floor of 1e-2: with a
-single key per row the exact dq is zero and the GPU returns rounding residue.
+and ds are rounded to bf16 before the matrix products (unit roundoff 2^-8 each), dO is rounded to bf16, and the
+gradients are stored as bf16 (2^-8).  Over the key or query sums these errors partly cancel, so each gradient tensor
+is checked block by block against its own scale, S = max |ref| over 64 rows of one (batch, head), floored at 1e-2
+(with a single key per row the exact dq is zero and the GPU returns rounding residue): |got - ref| <= 1.5e-2 S for
+every element and the block's mean |got - ref| <= 2e-3 S.  dlambda is within 1.5e-2 of the largest head's |dlambda|:
+it is a sum over rows of terms of both signs, each carrying the forward's bf16-probability error (2^-8 relative) in
+o2, and the cancellation enlarges the relative error of the total.  Observed over these cases: element 1.17e-2 S
+(dk1 of the full-size workload), block mean 1.58e-3 S (dq1 of a head with lambda 0.9), dlambda 8.7e-3; the bounds
+leave a margin of about 1.3x on each.
 """
 import numpy as np
 import pytest
@@ -19,8 +21,9 @@ import oracle
 
 pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("gpu")]
 
-REL_MAX, REL_MEAN, REL_DLAMBDA = 2.5e-2, 4e-3, 2e-2
-SCALE_FLOOR = 1e-2   # absolute floor of a gradient's scale (one key per row makes dq exactly zero)
+REL_MAX, REL_MEAN, REL_DLAMBDA = 1.5e-2, 2e-3, 1.5e-2
+ROW_BLOCK = 64       # rows per scale block
+SCALE_FLOOR = 1e-2   # absolute floor of a block's scale (one key per row makes dq exactly zero)
 
 
 def torch_mod():
@@ -60,20 +63,38 @@ def run_case(B, H, N, causal, layer, lam, seed):
     return out, g, ref, dev
 
 
+def block_scale(r, rows=ROW_BLOCK):
+    """Per (batch, head, block of `rows` rows) scale of a [B][H][N][w] gradient: max |ref| over the block, floored."""
+    B, H, N, w = r.shape
+    nb = -(-N // rows)
+    pad = np.zeros((B, H, nb * rows, w))
+    pad[:, :, :N] = np.abs(r)
+    s = pad.reshape(B, H, nb, rows * w).max(axis=-1)
+    return np.maximum(s, SCALE_FLOOR)
+
+
 def check_grads(g, ref, what):
     for k in ("dq1", "dk1", "dq2", "dk2", "dv"):
         got = host(g[k])
         r = ref[k]
-        scale = max(np.abs(r).max(), SCALE_FLOOR)
+        B, H, N, w = r.shape
+        sc = block_scale(r)                                      # [B][H][blocks]
         err = np.abs(got - r)
-        say(f"{what} {k}: max-abs {err.max():.3e} mean-abs {err.mean():.3e} (scale {scale:.3e}, "
-            f"rel max {err.max() / scale:.2e}, rel mean {err.mean() / scale:.2e})")
+        rel = err / np.repeat(sc, ROW_BLOCK, axis=2)[:, :, :N, None]
+        nb = sc.shape[2]
+        pad = np.zeros((B, H, nb * ROW_BLOCK, w))
+        pad[:, :, :N] = rel
+        # mean over each block's real rows only
+        cnt = np.minimum(ROW_BLOCK, N - ROW_BLOCK * np.arange(nb)) * w
+        rel_mean = pad.reshape(B, H, nb, ROW_BLOCK * w).sum(axis=-1) / cnt
+        say(f"{what} {k}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}; per {ROW_BLOCK}-row block relative "
+            f"max {rel.max():.2e} (bound {REL_MAX:.1e}), worst block mean {rel_mean.max():.2e} (bound {REL_MEAN:.1e})")
         assert np.isfinite(got).all(), k
-        assert err.max() <= REL_MAX * scale, f"{what} {k}: max-abs {err.max():.3e} vs scale {scale:.3e}"
-        assert err.mean() <= REL_MEAN * scale, f"{what} {k}: mean-abs {err.mean():.3e} vs scale {scale:.3e}"
+        assert rel.max() <= REL_MAX, f"{what} {k}: relative max {rel.max():.3e}"
+        assert rel_mean.max() <= REL_MEAN, f"{what} {k}: relative block mean {rel_mean.max():.3e}"
     dl = g["dlambda"].cpu().numpy().astype(np.float64)
     rel = np.abs(dl - ref["dlambda"]).max() / max(np.abs(ref["dlambda"]).max(), 1e-30)
-    say(f"{what} dlambda: got {dl} ref {ref['dlambda']} rel {rel:.2e}")
+    say(f"{what} dlambda: got {dl} ref {ref['dlambda']} rel {rel:.2e} (bound {REL_DLAMBDA:.1e})")
     assert rel <= REL_DLAMBDA
 
 
