@@ -23,7 +23,7 @@ EXPORTS = ["diffattn_fwd", "diffattn_fwd_heads", "diffattn_fwd_strided", "diffat
            "diffattn_decode_paged_workspace_bytes", "diffattn_decode_paged", "diffattn_decode_strided",
            "diffattn_train_saved_bytes", "diffattn_fwd_train", "diffattn_fwd_train_strided",
            "diffattn_bwd_workspace_bytes", "diffattn_bwd", "diffattn_bwd_strided", "diffattn_lambda_init",
-           "diffattn_status_str",
+           "diffattn_decode_noalloc", "diffattn_status_str",
            "diffattn_abi_version"]
 
 _lib = None
@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
     L.diffattn_decode.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, c_int, c_int, P,
                                   ctypes.c_size_t, P]
     L.diffattn_decode.restype = c_int
+    L.diffattn_decode_noalloc.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, c_int, c_int, P]
+    L.diffattn_decode_noalloc.restype = c_int
     L.diffattn_fwd_heads.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, P, c_int, c_int, P]
     L.diffattn_fwd_heads.restype = c_int
     L.diffattn_decode_heads.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, P, c_int, c_int, P,
@@ -205,6 +207,30 @@ def diffattn_decode(q1, k1, q2, k2, v, lam, layer: int, causal: bool = True, out
         st, name = lib().diffattn_decode_heads(*args, lh.data_ptr(), *tail), "diffattn_decode_heads"
     if st != 0:
         raise DiffAttnError(st, name)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # DIFFATTN_NOALLOC_SCRATCH_BYTES
+
+
+def diffattn_decode_noalloc(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool = True, out=None, stream=None):
+    """Decode as diffattn_decode, with the split partials in the library's per-GPU scratch array: the call allocates
+    nothing (pass `out` to keep the whole call allocation-free).  Calls that may overlap on one GPU race."""
+    import torch
+    _check_tensors((q1, k1, q2, k2, v))
+    B, H, d = q1.shape
+    L = k1.shape[2]
+    if out is None:
+        out = torch.empty((B, H, 2 * d), dtype=q1.dtype, device=q1.device)
+    for t, shp in ((q2, (B, H, d)), (k1, (B, H, L, d)), (k2, (B, H, L, d)), (v, (B, H, L, 2 * d)),
+                   (out, (B, H, 2 * d))):
+        if tuple(t.shape) != tuple(shp) or t.dtype != q1.dtype:
+            raise ValueError(f"shape/dtype mismatch: {tuple(t.shape)} {t.dtype}, expected {tuple(shp)} {q1.dtype}")
+    st = lib().diffattn_decode_noalloc(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
+                                       out.data_ptr(), B, H, L, d, _dtype_code(q1), float(lam), int(layer),
+                                       int(bool(causal)), _stream_handle(stream, q1.device))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_decode_noalloc")
     return out
 
 

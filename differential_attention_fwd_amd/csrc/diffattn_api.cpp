@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.h"
 
 namespace {
@@ -332,6 +334,45 @@ int decode_impl(const void* q1, const void* k1, const void* q2, const void* k2, 
 }  // namespace
 
 extern "C" {
+
+// Scratch of the allocation-free decode: one array per GPU, held from the library's load until the process ends.
+// In host code `scratch` is a host-side stand-in, not a device address: the device address of each GPU's copy is
+// looked up once per device, with that device current, and only that address is ever passed to a kernel.
+namespace {
+__device__ __attribute__((aligned(256))) unsigned char scratch[DIFFATTN_NOALLOC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+std::once_flag scratch_once[MAX_DEVICES];
+void* scratch_ptr[MAX_DEVICES];
+hipError_t scratch_err[MAX_DEVICES];
+
+// Device address of the current device's scratch array (DIFFATTN_ERR_HIP if it cannot be found).
+int scratch_of_current_device(void** p) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return DIFFATTN_ERR_HIP;
+    std::call_once(scratch_once[dev], [dev] {
+        scratch_err[dev] = hipGetSymbolAddress(&scratch_ptr[dev], HIP_SYMBOL(scratch));
+    });
+    if (scratch_err[dev] != hipSuccess || !scratch_ptr[dev]) return DIFFATTN_ERR_HIP;
+    *p = scratch_ptr[dev];
+    return DIFFATTN_OK;
+}
+}  // namespace
+
+int diffattn_decode_noalloc(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
+                            int64_t B, int64_t H, int64_t L, int d, int dtype, float lambda, int layer, int causal,
+                            void* stream) {
+    (void)causal;
+    // Size check first, before any HIP call; invalid shapes (need 0) are reported by decode_impl.
+    const size_t need = dtype == DIFFATTN_BF16 ? diffattn_decode_workspace_bytes(B, H, L, d) : 0;
+    if (need > DIFFATTN_NOALLOC_SCRATCH_BYTES) return DIFFATTN_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        const int st = scratch_of_current_device(&ws);
+        if (st) return st;
+    }
+    return decode_impl(q1, k1, q2, k2, v, out, B, H, 1, L, nullptr, false, d, dtype, lambda, nullptr, false, layer, ws,
+                       ws ? (size_t)DIFFATTN_NOALLOC_SCRATCH_BYTES : 0, stream);
+}
 
 int diffattn_decode(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
                     int64_t B, int64_t H, int64_t L, int d, int dtype, float lambda, int layer, int causal,

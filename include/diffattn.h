@@ -261,6 +261,24 @@ int diffattn_bwd_strided(const void *q1, const void *k1, const void *q2, const v
                          const float *lambda_heads, int layer, int causal, const int64_t *strides, void *workspace,
                          size_t workspace_bytes, void *stream);
 
+/*
+ * Decode without allocation, for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): diffattn_decode with the split partials kept in a scratch array
+ * that the library holds in each GPU's memory (DIFFATTN_NOALLOC_SCRATCH_BYTES, from the first call on that GPU
+ * until the process ends) instead of a caller workspace.  The call itself allocates nothing.
+ *   Arguments, layouts, results and errors as for diffattn_decode; the call must need at most
+ *   DIFFATTN_NOALLOC_SCRATCH_BYTES of partials (diffattn_decode_workspace_bytes(B, H, L, d); for example B = 64,
+ *   H = 16 up to L = 15360), else DIFFATTN_ERR_WORKSPACE before any HIP call.  The partials are fully rewritten by
+ *   every call (no state is carried between calls).  All calls on one GPU share its array: calls that may overlap
+ *   in time on one GPU (different streams, or threads) race and must be serialised by the caller.  Results are bit
+ *   for bit those of diffattn_decode.  The first call on a GPU, with that GPU current, looks up the array's device
+ *   address (DIFFATTN_ERR_HIP if that fails).
+ */
+#define DIFFATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int diffattn_decode_noalloc(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
+                            int64_t B, int64_t H, int64_t L, int d, int dtype, float lambda, int layer, int causal,
+                            void *stream);
+
 /* lambda_init(layer) = 0.8 - 0.6 exp(-0.3 (layer - 1)) in double, for layer >= 1 ([U]); NaN for layer < 1. */
 double diffattn_lambda_init(int layer);
 

@@ -417,3 +417,16 @@ def fwd_train_strided(lib, strides_none=False, out=None, saved=A[6], edit=None, 
 ])
 def test_fwd_train_strided_validation(lib, case, expect):
     assert fwd_train_strided(lib, **case) == expect
+
+
+def test_decode_noalloc_rejects_oversized_partials(lib):
+    """Partials beyond the library's scratch array are DIFFATTN_ERR_WORKSPACE before any HIP call; shape errors are
+    reported as for diffattn_decode."""
+    B, H, L = 64, 16, 16384
+    assert lib.diffattn_decode_workspace_bytes(B, H, L, 64) > da.NOALLOC_SCRATCH_BYTES
+    assert lib.diffattn_decode_noalloc(A[0], A[1], A[2], A[3], A[4], A[5], B, H, L, 64, BF16, 0.8, 1, 1,
+                                       None) == E_WS
+    assert lib.diffattn_decode_noalloc(A[0], A[1], A[2], A[3], A[4], A[5], 1, 1, 0, 64, BF16, 0.8, 1, 1,
+                                       None) == E_SHAPE
+    assert lib.diffattn_decode_noalloc(A[0], A[1], A[2], A[3], A[4], A[5], 1, 1, 64, 32, BF16, 0.8, 1, 1,
+                                       None) == E_UNSUP
