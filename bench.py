@@ -14,9 +14,18 @@ events recorded on the stream it is launched on.  Prints ONE JSON line.
   decode_paged  (not part of the step) the decode workload read from 64-row pages of a shuffled page pool through
             a block table: GB/s of the same bytes as decode
   backward  (not part of the step) the training forward and the backward pass on the prefill workload with a
-            synthetic output gradient, timed separately: 1792 FLOP per unmasked pair on the matrix cores (the
-            dQ kernel recomputes both score maps and dP: 768; the dK/dV kernel recomputes them and forms dV, dK1,
-            dK2: 1024)
+            synthetic output gradient, timed separately.  Its roofline counts 1280 FLOP per unmasked pair: the two
+            score maps and dP once (768) and dV, dQ1, dQ2, dK1, dK2 (512), the least an exact streaming backward
+            does; tflops_exec counts the 1792 the kernels execute (the dQ kernel recomputes both score maps and dP and
+            forms dQ1, dQ2: 768; the dK/dV kernel recomputes them and forms dV, dK1, dK2: 1024)
+  prefill_n65536  (not part of the step) the causal prefill at B1 H16 N65536 (layer 24): TFLOP/s with its roofline, and
+            the oracle's time on 256 sampled rows with the full-problem time extrapolated from them (labelled so)
+  clock     the GPU clock and socket power the box reports (amdsmi GPU metrics) while the prefill runs back to back
+            for about two seconds, and the prefill rate over that window
+  context   the same box's bf16 GEMM rate (torch.matmul 8192^3, random data) and streaming-read rate (a sum over a
+            4 GiB tensor): what library kernels reach here, next to the nominal peaks
+Each timed kernel reports the median over its repetitions (the headline value uses the median), with the mean and
+the minimum beside it.
 Every roofline's "traffic" is the HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
 (profiles/hbm_traffic.txt), used only while the kernel source still matches the hash recorded there, else null.
 """
@@ -87,7 +96,7 @@ def read_traffic(kernel):
         return None
 
 
-def cpu_baseline(inp_bits, lam, layer, N, target_rows):
+def cpu_baseline(inp_bits, lam, layer, N, target_rows, threads=None):
     """Time the oracle on every k-th query row of the prefill workload (uniform over the causal row costs)."""
     import numpy as np
 
@@ -100,7 +109,7 @@ def cpu_baseline(inp_bits, lam, layer, N, target_rows):
     stride = max(1, total // target_rows)
     rows = np.arange(0, total, stride, dtype=np.int64)
     pairs = int(((rows % N) + 1).sum())
-    threads = oracle.max_threads()
+    threads = threads or oracle.max_threads()
     oracle.diffattn(f["q1"][:1, :1, :8], f["k1"][:1, :1, :8], f["q2"][:1, :1, :8], f["k2"][:1, :1, :8],
                     f["v"][:1, :1, :8], lam, layer, True)  # load the library outside the timed region
     t0 = time.perf_counter()
@@ -137,17 +146,12 @@ def bench_decode_multi(da, stream, k1, k2, v, Dc, steps, T=4):
     for _ in range(3):
         run()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    st = med_stats(time_on_stream(run, stream, steps))
+    ms = st["ms"]
     nbytes = int(lens_np.sum()) * H * (2 * d * 2 + 2 * d * 2) + 2 * (2 * B * H * T * d + B * H * T * 2 * d)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": f"decode B{B} H{H} T{T} new tokens, cache lengths {int(lens_np.min())}..{int(lens_np.max())} "
-                        f"(seeded uniform in [{L // 2}, {L}]), d64 dv128", "steps": steps, "ms": round(ms, 4),
+                        f"(seeded uniform in [{L // 2}, {L}]), d64 dv128", "steps": steps, **st,
             "bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": read_traffic("decode_multi")}}
@@ -186,17 +190,12 @@ def bench_decode_paged(da, stream, q1, k1, q2, k2, v, Dc, steps, ref_out, nbytes
     torch.cuda.synchronize()
     if not torch.equal(out[:, :, 0].view(torch.int16), ref_out.view(torch.int16)):
         raise RuntimeError("paged decode differs from the contiguous decode on the same rows")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    st = med_stats(time_on_stream(run, stream, steps))
+    ms = st["ms"]
     gbs = nbytes / (ms * 1e-3) / 1e9
     del k1p, k2p, vp
     return {"workload": f"decode B{B} H{H} L{L} d64 dv128 in {P}-row pages (shuffled pool, block table)",
-            "steps": steps, "ms": round(ms, 4), "bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s",
+            "steps": steps, **st, "bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": read_traffic("decode_paged")}}
 
@@ -234,16 +233,162 @@ def bench_backward(da, di, stream, p_bits, q1, k1, q2, k2, v, lam, steps):
         bwd()
         ev[k][2].record(stream)
     torch.cuda.synchronize()
-    f_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    b_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    fst = med_stats([e[0].elapsed_time(e[1]) for e in ev])
+    bst = med_stats([e[1].elapsed_time(e[2]) for e in ev])
+    b_ms = bst["ms"]
     pairs = prefill_pairs(P["B"], P["H"], P["N"])
     flops = pairs * 1792
+    flops_min = pairs * 1280
     tf = flops / (b_ms * 1e-3) / 1e12
+    tf_min = flops_min / (b_ms * 1e-3) / 1e12
     return {"workload": "causal B4 H12 N4096 d64 dv128, layer 12, synthetic N(0,1) output gradient",
-            "steps": steps, "fwd_train_ms": round(f_ms, 4), "ms": round(b_ms, 4), "flops_exec": flops,
-            "tflops_exec": round(tf, 2),
+            "steps": steps, "fwd_train_ms": fst["ms"], "fwd_train_ms_min": fst["ms_min"], **bst,
+            "flops_exec": flops, "tflops_exec": round(tf, 2),
+            "flops_one_recompute": flops_min, "tflops_one_recompute": round(tf_min, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf_min, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                         "unit": "TFLOP/s", "frac": round(tf_min / PEAK_BF16_TFLOPS, 4),
+                         "flop_count": "1280 per unmasked pair (scores, dP and the five gradient products once)",
+                         "traffic": read_traffic("backward")}}
+
+def med_stats(ms):
+    """Median (the reported time), mean and minimum of a list of per-repetition times in ms."""
+    import statistics
+    return {"ms": round(statistics.median(ms), 4), "ms_mean": round(sum(ms) / len(ms), 4), "ms_min": round(min(ms), 4)}
+
+
+def time_on_stream(fn, stream, reps):
+    """Per-repetition times (ms) of fn() from HIP events recorded on `stream`."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def sample_clock(fn, stream, seconds=2.0, period=0.02):
+    """Run fn() back to back for about `seconds` while a thread samples the GPU metrics (current graphics clock,
+    socket power); the firmware refreshes them a few times per second, so only the samples of the second half of
+    the window are summarised.  Returns None when the metrics cannot be read."""
+    import statistics
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
+        amdsmi.amdsmi_get_gpu_metrics_info(h)
+    except Exception as e:   # no metrics on this box: say so rather than guess
+        return {"error": f"{type(e).__name__}: {e}"}
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                samples.append((time.perf_counter(), m.get("current_gfxclk"), m.get("current_socket_power")))
+            except Exception:
+                pass
+            time.sleep(period)
+
+    # one launch's duration, to size the window
+    one = statistics.median(time_on_stream(fn, stream, 5))
+    reps = max(10, int(seconds * 1e3 / max(one, 1e-3)))
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    ms = time_on_stream(fn, stream, reps)
+    t1 = time.perf_counter()
+    stop.set()
+    th.join()
+    late = [(c, p) for (t, c, p) in samples if t >= t0 + 0.5 * (t1 - t0) and isinstance(c, (int, float))]
+    out = {"reps": reps, "window_s": round(t1 - t0, 3), "ms_median_in_window": round(statistics.median(ms), 4),
+           "source": "amdsmi GPU metrics (current_gfxclk, current_socket_power), second half of the window"}
+    if late:
+        out["gfxclk_mhz_median"] = statistics.median(c for c, _ in late)
+        out["gfxclk_mhz_min"] = min(c for c, _ in late)
+        pw = [p for _, p in late if isinstance(p, (int, float))]
+        if pw:
+            out["socket_power_w_median"] = statistics.median(pw)
+        out["samples"] = len(late)
+    return out
+
+
+def context_rates(dev, stream):
+    """Library kernels on the same box: bf16 GEMM (torch.matmul, 8192^3, N(0,1) data) and a streaming read (sum of a
+    4 GiB bf16 tensor)."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(11)
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16, generator=g)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            a @ b
+        ms_g = time_on_stream(lambda: a @ b, stream, 20)
+    del a, b
+    x = torch.ones(1 << 31, device=dev, dtype=torch.bfloat16)   # 4 GiB
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            x.sum(dtype=torch.float32)
+        ms_r = time_on_stream(lambda: x.sum(dtype=torch.float32), stream, 10)
+    del x
+    import statistics
+    tg, tr = statistics.median(ms_g), statistics.median(ms_r)
+    return {"gemm_bf16_8192_tflops": round(2 * 8192 ** 3 / (tg * 1e-3) / 1e12, 1),
+            "gemm_bf16_8192_frac_of_peak": round(2 * 8192 ** 3 / (tg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "stream_read_gbs": round((1 << 32) / (tr * 1e-3) / 1e9, 1),
+            "stream_read_frac_of_peak": round((1 << 32) / (tr * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def bench_prefill_n65536(da, di, stream, dev, steps, oracle_rows=256):
+    """The causal prefill at B1 H16 N65536 (layer 24), timed on the launch stream, and the oracle on 256 sampled
+    rows (rows 0, 1, 63, 64, 127, 128, 4095, 4096, N - 1 of the first and last head, the rest seeded uniform), with
+    the full-problem time extrapolated from those rows' unmasked pairs."""
+    import numpy as np
+    import torch
+    import oracle
+    c = di.CONFIGS["prefill_n65536"]
+    B, H, N, d, layer = c["B"], c["H"], c["N"], c["d"], c["layer"]
+    bits = di.prefill_bf16(B, H, N, d, c["seed"])
+    lam = float(np.float32(da.diffattn_lambda_init(layer)))
+    t = {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev) for k, v in bits.items()}
+    out = torch.empty_like(t["v"])
+    torch.cuda.synchronize()
+
+    def run():
+        da.diffattn_fwd(t["q1"], t["k1"], t["q2"], t["k2"], t["v"], lam, layer, True, out=out, stream=stream)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    ms = time_on_stream(run, stream, steps)
+    st = med_stats(ms)
+    pairs = prefill_pairs(B, H, N)
+    flops = pairs * 12 * d
+    tf = flops / (st["ms"] * 1e-3) / 1e12
+    del t, out
+    fixed = [(h, i) for h in (0, H - 1) for i in (0, 1, 63, 64, 127, 128, 4095, 4096, N - 1)]
+    rng = np.random.default_rng(4)
+    sel = fixed + [(int(rng.integers(H)), int(rng.integers(N))) for _ in range(oracle_rows - len(fixed))]
+    rows = np.array([h * N + i for h, i in sel], dtype=np.int64)
+    sampled_pairs = int(((rows % N) + 1).sum())
+    f = {k: di.bf16_bits_to_f32(v) for k, v in bits.items()}
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam, layer, True, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"workload": f"causal prefill B{B} H{H} N{N} d64 dv128, layer {layer}", "steps": steps, **st,
+            "flops_exec": flops, "tflops_exec": round(tf, 2),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
-                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic("backward")}}
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+            "cpu_oracle": {"rows": int(rows.size), "unmasked_pairs": sampled_pairs, "seconds": round(dt, 3),
+                           "threads": threads,
+                           "extrapolated_full_seconds": round(dt * pairs / sampled_pairs, 1),
+                           "note": "full-problem time extrapolated from the sampled rows' unmasked pairs"}}
 
 
 def main():
@@ -259,6 +404,11 @@ def main():
                     help="timed multi-token decode repetitions (0 skips that leg)")
     ap.add_argument("--paged-steps", type=int, default=10,
                     help="timed paged decode repetitions (0 skips that leg)")
+    ap.add_argument("--n65536-steps", type=int, default=10,
+                    help="timed repetitions of the B1 H16 N65536 prefill leg (0 skips it)")
+    ap.add_argument("--clock-seconds", type=float, default=2.0,
+                    help="length of the back-to-back prefill window sampled for clock and power (0 skips it)")
+    ap.add_argument("--no-context", action="store_true", help="skip the library GEMM / streaming-read context leg")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -339,11 +489,11 @@ def main():
     pairs = prefill_pairs(P["B"], P["H"], P["N"])
     f_exec = pairs * 12 * P["d"]
     f_formula = pairs * 8 * P["d"]
-    pre_avg = sum(pre_ms) / K
-    pre_tflops = f_exec / (pre_avg * 1e-3) / 1e12
+    pst = med_stats(pre_ms)
+    pre_tflops = f_exec / (pst["ms"] * 1e-3) / 1e12
     dbytes = decode_bytes(Dc["B"], Dc["H"], Dc["L"], Dc["d"])
-    dec_avg = sum(dec_ms) / K
-    dec_gbs = dbytes / (dec_avg * 1e-3) / 1e9
+    dst = med_stats(dec_ms)
+    dec_gbs = dbytes / (dst["ms"] * 1e-3) / 1e9
 
     pre_traffic = read_traffic("prefill")
     dec_traffic = read_traffic("decode")
@@ -372,15 +522,17 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": pre_traffic},
-        "prefill": {"ms": round(pre_avg, 4), "ms_min": round(min(pre_ms), 4), "flops_exec": f_exec,
-                    "flops_formula": f_formula,
-                    "tflops_formula": round(f_formula / (pre_avg * 1e-3) / 1e12, 2)},
-        "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "ms": round(dec_avg, 4), "ms_min": round(min(dec_ms), 4),
-                   "bytes": dbytes,
+        "prefill": {**pst, "flops_exec": f_exec, "flops_formula": f_formula,
+                    "tflops_formula": round(f_formula / (pst["ms"] * 1e-3) / 1e12, 2)},
+        "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", **dst, "bytes": dbytes,
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": dec_traffic}},
         "wall_s": round(wall, 3),
     }
+    if args.clock_seconds > 0:
+        result["clock"] = sample_clock(prefill, stream, args.clock_seconds)
+    if not args.no_context:
+        result["context"] = context_rates(dev, stream)
     if args.multi_steps > 0:
         result["decode_multi"] = bench_decode_multi(da, stream, dk1, dk2, dv, Dc, args.multi_steps)
     if args.paged_steps > 0:
@@ -388,8 +540,15 @@ def main():
                                                     dbytes)
     if args.bwd_steps > 0:
         result["backward"] = bench_backward(da, di, stream, p_bits, pq1, pk1, pq2, pk2, pv, p_lam, args.bwd_steps)
+    if args.n65536_steps > 0:
+        del dq1, dk1, dq2, dk2, dv, ws
+        torch.cuda.empty_cache()
+        result["prefill_n65536"] = bench_prefill_n65536(da, di, stream, dev, args.n65536_steps)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(p_bits, p_lam, P["layer"], P["N"], args.cpu_rows)
+        cb = cpu_baseline(p_bits, p_lam, P["layer"], P["N"], args.cpu_rows)
+        one = cpu_baseline(p_bits, p_lam, P["layer"], P["N"], max(1, args.cpu_rows // 16), threads=1)
+        cb["single_core"] = {k: one[k] for k in ("value", "unit", "cores", "sample", "seconds")}
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
 

@@ -68,3 +68,20 @@ def test_more_than_one_gpu_is_refused(argv, env):
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_median_statistics():
+    # The reported time is the median (robust to the first, slower repetitions); mean and minimum ride along.
+    st = bench.med_stats([0.5, 0.3, 0.31, 0.29, 0.3])
+    assert st == {"ms": 0.3, "ms_mean": 0.34, "ms_min": 0.29}
+    assert bench.med_stats([2.0, 1.0]) ["ms"] == 1.5
+
+
+def test_backward_flop_counts():
+    # 1280 per unmasked pair: S1, S2 (2 x 2d) and dP (2 x 2d'... one dot over the 2d value channels) once, plus dV
+    # (2 x 2d) and dQ1, dQ2, dK1, dK2 (4 x 2d), d = 64, 2d' = 128: 256 + 256 + 256 + 512.
+    d = 64
+    assert 2 * (2 * d) + 2 * (2 * d) + 2 * (2 * d) + 4 * (2 * d) == 1280
+    # executed: the dQ kernel recomputes S1, S2, dP (512) and forms dQ1, dQ2 (256); dK/dV recomputes them (512)
+    # and forms dV, dK1, dK2 (512)
+    assert (512 + 256) + (512 + 512) == 1792
