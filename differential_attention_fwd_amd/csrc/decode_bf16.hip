@@ -34,9 +34,12 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int D = 64;
 constexpr int DV = 128;
 constexpr int THREADS = 256;
-constexpr int MAX_SPLIT_KEYS = 1024;          // keys per split (scores of both maps fit in 8 KiB of LDS)
-constexpr int PT_MAX = 128;                   // page-table entries staged per split
+constexpr int MAX_SPLIT_KEYS = 1024;          // one token: keys per split (scores of both maps fit in 8 KiB of LDS)
+constexpr int MULTI_MAX_SPLIT_KEYS = 8192;    // several tokens: keys per split (the kernel keeps no per-key state)
+constexpr int PT_MAX = 128;                   // page-table entries staged per split (one token)
+constexpr int MULTI_PT_MAX = 520;             // the same for several tokens
 static_assert(MAX_SPLIT_KEYS / 16 + 2 <= PT_MAX, "a split spans at most keys / 16 + 2 pages of the smallest size");
+static_assert(MULTI_MAX_SPLIT_KEYS / 16 + 2 <= MULTI_PT_MAX, "a split spans at most keys / 16 + 2 pages");
 constexpr int PART_FLOATS = 4 + 2 * DV;       // m1, l1, m2, l2, O1[128], O2[128]
 constexpr int MAX_T = 16;                     // new tokens per sequence in multi-token decode
 constexpr float LOG2E = 1.4426950408889634f;
@@ -72,10 +75,10 @@ struct SplitPlan {
     int split_keys;  // keys per split (the last split may be shorter)
 };
 
-__host__ __device__ inline SplitPlan plan_splits(int64_t BH, int64_t L) {
-    // At least ceil(L / MAX_SPLIT_KEYS) splits; more for few heads so that the grid has >= ~2048 workgroups,
+__host__ __device__ inline SplitPlan plan_splits(int64_t BH, int64_t L, int64_t max_keys) {
+    // At least ceil(L / max_keys) splits; more for few heads so that the grid has >= ~2048 workgroups,
     // but never below 64 keys per split.
-    int64_t s = (L + MAX_SPLIT_KEYS - 1) / MAX_SPLIT_KEYS;
+    int64_t s = (L + max_keys - 1) / max_keys;
     const int64_t want = (2048 + BH - 1) / (BH > 0 ? BH : 1);
     const int64_t cap = (L + 63) / 64;
     if (s < want) s = want < cap ? want : cap;
@@ -89,13 +92,13 @@ __host__ __device__ inline SplitPlan plan_splits(int64_t BH, int64_t L) {
 // into ptab (clamped to the pool; positions past the table repeat its last entry), so that a row's page is an LDS
 // read rather than a dependent global load.  Returns the first staged page.  The caller makes the writes visible
 // (a barrier, or the same wave's later reads).
-template <bool PAGED>
+template <bool PAGED, int ENTRIES>
 __device__ __forceinline__ int stage_pages(const DecodePages& pg, int b, int j0, int* ptab, int tid, int nthreads) {
     if constexpr (!PAGED) {
         return 0;
     } else {
         const int pg0 = j0 >> pg.log2_page;
-        for (int i = tid; i < PT_MAX; i += nthreads) {
+        for (int i = tid; i < ENTRIES; i += nthreads) {
             const int idx = min(pg0 + i, pg.max_pages - 1);
             ptab[i] = min(max(pg.table[(size_t)b * pg.max_pages + idx], 0), pg.num_pages - 1);
         }
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     }
     const float c = LOG2E * 0.125f;  // log2(e) / sqrt(64)
     const int hh = bh % H, bb = bh / H;
-    const int pg0 = stage_pages<PAGED>(pg, bb, j0, ptab, tid, THREADS);
+    const int pg0 = stage_pages<PAGED, PT_MAX>(pg, bb, j0, ptab, tid, THREADS);
     if constexpr (PAGED) __syncthreads();
 
     // Phase 1: scores.  Lane handles 16-byte chunk (lane % 8) of row (lane / 8) of an 8-row group; the workgroup
@@ -297,36 +300,30 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
     *(unsigned*)(gout + (size_t)item * DV + 2 * lane) = w;
 }
 
-// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-constexpr int waitcnt_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }   // vm only
-constexpr int waitcnt_lgkm0() { return 15 | (7 << 4) | (0 << 8) | (3 << 14); }                       // lgkm only
-template <int V> struct Slot2 { static constexpr int value = V; };
+template <bool V> struct Flag { static constexpr bool value = V; };
 
 // Multi-token split on the matrix cores: one wave per (head, key split), all T <= 16 queries of the head as the 16
 // columns of v_mfma_f32_16x16x32_bf16 tiles (A 16 x 32: lane holds A[m = l % 16][k = 8 (l / 16) + j]; B 32 x 16:
 // lane holds B[k = 8 (l / 16) + j][n = l % 16]; D 16 x 16: lane holds D[m = 4 (l / 16) + i][n = l % 16]).
-//   * Scores S^T = K Q^T per 32-key tile: A = K rows from LDS, B = the queries.  Lane l then holds query t = l % 16
-//     and keys 4 g + i, 16 + 4 g + i of the tile (g = l / 16), which are, in order, its 8 probabilities as the B
-//     operand of O^T = V^T P^T.
-//   * K1, K2 and V tiles go straight to LDS (global_load_lds_dwordx4, 16 bytes per lane) through a 2-slot ring, one
-//     tile ahead; each V^T A operand (one channel, the lane's 8 keys) is two ds_read_b64_tr_b16 reads of the
-//     row-major V tile.  Only this wave reads its slots, so a vmcnt wait orders them (no barrier).  The loads are
-//     issued as inline assembly: the compiler then tracks no vector-memory operation inside the loop and adds no
-//     waits of its own (its tracking of direct-to-LDS loads cannot tell the two slots apart across the loop and
-//     would wait for the prefetch as well).
+//   * Scores S^T = K Q^T per 32-key tile: A = K rows, loaded from global memory straight into the operand layout
+//     (each lane 16 bytes of one key row per operand), B = the queries.  Lane l then holds query t = l % 16 and keys
+//     4 g + i, 16 + 4 g + i of the tile (g = l / 16), which are, in order, its 8 probabilities as the B operand of
+//     O^T = V^T P^T.
+//   * V rows are loaded into registers (16 lanes per 256-byte row, nontemporal) and written to the wave's one 8 KiB
+//     LDS tile; each V^T A operand (one channel, the lane's 8 keys) is two ds_read_b64_tr_b16 reads of it.  The next
+//     tile's rows are loaded while this one is computed.  With no K in LDS a wave needs 8 KiB of it, so the register
+//     file, not the LDS, sets the occupancy (two waves per SIMD).
+//   * Splits are long (up to 8192 keys, see plan_call): fewer, longer streams read faster here.
 //   * Online softmax per query and map, offsets moved only when a tile's max exceeds them by more than 2^8 (so no
 //     probability exceeds 2^8); offsets start at -FLT_MAX so a query with no visible key in the split keeps an empty
 //     state without NaN.  The split's state per query goes to the workspace in the merge kernel's format.
-constexpr int MQ = 16;                 // query columns of the tile
 constexpr int MT = 32;                 // keys per tile
 constexpr int MV_TILE = MT * DV * 2;   // 8 KiB
-constexpr int MK_TILE = MT * D * 2;    // 4 KiB
 constexpr float MULTI_RESCALE = 8.0f;  // log2 units
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -356,24 +353,6 @@ __device__ __forceinline__ int mv_sw(int r) {
     return ((r & 1) << 3) ^ (((r >> 1) & 1) << 2) ^ (((r >> 2) & 1) * 3) ^ (((r >> 3) & 1) << 1);
 }
 __device__ __forceinline__ int mv_off(int row, int chunk) { return row * 256 + ((chunk ^ mv_sw(row)) << 4); }
-// K tile in LDS: row r of 128 bytes, chunk c at c ^ ((r >> 1) & 7): the 16 rows of one chunk read by a 16-lane group
-// hit 16 distinct bank quads.
-__device__ __forceinline__ int mk_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
-
-// One 16-byte-per-lane direct load from global memory to LDS: lane L writes LDS [lds + 16 L, lds + 16 L + 16) with
-// the 16 bytes at src, nontemporal (each cache row is read once).  The s_nop is the wait state an LDS DMA needs after an SALU write of M0 (the compiler cannot
-// insert it inside the asm); nothing else in this kernel keeps a value in M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* src, unsigned lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ __forceinline__ unsigned lds_u32(const void* p) {
-    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
 struct MultiMap {
     float m, l;   // running offset (log2 units of the scaled scores) and this lane's part of the sum
 };
@@ -406,7 +385,7 @@ __device__ __forceinline__ bf16x8 multi_softmax(const f32x4 (&s)[2], MultiMap& s
 }
 
 template <bool PAGED>
-__global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* __restrict__ gq1,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_multi_mfma_kernel(const uint16_t* __restrict__ gq1,
                                                                const uint16_t* __restrict__ gk1,
                                                                const uint16_t* __restrict__ gq2,
                                                                const uint16_t* __restrict__ gk2,
@@ -414,9 +393,8 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
                                                                float* __restrict__ ws, int L, int T, int splits,
                                                                int split_keys, const int* __restrict__ lens, int H,
                                                                DecodePages pg, CacheStrides cs) {
-    __shared__ __attribute__((aligned(16))) unsigned char vs0[MV_TILE], vs1[MV_TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char ks0[2 * MK_TILE], ks1[2 * MK_TILE];   // K1 | K2
-    __shared__ int ptab[PAGED ? PT_MAX : 1];   // paged caches: the split's page indices
+    __shared__ __attribute__((aligned(16))) unsigned char vs[MV_TILE];   // the V tile being used
+    __shared__ int ptab[PAGED ? MULTI_PT_MAX : 1];   // paged caches: the split's page indices
 
     const int lane = threadIdx.x;
     const int g = lane >> 4, l16 = lane & 15;
@@ -463,39 +441,43 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
     }
 
     // Cache row index of absolute row r of this sequence.  Paged caches read the page index from the split's staged
-    // table (LDS), so no global load stands between the loop's direct loads.
+    // table (LDS), so no global load stands in front of a tile's loads.  One wave: its own later reads see the table.
     const int hh = bh % H, bb = bh / H;
-    const int pg0 = stage_pages<PAGED>(pg, bb, j0, ptab, lane, 64);   // one wave: its own later reads see them
+    const int pg0 = stage_pages<PAGED, MULTI_PT_MAX>(pg, bb, j0, ptab, lane, 64);
     auto elem = [&](int r, int t, int width) __attribute__((always_inline)) -> int64_t {
         return cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, r, t, width);
     };
 
-    // Tile loads (rows past the split's end repeat its last row and are masked).  K1 and K2: 4 pieces each of 8
-    // rows x 128 bytes; lane L of piece p writes LDS position 16 L, i.e. row 8 p + L / 8, stored chunk L % 8 =
-    // logical chunk ^ ((row >> 1) & 7).  V: 8 pieces of 4 rows x 256 bytes; lane L of piece p writes row
-    // 4 p + L / 16, stored chunk L % 16 = logical chunk ^ mv_sw(row).
+    // Tile loads (rows past the split's end repeat its last row and are masked), into registers.
+    //   K1 and K2 go straight into the layout of the A operand of S^T = K Q^T: for key block kb and feature half kh,
+    //   lane l holds key row 16 kb + l16 of the tile, features 32 kh + 8 g .. + 7.
+    //   V rows are staged through LDS for the transposing reads: lane L holds key 4 p + L / 16, 16-byte chunk L % 16
+    //   (p = 0..7), written to LDS at mv_off(row, chunk).
     const int n_tiles = (n + MT - 1) / MT;
-    auto load_tile = [&](int tile, unsigned char* kslot, unsigned char* vslot) __attribute__((always_inline)) {
+    u32x4 ka[2][2], kb2[2][2], vw[8];
+    auto load_k = [&](int tile) __attribute__((always_inline)) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int rr = 8 * p + (lane >> 3);
-            const int r = min(tile * MT + rr, n - 1);
-            const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
-            dma16(gk1 + elem(j0 + r, C_K1, D) + 8 * chunk, lds_u32(kslot + 1024 * p));
-            dma16(gk2 + elem(j0 + r, C_K2, D) + 8 * chunk, lds_u32(kslot + MK_TILE + 1024 * p));
-        }
+        for (int kb = 0; kb < 2; ++kb) {
+            const int r = min(tile * MT + 16 * kb + l16, n - 1);
+            const int64_t e1 = elem(j0 + r, C_K1, D), e2 = elem(j0 + r, C_K2, D);
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int rr = 4 * p + (lane >> 4);
-            const int r = min(tile * MT + rr, n - 1);
-            const int chunk = (lane & 15) ^ mv_sw(rr);
-            dma16(gv + elem(j0 + r, C_V, DV) + 8 * chunk, lds_u32(vslot + 1024 * p));
+            for (int kh = 0; kh < 2; ++kh) {
+                ka[kb][kh] = *(const u32x4*)(gk1 + e1 + 32 * kh + 8 * g);
+                kb2[kb][kh] = *(const u32x4*)(gk2 + e2 + 32 * kh + 8 * g);
+            }
         }
     };
-    constexpr int LOADS_PER_TILE = 8 + 8;   // K1 + K2 pieces, V pieces
-    // K A-operand of key block kb and feature half kh: row 16 kb + l16, chunk 4 kh + g; the row swizzle does not
-    // depend on kb, so mk_off(16 kb + l16, 4 kh + g) = (k_rd0 ^ (64 kh)) + 2048 kb.
-    const int k_rd0 = mk_off(l16, g);
+    auto load_v = [&](int tile) __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int r = min(tile * MT + 4 * p + (lane >> 4), n - 1);
+            vw[p] = ldnt(gv + elem(j0 + r, C_V, DV) + 8 * (lane & 15));
+        }
+    };
+    auto store_v = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) *(u32x4*)(vs + mv_off(4 * p + (lane >> 4), lane & 15)) = vw[p];
+    };
 
     // V^T operand offsets: lane 4 jj + qq of 16-lane group g supplies row 4 g + jj (then 16 + 4 g + jj), channels
     // 16 cb + 4 qq .. + 3, and receives channel 16 cb + l16 of those 4 keys; cb XORs 32 cb into the offset.
@@ -515,29 +497,21 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
         for (int i = 0; i < 4; ++i) { o1[cb][i] = 0.f; o2[cb][i] = 0.f; }
     MultiMap st1 = {-__FLT_MAX__, 0.f}, st2 = st1;
 
-    load_tile(0, ks0, vs0);
+    load_v(0);
+    load_k(0);
     // Q must have landed before the loop: the compiler waits for it here (and with it for tile 0's loads, issued
     // after it), so it places no wait for Q inside the loop.
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) asm volatile("" ::"v"(qa[kh]), "v"(qb[kh]));
-    // PREFETCH: issue the next tile's loads first (the caller guarantees it exists), then wait for this tile's.
-    // Both are compile-time, so the loop has no branch around the loads and the compiler's own waits stay exact.
-    auto step = [&](auto S, auto PREFETCH, int tile) __attribute__((always_inline)) {
-        constexpr int s0 = decltype(S)::value;
-        unsigned char* cur = s0 ? vs1 : vs0;
-        unsigned char* nxt = s0 ? vs0 : vs1;
-        const unsigned char* kcur = s0 ? ks1 : ks0;
-        unsigned char* knxt = s0 ? ks0 : ks1;
-        // The scheduling barriers keep this tile's matrix work after the wait (the compiler would otherwise hoist it
-        // and add waits of its own that also cover the prefetch).
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (decltype(PREFETCH)::value) {
-            load_tile(tile + 1, knxt, nxt);
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS_PER_TILE));   // tile `tile` has landed
-        } else {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    // One tile per step.  The next tile's V rows are loaded as soon as this tile's are in LDS, and its K rows as soon
+    // as this tile's scores are issued, so a tile's loads have one whole step to land.  PREFETCH is compile-time (the
+    // last tile is peeled), so the loop has no branch around the loads and the compiler's waits stay exact.  This
+    // wave alone uses its LDS tile, and its LDS operations complete in order, so no barrier or extra wait orders the
+    // next step's writes after this step's reads.
+    auto step = [&](auto PREFETCH, int tile) __attribute__((always_inline)) {
+        constexpr bool pf = decltype(PREFETCH)::value;
+        store_v();
+        if constexpr (pf) load_v(tile + 1);
         f32x4 s1[2], s2[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -545,11 +519,11 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
             for (int i = 0; i < 4; ++i) { s1[kb][i] = 0.f; s2[kb][i] = 0.f; }
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
-                const int off = (k_rd0 ^ (64 * kh)) + 2048 * kb;
-                s1[kb] = mfma16(*(const bf16x8*)(kcur + off), qa[kh], s1[kb]);
-                s2[kb] = mfma16(*(const bf16x8*)(kcur + MK_TILE + off), qb[kh], s2[kb]);
+                s1[kb] = mfma16(__builtin_bit_cast(bf16x8, ka[kb][kh]), qa[kh], s1[kb]);
+                s2[kb] = mfma16(__builtin_bit_cast(bf16x8, kb2[kb][kh]), qb[kh], s2[kb]);
             }
         }
+        if constexpr (pf) load_k(tile + 1);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -563,24 +537,14 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
         const bf16x8 p2 = multi_softmax(s2, st2, o2);
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) {
-            const bf16x8 va = v_frag(cur, cb);
+            const bf16x8 va = v_frag(vs, cb);
             o1[cb] = mfma16(va, p1, o1[cb]);
             o2[cb] = mfma16(va, p2, o2[cb]);
         }
-        // This tile's LDS reads are done before the next step's direct loads overwrite its slots.
-        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
     };
     int tile = 0;
-    for (; tile + 2 < n_tiles; tile += 2) {
-        step(Slot2<0>{}, Slot2<1>{}, tile);
-        step(Slot2<1>{}, Slot2<1>{}, tile + 1);
-    }
-    if (tile + 1 < n_tiles) {
-        step(Slot2<0>{}, Slot2<1>{}, tile);
-        step(Slot2<1>{}, Slot2<0>{}, tile + 1);
-    } else {
-        step(Slot2<0>{}, Slot2<0>{}, tile);
-    }
+    for (; tile + 1 < n_tiles; ++tile) step(Flag<true>{}, tile);
+    step(Flag<false>{}, tile);
 
     // The split's state per query column: offsets, sums over the column's four lanes, and O (lane holds channels
     // 16 cb + 4 g + i of its column).
@@ -601,10 +565,12 @@ __global__ __launch_bounds__(64) void decode_multi_mfma_kernel(const uint16_t* _
     }
 }
 
-// Split plan of a call (the same for every T).
+// Split plan of a call.  The multi-token kernel keeps no per-key state, so its splits may be long: at least
+// ceil(L / 8192) per head, more only to keep ~2048 waves in the grid (about one full round at 8 resident per CU).
+// Fewer, longer splits stream faster than more, shorter ones (B64 H16, ragged caches of 4K-8K rows, T = 4: splits
+// of 1024 keys 5.1 TB/s, 2048 5.7, 4096 5.8).
 SplitPlan plan_call(int64_t BH, int64_t L, int T) {
-    (void)T;   // the multi-token kernel keeps no per-key state, so every T shares the single-token plan
-    return plan_splits(BH, L);
+    return plan_splits(BH, L, T == 1 ? MAX_SPLIT_KEYS : MULTI_MAX_SPLIT_KEYS);
 }
 
 }  // namespace

@@ -733,6 +733,45 @@ def test_decode_paged(B, H, T, P, max_pages, lens, layer, bad):
     check_bf16(host_bf16(out), ref, f"decode paged T{T} page {P}", raw=layer == 0)
 
 
+def test_decode_multi_token_long_splits():
+    """Multi-token decode at the benchmarked size (B64 H16 T4, caches padded to 8192 rows with seeded ragged lengths
+    in [4096, 8192]), where the split plan gives each head two splits of 4096 keys: padded and paged (16-row pages,
+    so one split spans 256 pages of a shuffled pool) give identical bits, and sampled sequences match the oracle."""
+    torch = torch_mod()
+    B, H, T, L, P = 64, 16, 4, 8192, 16
+    inp = varlen_inputs(B, H, T, L, seed=880)
+    lens = np.random.default_rng(881).integers(L // 2, L + 1, size=B).astype(np.int32)
+    say(f"case: decode multi-token long splits B{B} H{H} T{T} L{L} lens {lens.min()}..{lens.max()} page {P}")
+    splits = da.diffattn_decode_varlen_workspace_bytes(B, H, T, L, 64) // (B * H * T * 1040)
+    assert splits == 2
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    ldev = torch.from_numpy(lens).to("cuda:0")
+    out = da.diffattn_decode_varlen(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.8, 1, lens=ldev)
+    torch.cuda.synchronize()
+    for k in ("k1", "k2", "v"):
+        del dev[k]
+    max_pages = L // P
+    perm = np.random.default_rng(882).permutation(B * max_pages)
+    pools = {}
+    for k in ("k1", "k2", "v"):
+        w = inp[k].shape[-1]
+        pg = inp[k].reshape(B, H, max_pages, P, w).transpose(0, 2, 1, 3, 4).reshape(B * max_pages, H, P, w)
+        pool = np.empty_like(pg)
+        pool[perm] = pg
+        pools[k] = dev_bf16(pool)
+        del pg, pool
+    table = torch.from_numpy(perm.reshape(B, max_pages).astype(np.int32)).to("cuda:0")
+    outp = da.diffattn_decode_paged(dev["q1"], pools["k1"], dev["q2"], pools["k2"], pools["v"], table, 0.8, 1,
+                                    lens=ldev)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), outp.view(torch.int16))
+    got = host_bf16(out)
+    for b in (0, 31, 63):
+        f = widen({k: v[b:b + 1] for k, v in inp.items()})
+        ref = varlen_reference(f, T, L, lens[b:b + 1], float(np.float32(0.8)), 1)
+        check_bf16(got[b:b + 1], ref, f"decode multi-token long splits b{b} len {lens[b]}")
+
+
 @pytest.mark.parametrize("T,paged,layer", [(2, False, 0), (16, False, 1), (2, True, 1), (16, True, 0)])
 def test_decode_multi_token_rescale(T, paged, layer):
     """Multi-token decode with map-1 scores that grow inside every split (half a nat per key), so the online softmax
