@@ -384,7 +384,8 @@ def bench_prefill_n65536(da, di, stream, dev, steps, oracle_rows=256):
     return {"workload": f"causal prefill B{B} H{H} N{N} d64 dv128, layer {layer}", "steps": steps, **st,
             "flops_exec": flops, "tflops_exec": round(tf, 2),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
-                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": read_traffic("prefill_n65536")},
             "cpu_oracle": {"rows": int(rows.size), "unmasked_pairs": sampled_pairs, "seconds": round(dt, 3),
                            "threads": threads,
                            "extrapolated_full_seconds": round(dt * pairs / sampled_pairs, 1),
