@@ -54,6 +54,7 @@ constexpr int K_SLOT_BYTES = 2 * K_TILE_BYTES;
 // Compile-time ring slot.  Each ring slot is its own __shared__ array, so the compiler can tell an LDS read of one
 // slot from a direct load still landing in another and does not drain the prefetches before every LDS read.
 template <int V> struct Slot { static constexpr int value = V; };
+template <bool V> struct Flag { static constexpr bool value = V; };
 template <int S, class T> __device__ __forceinline__ T* pick4(T* a, T* b, T* c, T* d) {
     static_assert(RING == 4, "one array per ring slot");
     if constexpr (S % 4 == 0) return a;
@@ -121,6 +122,14 @@ __device__ __forceinline__ float softmax_tile(const f32x16& s, MapState& st, f32
         part = exp_pack(s, ml, c, lo, hi);
     }
     return part;
+}
+
+// The first tile of a wave's rows (every row sees at least one of its keys): the offset is the tile's row max, and O
+// and l are still zero, so nothing is rescaled.  Same values as softmax_tile's exact path from the initial state.
+__device__ __forceinline__ float softmax_first(const f32x16& s, MapState& st, float c, bf16x8& lo, bf16x8& hi) {
+    st.ms = pair_max(max16(s));
+    st.ml = st.ms * c;
+    return exp_pack(s, st.ml, c, lo, hi);
 }
 
 // SAVE: also write each row's training statistics (SAVED_* in launch.h) for the backward pass.
@@ -268,8 +277,12 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
         const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * 64));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    auto step = [&](auto S, int t) {   // S = t % 4
+    // Mask bound of tile kv0: key kv0 + 8 (i / 4) + 4 h + i % 4 is visible to the lane's row q iff it is at most
+    // min(q, N - 1), i.e. iff 8 (i / 4) + i % 4 <= min(q, N - 1) - kv0 - 4 h (compile-time left-hand sides).
+    const int q_vis = min(q0w + l32, N - 1) - 4 * h;
+    auto step = [&](auto S, auto FIRST, int t) {   // S = t % 4; FIRST: the wave's first tile (t = 0)
         constexpr int s0 = decltype(S)::value;
+        constexpr bool first = decltype(FIRST)::value;
         issue_k(Slot<(s0 + 3) % 4>{}, t + 3);
         issue_v(Slot<(s0 + 3) % 4>{}, t + 3);
         const int kv0 = t * BN;
@@ -291,25 +304,24 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
                 s2 = mfma(kb, qb[kc], s2);
             }
             if ((causal && kv0 + BN - 1 > q0w) || kv0 + BN > N) {
-                const int q = q0w + l32;
+                const int d = (causal ? q_vis : N - 1 - 4 * h) - kv0;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int key = kv0 + 8 * (i >> 2) + 4 * h + (i & 3);
-                    const bool vis = key < N && (!causal || key <= q);
+                    const bool vis = 8 * (i >> 2) + (i & 3) <= d;
                     s1[i] = vis ? s1[i] : -INFINITY;
                     s2[i] = vis ? s2[i] : -INFINITY;
                 }
             }
             bf16x8 p1[2], p2[2];
             __builtin_amdgcn_s_setprio(0);
-            const float part1 = softmax_tile(s1, st1, o1, c, p1[0], p1[1]);
+            const float part1 = first ? softmax_first(s1, st1, c, p1[0], p1[1]) : softmax_tile(s1, st1, o1, c, p1[0], p1[1]);
             __builtin_amdgcn_s_setprio(1);
             bf16x8 va[4][2];
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) va[cb][0] = v_frag(vb_ + v_rd0 + 2048 * cb);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) o1[cb] = mfma(va[cb][0], p1[0], o1[cb]);
-            const float part2 = softmax_tile(s2, st2, o2, c, p2[0], p2[1]);
+            const float part2 = first ? softmax_first(s2, st2, c, p2[0], p2[1]) : softmax_tile(s2, st2, o2, c, p2[0], p2[1]);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) va[cb][1] = v_frag(vb_ + v_rd0 + 2048 * cb + 1024);
 #pragma unroll
@@ -327,11 +339,12 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * (K_PIECES_PER_WAVE + V_PIECES_PER_WAVE)));
         lds_barrier();
     };
-    for (int t = 0; t < n_tiles; t += 4) {
-        step(Slot<0>{}, t);
-        if (t + 1 < n_tiles) step(Slot<1>{}, t + 1);
-        if (t + 2 < n_tiles) step(Slot<2>{}, t + 2);
-        if (t + 3 < n_tiles) step(Slot<3>{}, t + 3);
+    step(Slot<0>{}, Flag<true>{}, 0);
+    for (int t = 1; t < n_tiles; t += 4) {
+        step(Slot<1>{}, Flag<false>{}, t);
+        if (t + 1 < n_tiles) step(Slot<2>{}, Flag<false>{}, t + 1);
+        if (t + 2 < n_tiles) step(Slot<3>{}, Flag<false>{}, t + 2);
+        if (t + 3 < n_tiles) step(Slot<0>{}, Flag<false>{}, t + 3);
     }
     // Drain the trailing prefetches before the workgroup can retire (their LDS writes must not outlive it).
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
