@@ -8,7 +8,8 @@ events recorded on the stream it is launched on.  Prints ONE JSON line.
   value     prefill TFLOP/s, counting 12*d FLOP per unmasked (query, key) pair (two Q.K^T products of width d and
             two P.V products of width 2d), i.e. B*H*N*(N+1)/2 pairs
   roofline  the prefill kernel against the bf16 dense MFMA peak; decode carries its own against HBM bandwidth
-  cpu_baseline  the double-precision CPU oracle on the same prefill workload (all rows by default)
+  cpu_baseline  the double-precision CPU oracle on the same prefill workload (all rows by default; on one thread,
+            every 16th row), and on the whole decode workload (all threads and one)
   decode_multi  (not part of the step) multi-token decode, 4 new tokens per sequence against ragged caches of
             4096..8192 rows at B64 H16: GB/s of the valid cache rows read
   decode_paged  (not part of the step) the decode workload read from 64-row pages of a shuffled page pool through
@@ -18,6 +19,8 @@ events recorded on the stream it is launched on.  Prints ONE JSON line.
             score maps and dP once (768) and dV, dQ1, dQ2, dK1, dK2 (512), the least an exact streaming backward
             does; tflops_exec counts the 1792 the kernels execute (the dQ kernel recomputes both score maps and dP and
             forms dQ1, dQ2: 768; the dK/dV kernel recomputes them and forms dV, dK1, dK2: 1024)
+  prefill_n1024  (not part of the step) the small causal prefill B1 H8 N1024 (layer 1), reported, not gated (64 row
+            tiles for 256 CUs), and the oracle's time on the whole problem, all host threads and one
   prefill_n65536  (not part of the step) the causal prefill at B1 H16 N65536 (layer 24): TFLOP/s with its roofline, and
             the oracle's time on 256 sampled rows with the full-problem time extrapolated from them (labelled so)
   clock     the GPU clock and socket power the box reports (amdsmi GPU metrics) while the prefill runs back to back
@@ -344,6 +347,66 @@ def context_rates(dev, stream):
             "stream_read_frac_of_peak": round((1 << 32) / (tr * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def bench_prefill_n1024(da, di, stream, dev, steps):
+    """The small causal prefill B1 H8 N1024 (layer 1): 64 row tiles for 256 CUs, so launch- and latency-bound (reported,
+    not gated), timed on the launch stream; and the oracle on the whole problem on all host threads and on one."""
+    import numpy as np
+    import torch
+    import oracle
+    c = di.CONFIGS["prefill_n1024"]
+    B, H, N, d, layer = c["B"], c["H"], c["N"], c["d"], c["layer"]
+    bits = di.prefill_bf16(B, H, N, d, c["seed"])
+    lam = float(np.float32(da.diffattn_lambda_init(layer)))
+    t = {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev) for k, v in bits.items()}
+    out = torch.empty_like(t["v"])
+    torch.cuda.synchronize()
+
+    def run():
+        da.diffattn_fwd(t["q1"], t["k1"], t["q2"], t["k2"], t["v"], lam, layer, True, out=out, stream=stream)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    st = med_stats(time_on_stream(run, stream, steps))
+    pairs = prefill_pairs(B, H, N)
+    flops = pairs * 12 * d
+    tf = flops / (st["ms"] * 1e-3) / 1e12
+    f = {k: di.bf16_bits_to_f32(v) for k, v in bits.items()}
+    timings = {}
+    for threads in (oracle.max_threads(), 1):
+        t0 = time.perf_counter()
+        oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam, layer, True, threads=threads)
+        timings[threads] = time.perf_counter() - t0
+    return {"workload": f"causal prefill B{B} H{H} N{N} d64 dv128, layer {layer}", "steps": steps, **st,
+            "flops_exec": flops, "tflops_exec": round(tf, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "note": "64 workgroups of 128 rows for 256 CUs: not a roofline case"},
+            "cpu_oracle": {"rows": B * H * N, "seconds_all_threads": round(timings[oracle.max_threads()], 4),
+                           "threads": oracle.max_threads(), "seconds_one_thread": round(timings[1], 4)}}
+
+
+def decode_oracle_time(di, d_bits, chunk=8):
+    """The oracle on the whole decode workload (64 sequences x 16 heads, 8192 cache rows each), on all host threads
+    and on one; the bf16 inputs are widened and evaluated 8 sequences at a time to bound host memory (the widening
+    is outside the timed calls)."""
+    import oracle
+    Dc = DECODE
+    n = oracle.max_threads()
+    tot = {n: 0.0, 1: 0.0}
+    for b0 in range(0, Dc["B"], chunk):
+        f = {k: di.bf16_bits_to_f32(v[b0:b0 + chunk]) for k, v in d_bits.items()}
+        for threads in (n, 1):
+            t0 = time.perf_counter()
+            oracle.decode(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], Dc["lam"], Dc["layer"], threads=threads)
+            tot[threads] += time.perf_counter() - t0
+        del f
+    return {"sample": f"the whole decode workload (B{Dc['B']} H{Dc['H']} L{Dc['L']}), double precision, on "
+                      f"'{cpu_model()}'",
+            "seconds_all_threads": round(tot[n], 3), "threads": n, "seconds_one_thread": round(tot[1], 3),
+            "gbs_all_threads": round(decode_bytes(Dc["B"], Dc["H"], Dc["L"], Dc["d"]) / tot[n] / 1e9, 2)}
+
+
 def bench_prefill_n65536(da, di, stream, dev, steps, oracle_rows=256):
     """The causal prefill at B1 H16 N65536 (layer 24), timed on the launch stream, and the oracle on 256 sampled
     rows (rows 0, 1, 63, 64, 127, 128, 4095, 4096, N - 1 of the first and last head, the rest seeded uniform), with
@@ -407,6 +470,8 @@ def main():
                     help="timed paged decode repetitions (0 skips that leg)")
     ap.add_argument("--n65536-steps", type=int, default=10,
                     help="timed repetitions of the B1 H16 N65536 prefill leg (0 skips it)")
+    ap.add_argument("--n1024-steps", type=int, default=20,
+                    help="timed repetitions of the B1 H8 N1024 prefill leg (0 skips it)")
     ap.add_argument("--clock-seconds", type=float, default=2.0,
                     help="length of the back-to-back prefill window sampled for clock and power (0 skips it)")
     ap.add_argument("--no-context", action="store_true", help="skip the library GEMM / streaming-read context leg")
@@ -444,7 +509,8 @@ def main():
     Dc = DECODE
     d_bits = di.decode_bf16(Dc["B"], Dc["H"], Dc["L"], Dc["d"], Dc["seed"])
     dq1, dk1, dq2, dk2, dv = (to_dev(d_bits[k]) for k in ("q1", "k1", "q2", "k2", "v"))
-    del d_bits
+    if args.no_cpu_baseline:
+        del d_bits   # kept otherwise for the oracle's decode timing
     dout = torch.empty((Dc["B"], Dc["H"], 2 * Dc["d"]), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(da.diffattn_decode_workspace_bytes(Dc["B"], Dc["H"], Dc["L"], Dc["d"]), dtype=torch.uint8,
                      device=dev)
@@ -541,6 +607,8 @@ def main():
                                                     dbytes)
     if args.bwd_steps > 0:
         result["backward"] = bench_backward(da, di, stream, p_bits, pq1, pk1, pq2, pk2, pv, p_lam, args.bwd_steps)
+    if args.n1024_steps > 0:
+        result["prefill_n1024"] = bench_prefill_n1024(da, di, stream, dev, args.n1024_steps)
     if args.n65536_steps > 0:
         del dq1, dk1, dq2, dk2, dv, ws
         torch.cuda.empty_cache()
@@ -549,6 +617,7 @@ def main():
         cb = cpu_baseline(p_bits, p_lam, P["layer"], P["N"], args.cpu_rows)
         one = cpu_baseline(p_bits, p_lam, P["layer"], P["N"], max(1, args.cpu_rows // 16), threads=1)
         cb["single_core"] = {k: one[k] for k in ("value", "unit", "cores", "sample", "seconds")}
+        cb["decode"] = decode_oracle_time(di, d_bits)
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
