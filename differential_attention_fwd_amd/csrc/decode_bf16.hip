@@ -75,11 +75,11 @@ struct SplitPlan {
     int split_keys;  // keys per split (the last split may be shorter)
 };
 
-__host__ __device__ inline SplitPlan plan_splits(int64_t BH, int64_t L, int64_t max_keys) {
-    // At least ceil(L / max_keys) splits; more for few heads so that the grid has >= ~2048 workgroups,
+__host__ __device__ inline SplitPlan plan_splits(int64_t BH, int64_t L, int64_t max_keys, int64_t min_grid) {
+    // At least ceil(L / max_keys) splits; more for few heads so that the grid has >= ~min_grid workgroups,
     // but never below 64 keys per split.
     int64_t s = (L + max_keys - 1) / max_keys;
-    const int64_t want = (2048 + BH - 1) / (BH > 0 ? BH : 1);
+    const int64_t want = (min_grid + BH - 1) / (BH > 0 ? BH : 1);
     const int64_t cap = (L + 63) / 64;
     if (s < want) s = want < cap ? want : cap;
     if (s < 1) s = 1;
@@ -565,12 +565,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     }
 }
 
-// Split plan of a call.  The multi-token kernel keeps no per-key state, so its splits may be long: at least
-// ceil(L / 8192) per head, more only to keep ~2048 waves in the grid (about one full round at 8 resident per CU).
-// Fewer, longer splits stream faster than more, shorter ones (B64 H16, ragged caches of 4K-8K rows, T = 4: splits
-// of 1024 keys 5.1 TB/s, 2048 5.7, 4096 5.8).
+// Split plan of a call.  The single-token kernel takes splits of at most 1024 keys (its scores live in LDS) and at
+// least ~2048 workgroups.  The multi-token kernel keeps no per-key state, so its splits may be long: at least
+// ceil(L / 8192) per head, more only to keep ~1024 waves in the grid (four per CU).  Fewer, longer splits stream
+// faster than more, shorter ones (B64 H16, ragged caches of 4K-8K rows, T = 4: splits of 1024 keys 5.1 TB/s, 2048
+// 5.7, 4096 5.85, one 8192-key split per head 5.93).
 SplitPlan plan_call(int64_t BH, int64_t L, int T) {
-    return plan_splits(BH, L, T == 1 ? MAX_SPLIT_KEYS : MULTI_MAX_SPLIT_KEYS);
+    return T == 1 ? plan_splits(BH, L, MAX_SPLIT_KEYS, 2048) : plan_splits(BH, L, MULTI_MAX_SPLIT_KEYS, 1024);
 }
 
 }  // namespace
