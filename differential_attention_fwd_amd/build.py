@@ -15,6 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdiffattn.so")
+CHECK_BUILD = os.path.join(BUILD, "check")
+CHECK_LIB = os.path.join(HERE, "libdiffattn_check.so")
 SOURCES = ["diffattn_api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "attn_f32.hip", "backward_bf16.hip"]
 # Per-source extra flags.  The prefill kernel never produces a NaN (see its header), and without NaN semantics
 # v_max3 needs no quieting of MFMA results.
@@ -27,9 +29,10 @@ FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-
          "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, check: bool = False) -> str:
+    obj = os.path.join(CHECK_BUILD if check else BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *(["-DDIFFATTN_CHECK"] if check else []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -40,19 +43,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link libdiffattn.so next to this file.  Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libdiffattn.so next to this file, and the check build
+    libdiffattn_check.so (-DDIFFATTN_CHECK: every LDS piece is filled with NaN before its direct load is issued, so a
+    read that races ahead of a load shows up as NaN in the output; for tests only).  Always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(CHECK_BUILD, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + [(s, True) for s in SOURCES]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CHECK_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CHECK_LIB}")
     return LIB
 
 

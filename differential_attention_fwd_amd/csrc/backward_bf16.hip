@@ -224,6 +224,11 @@ void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict_
         constexpr int s0 = decltype(S)::value;
         unsigned char* ks = pick4<s0>(kr0, kr1, kr2, kr3);
         unsigned char* vs = pick4<s0>(vr0, vr1, vr2, vr3);
+        check_fill(ks + 1024 * wave, 16);
+        check_fill(ks + K_TILE + 1024 * wave, 16);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) check_fill(vs + 1024 * (wave + WAVES * j), 16);
+        check_fence();
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk1, (lds_void*)(ks + 1024 * wave), 16,
                                                  (int)(k1_voff + (unsigned)t * k1_step), 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk2, (lds_void*)(ks + K_TILE + 1024 * wave), 16,
@@ -451,6 +456,12 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
     const unsigned st_voff = (unsigned)(lane & 31) * (STAT_FLOATS * 4) + 4u * (unsigned)wave;
     auto issue = [&](auto S, int u) __attribute__((always_inline)) {
         unsigned char* s = pick3<decltype(S)::value>(sl0, sl1, sl2);
+        check_fill(s + 1024 * wave, 16);
+        check_fill(s + Q_TILE_BYTES + 1024 * wave, 16);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) check_fill(s + 2 * Q_TILE_BYTES + 1024 * (wave + WAVES * j), 16);
+        if (lane < 32) check_fill(s + ST_OFF + 128 * wave, 4);   // lanes 0..31 load 4 bytes each
+        check_fence();
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rq1, (lds_void*)(s + 1024 * wave), 16,
                                                  (int)(q1_voff + (unsigned)u * q1_step), 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rq2, (lds_void*)(s + Q_TILE_BYTES + 1024 * wave), 16,

@@ -220,6 +220,9 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     auto issue_k = [&](auto S, int t) {   // S = t % 4
         unsigned char* slot = pick4<decltype(S)::value>(kr0, kr1, kr2, kr3);
 #pragma unroll
+        for (int j = 0; j < K_PIECES_PER_WAVE; ++j) check_fill(slot + kd_lds[j], 16);
+        check_fence();
+#pragma unroll
         for (int j = 0; j < K_PIECES_PER_WAVE; ++j) {
             // The tile offset goes into the VGPR offset: the SGPR offset is not part of the buffer range check.
             const unsigned ko = kd_voff[j] + (unsigned)t * kd_step[j];
@@ -231,6 +234,9 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     };
     auto issue_v = [&](auto S, int t) {   // S = t % 4
         unsigned char* slot = pick4<decltype(S)::value>(vr0, vr1, vr2, vr3);
+#pragma unroll
+        for (int j = 0; j < V_PIECES_PER_WAVE; ++j) check_fill(slot + 1024 * (wave + WAVES * j), 16);
+        check_fence();
 #pragma unroll
         for (int j = 0; j < V_PIECES_PER_WAVE; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(slot + 1024 * (wave + WAVES * j)), 16,

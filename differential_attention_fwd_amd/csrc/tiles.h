@@ -58,4 +58,25 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Check builds (compiled with -DDIFFATTN_CHECK, see build.py): before a wave issues a direct load of `size` bytes
+// per lane into an LDS piece, each lane fills the bytes its load will write with NaN (bf16 and fp32 alike).  Call
+// check_fence() after the fills of a tile and before its loads: the fills then complete before the loads can land,
+// and a read of the piece before its load has landed returns NaN, which reaches the output.  Ordinary builds
+// compile both to nothing.
+__device__ __forceinline__ void check_fill(unsigned char* piece, int size) {
+#ifdef DIFFATTN_CHECK
+    unsigned char* p = piece + size * (int)(threadIdx.x & 63);
+    if (size == 16) *(u32x4*)p = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+    else *(unsigned*)p = 0x7fc07fc0u;
+#else
+    (void)piece;
+    (void)size;
+#endif
+}
+__device__ __forceinline__ void check_fence() {
+#ifdef DIFFATTN_CHECK
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+#endif
+}
+
 }  // namespace diffattn
