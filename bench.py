@@ -25,8 +25,9 @@ events recorded on the stream it is launched on.  Prints ONE JSON line.
             the oracle's time on 256 sampled rows with the full-problem time extrapolated from them (labelled so)
   clock     the GPU clock and socket power the box reports (amdsmi GPU metrics) while the prefill runs back to back
             for about two seconds, and the prefill rate over that window
-  context   the same box's bf16 GEMM rate (torch.matmul 8192^3, random data) and streaming-read rate (a sum over a
-            4 GiB tensor): what library kernels reach here, next to the nominal peaks
+  context   the same box's bf16 GEMM rate (torch.matmul 8192^3, random data), torch's streaming read (a sum over a
+            4 GiB tensor), and the best streaming read of a plain probe kernel (16-byte nontemporal loads, the decode
+            kernels' access pattern; libstreamprobe.so): what this machine reaches, next to the nominal peaks
 Each timed kernel reports the median over its repetitions (the headline value uses the median), with the mean and
 the minimum beside it.
 Every roofline's "traffic" is the HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
@@ -338,13 +339,46 @@ def context_rates(dev, stream):
         for _ in range(2):
             x.sum(dtype=torch.float32)
         ms_r = time_on_stream(lambda: x.sum(dtype=torch.float32), stream, 10)
-    del x
     import statistics
     tg, tr = statistics.median(ms_g), statistics.median(ms_r)
+    probe = stream_probe(x, stream)
+    del x
     return {"gemm_bf16_8192_tflops": round(2 * 8192 ** 3 / (tg * 1e-3) / 1e12, 1),
             "gemm_bf16_8192_frac_of_peak": round(2 * 8192 ** 3 / (tg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "stream_read_gbs": round((1 << 32) / (tr * 1e-3) / 1e9, 1),
-            "stream_read_frac_of_peak": round((1 << 32) / (tr * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            "torch_sum_read_gbs": round((1 << 32) / (tr * 1e-3) / 1e9, 1),
+            **probe}
+
+
+def stream_probe(x, stream):
+    """Best streaming-read rate of this machine over a few launch shapes: one read of the 4 GiB tensor x with 16-byte
+    nontemporal loads (the decode kernels' access pattern), median of 5 reads per shape (libstreamprobe.so)."""
+    import ctypes
+    import statistics
+    import torch
+    from differential_attention_fwd_amd import build as dbuild
+    if not os.path.exists(dbuild.PROBE_LIB):
+        return {"stream_read_error": f"{dbuild.PROBE_LIB} is not built"}
+    L = ctypes.CDLL(dbuild.PROBE_LIB)
+    L.stream_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
+    L.stream_read_probe.restype = ctypes.c_int
+    nbytes = x.numel() * x.element_size()
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=x.device)
+        for unroll in (2, 4, 8):
+            def run():
+                rc = L.stream_read_probe(x.data_ptr(), nbytes, out.data_ptr(), blocks, unroll, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"stream_read_probe failed: {rc}")
+            run()
+            ms = statistics.median(time_on_stream(run, stream, 5))
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, blocks, unroll)
+    return {"stream_read_gbs": round(best[0], 1), "stream_read_frac_of_peak": round(best[0] / PEAK_HBM_GBS, 4),
+            "stream_read_shape": f"{best[1]} workgroups of 256 threads, {best[2]} 16-byte nontemporal loads in flight "
+                                 f"per thread, best of 12 shapes"}
 
 
 def bench_prefill_n1024(da, di, stream, dev, steps):

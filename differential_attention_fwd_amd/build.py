@@ -17,6 +17,9 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdiffattn.so")
 CHECK_BUILD = os.path.join(BUILD, "check")
 CHECK_LIB = os.path.join(HERE, "libdiffattn_check.so")
+# Measurement context for bench.py (a streaming-read probe), not part of the library.
+PROBE_SRC = "stream_probe.hip"
+PROBE_LIB = os.path.join(HERE, "libstreamprobe.so")
 SOURCES = ["diffattn_api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "attn_f32.hip", "backward_bf16.hip"]
 # Per-source extra flags.  The prefill kernel never produces a NaN (see its header), and without NaN semantics
 # v_max3 needs no quieting of MFMA results.
@@ -58,13 +61,15 @@ def build(verbose: bool = False) -> str:
     read that races ahead of a load shows up as NaN in the output; for tests only).  Always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(CHECK_BUILD, exist_ok=True)
-    jobs = [(s, False) for s in SOURCES] + [(s, True) for s in SOURCES]
+    jobs = [(s, False) for s in SOURCES] + [(s, True) for s in SOURCES] + [(PROBE_SRC, False)]
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         objs = list(ex.map(lambda j: _compile(*j), jobs))
-    _link(objs[:len(SOURCES)], LIB)
-    _link(objs[len(SOURCES):], CHECK_LIB)
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:2 * n], CHECK_LIB)
+    _link(objs[2 * n:], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} and {CHECK_LIB}")
+        print(f"built {LIB}, {CHECK_LIB} and {PROBE_LIB}")
     return LIB
 
 
