@@ -215,6 +215,28 @@ def dec_var(lib, T=4, L=100, lens=A[7], out=A[5], ws=A[6], ws_bytes=None, B=2, H
                                       ws, ws_bytes, None)
 
 
+def split_plan(BH, L, max_keys, min_grid):
+    """The decode split plan, restated: at least ceil(L / max_keys) splits per head, more (up to 64 keys per split) to
+    reach about min_grid split workgroups, then as many equal splits as the resulting split length needs."""
+    s = -(-L // max_keys)
+    want, cap = -(-min_grid // BH), -(-L // 64)
+    if s < want:
+        s = min(want, cap)
+    keys = -(-L // s)
+    return -(-L // keys)
+
+
+@pytest.mark.parametrize("B,H,L", [(64, 16, 8192), (1, 2, 8192), (4, 8, 100000), (2, 3, 777), (128, 16, 65536)])
+def test_decode_split_plans(lib, B, H, L):
+    """One token: splits of at most 1024 keys and ~2048 workgroups; several tokens: at most 8192 keys and ~1024 waves
+    (workspace = B H T splits x 1040 bytes: m, l and O of both maps per split)."""
+    for T, max_keys, grid in ((1, 1024, 2048), (4, 8192, 1024), (16, 8192, 1024)):
+        splits = split_plan(B * H, L, max_keys, grid)
+        assert lib.diffattn_decode_varlen_workspace_bytes(B, H, T, L, 64) == B * H * T * splits * 1040, (T, splits)
+    # the benchmarked multi-token size: one 8192-key split per head
+    assert split_plan(64 * 16, 8192, 8192, 1024) == 1
+
+
 def test_varlen_workspace_sizes(lib):
     one = lib.diffattn_decode_varlen_workspace_bytes(64, 16, 1, 8192, 64)
     assert one == lib.diffattn_decode_workspace_bytes(64, 16, 8192, 64)
