@@ -405,6 +405,20 @@ def bench_prefill_n1024(da, di, stream, dev, steps):
     pairs = prefill_pairs(B, H, N)
     flops = pairs * 12 * d
     tf = flops / (st["ms"] * 1e-3) / 1e12
+    # The split-key entry point for launches this small (query tiles' keys split across workgroups, then merged).
+    ws = torch.empty(max(da.diffattn_fwd_split_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8, device=dev)
+    out_s = torch.empty_like(out)
+    torch.cuda.synchronize()
+
+    def run_split():
+        da.diffattn_fwd_split(t["q1"], t["k1"], t["q2"], t["k2"], t["v"], lam, layer, True, out=out_s, workspace=ws,
+                              stream=stream)
+
+    for _ in range(3):
+        run_split()
+    torch.cuda.synchronize()
+    sst = med_stats(time_on_stream(run_split, stream, steps))
+    tfs = flops / (sst["ms"] * 1e-3) / 1e12
     f = {k: di.bf16_bits_to_f32(v) for k, v in bits.items()}
     timings = {}
     for threads in (oracle.max_threads(), 1):
@@ -416,6 +430,8 @@ def bench_prefill_n1024(da, di, stream, dev, steps):
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                          "note": "64 workgroups of 128 rows for 256 CUs: not a roofline case"},
+            "split": {**sst, "tflops_exec": round(tfs, 2), "frac": round(tfs / PEAK_BF16_TFLOPS, 4),
+                      "entry": "diffattn_fwd_split (key splits merged by log-sum-exp; the time includes the merge)"},
             "cpu_oracle": {"rows": B * H * N, "seconds_all_threads": round(timings[oracle.max_threads()], 4),
                            "threads": oracle.max_threads(), "seconds_one_thread": round(timings[1], 4)}}
 

@@ -18,7 +18,8 @@ DIFFATTN_F32 = 1
 STATUS = {0: "DIFFATTN_OK", -1: "DIFFATTN_ERR_NULL", -2: "DIFFATTN_ERR_SHAPE", -3: "DIFFATTN_ERR_UNSUPPORTED",
           -4: "DIFFATTN_ERR_ALIGN", -5: "DIFFATTN_ERR_LAYER", -6: "DIFFATTN_ERR_LAMBDA",
           -7: "DIFFATTN_ERR_WORKSPACE", -8: "DIFFATTN_ERR_ALIAS", -9: "DIFFATTN_ERR_HIP"}
-EXPORTS = ["diffattn_fwd", "diffattn_fwd_heads", "diffattn_fwd_strided", "diffattn_decode", "diffattn_decode_heads",
+EXPORTS = ["diffattn_fwd", "diffattn_fwd_heads", "diffattn_fwd_strided", "diffattn_fwd_split_workspace_bytes",
+           "diffattn_fwd_split", "diffattn_decode", "diffattn_decode_heads",
            "diffattn_decode_workspace_bytes", "diffattn_decode_varlen_workspace_bytes", "diffattn_decode_varlen",
            "diffattn_decode_paged_workspace_bytes", "diffattn_decode_paged", "diffattn_decode_strided",
            "diffattn_train_saved_bytes", "diffattn_fwd_train", "diffattn_fwd_train_strided",
@@ -58,6 +59,11 @@ def lib() -> ctypes.CDLL:
     L.diffattn_decode_heads.restype = c_int
     L.diffattn_fwd_strided.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, P, c_int, c_int, P, P]
     L.diffattn_fwd_strided.restype = c_int
+    L.diffattn_fwd_split_workspace_bytes.argtypes = [i64, i64, i64, c_int]
+    L.diffattn_fwd_split_workspace_bytes.restype = ctypes.c_size_t
+    L.diffattn_fwd_split.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, c_int, c_int, P,
+                                     ctypes.c_size_t, P]
+    L.diffattn_fwd_split.restype = c_int
     L.diffattn_decode_varlen_workspace_bytes.argtypes = [i64, i64, i64, i64, c_int]
     L.diffattn_decode_varlen_workspace_bytes.restype = ctypes.c_size_t
     L.diffattn_decode_varlen.argtypes = [P, P, P, P, P, P, i64, i64, i64, i64, P, c_int, c_int, c_float, P, c_int, P,
@@ -149,6 +155,37 @@ def _lambda_heads(lam, H, device):
     if lam.dtype != torch.float32 or lam.device != device or tuple(lam.shape) != (H,) or not lam.is_contiguous():
         raise ValueError(f"per-head lambda must be a contiguous float32 tensor of shape ({H},) on {device}")
     return lam
+
+
+def diffattn_fwd_split_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().diffattn_fwd_split_workspace_bytes(int(B), int(H), int(N), int(d)))
+
+
+def diffattn_fwd_split(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool, out=None, workspace=None,
+                       stream=None):
+    """Split-key prefill (bf16, d = 64, dense): diffattn_fwd's result up to rounding, for launches too small to fill
+    the GPU.  `workspace`: a GPU tensor of at least diffattn_fwd_split_workspace_bytes(B, H, N, d) bytes (allocated
+    here if None)."""
+    import torch
+    _check_tensors((q1, k1, q2, k2, v))
+    B, H, N, d = q1.shape
+    if out is None:
+        out = torch.empty((B, H, N, 2 * d), dtype=q1.dtype, device=q1.device)
+    _check_tensors((out,))
+    for t, shp in ((k1, q1.shape), (q2, q1.shape), (k2, q1.shape), (v, (B, H, N, 2 * d)), (out, (B, H, N, 2 * d))):
+        if tuple(t.shape) != tuple(shp) or t.dtype != q1.dtype:
+            raise ValueError(f"shape/dtype mismatch: {tuple(t.shape)} {t.dtype}, expected {tuple(shp)} {q1.dtype}")
+    need = diffattn_fwd_split_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    _check_tensors((workspace,))
+    st = lib().diffattn_fwd_split(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
+                                  out.data_ptr(), B, H, N, d, _dtype_code(q1), float(lam), int(layer),
+                                  int(bool(causal)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream_handle(stream, q1.device))
+    if st != 0:
+        raise DiffAttnError(st, "diffattn_fwd_split")
+    return out
 
 
 def diffattn_fwd(q1, k1, q2, k2, v, lam, layer: int, causal: bool, out=None, stream=None):

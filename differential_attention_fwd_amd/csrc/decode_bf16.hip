@@ -41,6 +41,7 @@ constexpr int MULTI_PT_MAX = 520;             // the same for several tokens
 static_assert(MAX_SPLIT_KEYS / 16 + 2 <= PT_MAX, "a split spans at most keys / 16 + 2 pages of the smallest size");
 static_assert(MULTI_MAX_SPLIT_KEYS / 16 + 2 <= MULTI_PT_MAX, "a split spans at most keys / 16 + 2 pages");
 constexpr int PART_FLOATS = 4 + 2 * DV;       // m1, l1, m2, l2, O1[128], O2[128]
+static_assert(PART_FLOATS == PARTIAL_FLOATS, "the decode's split states are the shared partial-state format");
 constexpr int MAX_T = 16;                     // new tokens per sequence in multi-token decode
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -260,44 +261,13 @@ __global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* _
     for (int k = tid; k < 2 * DV; k += THREADS) dst[4 + k] = part[0][k] + part[1][k] + part[2][k] + part[3][k];
 }
 
-// One wave per head: lane owns channels 2*lane and 2*lane + 1.
-// Work item = (head, query): blockIdx.x = bh * T + t.  Every query sees at least one key, so some split is
+// One wave per (head, query): blockIdx.x = bh * T + t.  Every query sees at least one key, so some split is
 // non-empty and the merged maxima are finite.
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ ws, uint16_t* __restrict__ gout,
                                                           int splits, int T, Epilogue ep) {
     const int item = blockIdx.x;
-    const int bh = item / T;
-    const int lane = threadIdx.x;
-    const float* part = ws + (size_t)item * splits * PART_FLOATS;
-    float M1 = -INFINITY, M2 = -INFINITY;
-    for (int s = 0; s < splits; ++s) {
-        M1 = fmaxf(M1, part[s * PART_FLOATS + 0]);
-        M2 = fmaxf(M2, part[s * PART_FLOATS + 2]);
-    }
-    float L1 = 0.f, L2 = 0.f, o1a = 0.f, o1b = 0.f, o2a = 0.f, o2b = 0.f;
-    for (int s = 0; s < splits; ++s) {
-        const float* p = part + s * PART_FLOATS;
-        const float w1 = __builtin_amdgcn_exp2f(p[0] - M1);
-        const float w2 = __builtin_amdgcn_exp2f(p[2] - M2);
-        L1 += w1 * p[1];
-        L2 += w2 * p[3];
-        o1a += w1 * p[4 + 2 * lane];
-        o1b += w1 * p[4 + 2 * lane + 1];
-        o2a += w2 * p[4 + DV + 2 * lane];
-        o2b += w2 * p[4 + DV + 2 * lane + 1];
-    }
-    const float inv1 = 1.f / L1, inv2 = lambda_of(ep, bh) / L2;
-    float ya = o1a * inv1 - o2a * inv2;
-    float yb = o1b * inv1 - o2b * inv2;
-    if (ep.normalise) {
-        const float ss = wave_sum(ya * ya + yb * yb);
-        const float r = __builtin_amdgcn_rsqf(ss * (1.f / DV) + 1e-5f) * ep.out_scale;
-        ya *= r;
-        yb *= r;
-    }
-    const unsigned w = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)ya) |
-                       ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)yb) << 16);
-    *(unsigned*)(gout + (size_t)item * DV + 2 * lane) = w;
+    merge_partial_row(ws + (size_t)item * splits * PART_FLOATS, splits, ep, item / T, gout + (size_t)item * DV,
+                      (int)threadIdx.x);
 }
 
 template <bool V> struct Flag { static constexpr bool value = V; };

@@ -104,7 +104,7 @@ const char* diffattn_status_str(int status) {
         case DIFFATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
         case DIFFATTN_ERR_LAYER: return "layer index must be >= 0";
         case DIFFATTN_ERR_LAMBDA: return "lambda must be finite";
-        case DIFFATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case DIFFATTN_ERR_WORKSPACE: return "workspace missing or too small";
         case DIFFATTN_ERR_ALIAS: return "output or workspace overlaps another argument";
         case DIFFATTN_ERR_HIP: return "HIP runtime error at launch";
         default: return "unknown status";
@@ -227,6 +227,58 @@ int diffattn_fwd_strided(const void* q1, const void* k1, const void* q2, const v
     return hip_status(diffattn::launch_prefill_bf16_d64((const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2,
                                                         (const uint16_t*)k2, (const uint16_t*)v, (uint16_t*)out, B, H,
                                                         N, causal, S, ep, nullptr, (hipStream_t)stream));
+}
+
+size_t diffattn_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int d) {
+    int64_t BH, rows, floats;
+    if (B < 0 || H < 0 || N < 0 || N > DIFFATTN_MAX_LEN || d != 64 || !mul_ok(B, H, &BH) || BH > INT32_MAX ||
+        !mul_ok(BH, N, &rows))
+        return 0;
+    const int splits = diffattn::prefill_key_splits_max(BH, N);
+    if (splits <= 1 || !mul_ok(rows, (int64_t)splits * diffattn::PARTIAL_FLOATS, &floats) ||
+        floats > INT64_MAX / 4)
+        return 0;
+    return (size_t)floats * sizeof(float);
+}
+
+int diffattn_fwd_split(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
+                       int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda, int layer, int causal,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || H < 0 || N < 0 || N > DIFFATTN_MAX_LEN) return DIFFATTN_ERR_SHAPE;
+    int st = check_dtype_d(dtype, d);
+    if (st) return st;
+    if (dtype != DIFFATTN_BF16 || d != 64) return DIFFATTN_ERR_UNSUPPORTED;
+    Epilogue ep;
+    st = make_epilogue(lambda, layer, &ep);
+    if (st) return st;
+    int64_t BH, rows, qk_elems, v_elems;
+    if (!mul_ok(B, H, &BH) || BH > INT32_MAX || !mul_ok(BH, N, &rows) || rows > INT32_MAX ||
+        !mul_ok(rows, d, &qk_elems) || !mul_ok(rows, 2 * (int64_t)d, &v_elems))
+        return DIFFATTN_ERR_SHAPE;
+    if (rows == 0) return DIFFATTN_OK;
+    if (!q1 || !k1 || !q2 || !k2 || !v || !out) return DIFFATTN_ERR_NULL;
+    if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2) || !aligned16(v) || !aligned16(out))
+        return DIFFATTN_ERR_ALIGN;
+    const size_t qk_bytes = (size_t)qk_elems * 2, v_bytes = (size_t)v_elems * 2;
+    const Span o{(uintptr_t)out, (uintptr_t)out + v_bytes};
+    const Span ins[5] = {{(uintptr_t)q1, (uintptr_t)q1 + qk_bytes}, {(uintptr_t)k1, (uintptr_t)k1 + qk_bytes},
+                         {(uintptr_t)q2, (uintptr_t)q2 + qk_bytes}, {(uintptr_t)k2, (uintptr_t)k2 + qk_bytes},
+                         {(uintptr_t)v, (uintptr_t)v + v_bytes}};
+    for (const Span& s : ins)
+        if (overlaps(o, s)) return DIFFATTN_ERR_ALIAS;
+    const size_t need = diffattn_fwd_split_workspace_bytes(B, H, N, d);
+    if (need > 0) {
+        if (!workspace) return DIFFATTN_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return DIFFATTN_ERR_ALIGN;
+        if (workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+        const Span w{(uintptr_t)workspace, (uintptr_t)workspace + need};
+        if (overlaps(w, o)) return DIFFATTN_ERR_ALIAS;
+        for (const Span& s : ins)
+            if (overlaps(w, s)) return DIFFATTN_ERR_ALIAS;
+    }
+    return hip_status(diffattn::launch_prefill_split_bf16_d64(
+        (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2, (const uint16_t*)k2, (const uint16_t*)v,
+        (uint16_t*)out, B, H, N, causal, ep, (float*)workspace, (hipStream_t)stream));
 }
 
 size_t diffattn_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {

@@ -55,6 +55,62 @@ hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const
                                    const uint16_t* v, uint16_t* out, int64_t B, int64_t H, int64_t N, int causal,
                                    const Strides& st, Epilogue ep, float* saved, hipStream_t stream);
 
+// Partial state of one row over one key range, the split launches' workspace format (the decode and the split-key
+// prefill), PARTIAL_FLOATS fp32: [0] m1, [2] m2 the two maps' offsets (log2 units of the scaled scores, -inf for a
+// row that saw no key), [1] l1, [3] l2 their sums at those offsets, then the unnormalised O1 and O2 (128 each).
+constexpr int PARTIAL_FLOATS = 4 + 2 * 128;
+
+// Merge the n partial states at `part` (consecutive, PARTIAL_FLOATS apart) of one row by log-sum-exp, apply the
+// epilogue of (batch, head) unit bh and store the row's 128 outputs in bf16.  One wave per row: lane owns channels
+// 2 lane and 2 lane + 1.  At least one state must hold a key (finite offsets).
+__device__ __forceinline__ void merge_partial_row(const float* __restrict__ part, int n, const Epilogue& ep, int bh,
+                                                  uint16_t* __restrict__ out_row, int lane) {
+    float M1 = -INFINITY, M2 = -INFINITY;
+    for (int s = 0; s < n; ++s) {
+        M1 = fmaxf(M1, part[s * PARTIAL_FLOATS + 0]);
+        M2 = fmaxf(M2, part[s * PARTIAL_FLOATS + 2]);
+    }
+    float L1 = 0.f, L2 = 0.f, o1a = 0.f, o1b = 0.f, o2a = 0.f, o2b = 0.f;
+    for (int s = 0; s < n; ++s) {
+        const float* p = part + s * PARTIAL_FLOATS;
+        const float w1 = __builtin_amdgcn_exp2f(p[0] - M1);
+        const float w2 = __builtin_amdgcn_exp2f(p[2] - M2);
+        L1 += w1 * p[1];
+        L2 += w2 * p[3];
+        o1a += w1 * p[4 + 2 * lane];
+        o1b += w1 * p[4 + 2 * lane + 1];
+        o2a += w2 * p[4 + 128 + 2 * lane];
+        o2b += w2 * p[4 + 128 + 2 * lane + 1];
+    }
+    const float inv1 = 1.f / L1, inv2 = lambda_of(ep, bh) / L2;
+    float ya = o1a * inv1 - o2a * inv2;
+    float yb = o1b * inv1 - o2b * inv2;
+    if (ep.normalise) {
+        float ss = ya * ya + yb * yb;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+        const float r = __builtin_amdgcn_rsqf(ss * (1.f / 128) + 1e-5f) * ep.out_scale;
+        ya *= r;
+        yb *= r;
+    }
+    const unsigned w = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)ya) |
+                       ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)yb) << 16);
+    *(unsigned*)(out_row + 2 * lane) = w;
+}
+
+// Split-key prefill for launches too small to fill the GPU (see prefill_key_splits): each row tile's key range is
+// cut into splits handled by separate workgroups, which write per-row partial states; a merge kernel then combines
+// each row's non-empty ones and applies the epilogue.
+// Key splits per row tile for a dense (B*H, N) prefill (1: the ordinary launch is the faster).
+int prefill_key_splits(int64_t BH, int64_t N, int causal);
+// The largest prefill_key_splits over both masks, which sizes the workspace.
+int prefill_key_splits_max(int64_t BH, int64_t N);
+// The dense bf16 prefill (d = 64, as launch_prefill_bf16_d64 with contiguous strides) through key splits: `part`
+// holds B*H*N*prefill_key_splits_max(B*H, N)*PARTIAL_FLOATS floats (unused when the plan is 1 split).
+hipError_t launch_prefill_split_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2,
+                                         const uint16_t* k2, const uint16_t* v, uint16_t* out, int64_t B, int64_t H,
+                                         int64_t N, int causal, Epilogue ep, float* part, hipStream_t stream);
+
 // Element strides of the backward's caller tensors, indexed q1, k1, q2, k2, v, dy, dq1, dk1, dq2, dk2, dv: batch,
 // head and row.  The feature dimension is contiguous.
 constexpr int BWD_TENSORS = 11;

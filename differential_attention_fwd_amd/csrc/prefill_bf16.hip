@@ -34,6 +34,9 @@
 // This translation unit is compiled with -fno-honor-nans: no NaN can arise (inputs are finite, masked scores are
 // -inf, the running offsets start at -FLT_MAX rather than -inf, and every processed row has a visible key in its
 // first tile), and it lets v_max3 run without quieting.
+#include <algorithm>
+#include <mutex>
+
 #include "launch.h"
 #include "tiles.h"
 
@@ -132,13 +135,39 @@ __device__ __forceinline__ float softmax_first(const f32x16& s, MapState& st, fl
     return exp_pack(s, st.ml, c, lo, hi);
 }
 
+// Key-split launches: the key tiles of a row tile are cut into ranges of kt_split tiles; a causal row tile reaches
+// only the ranges up to its diagonal, so it has fewer.  One workgroup per non-empty (row tile, head, range) item,
+// which writes each row's partial state for its range (PARTIAL_FLOATS in launch.h, row-major over (b, h, row, split))
+// instead of the output.  The grid holds no empty item, and items are ordered by the number of ranges their row tile
+// has, most first (the causal diagonal's and the last tile's being the longest runs), so that consecutive workgroups,
+// which the hardware deals out to the XCDs in turn, are alike in cost.
+struct KeySplit {
+    int splits, kt_split;
+    float* part;
+};
+
+// The first row tile of a causal launch that reaches range j - 1, i.e. has at least j ranges (j >= 1): row tile rt
+// < n_row_tiles - 1 spans (rt + 1) BM / BN key tiles, the last one all of them.
+__device__ __host__ inline int first_row_tile_with(int j, int kt_split, int n_row_tiles) {
+    const int64_t r = (int64_t)(j - 1) * kt_split * BN / BM;
+    return r < n_row_tiles - 1 ? (int)r : n_row_tiles - 1;
+}
+
+// Number of ranges of causal row tile rt.
+__device__ __host__ inline int ranges_of(int rt, int kt_split, int n_row_tiles, int key_tiles) {
+    const int kend = rt == n_row_tiles - 1 ? key_tiles : (rt + 1) * (BM / BN);
+    return (kend + kt_split - 1) / kt_split;
+}
+
 // SAVE: also write each row's training statistics (SAVED_* in launch.h) for the backward pass.
-template <bool SAVE>
+// SPLIT: cover one key range of the row tile and write partial states (KeySplit).
+template <bool SAVE, bool SPLIT>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1,
                              const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
                              const uint16_t* __restrict__ gv, uint16_t* __restrict__ gout, int BH, int H, int N,
-                             int n_row_tiles, int causal, Strides st, Epilogue ep, float* __restrict__ saved) {
+                             int n_row_tiles, int causal, Strides st, Epilogue ep, float* __restrict__ saved,
+                             KeySplit ks) {
     __shared__ __attribute__((aligned(16))) unsigned char kr0[K_SLOT_BYTES], kr1[K_SLOT_BYTES], kr2[K_SLOT_BYTES],
         kr3[K_SLOT_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char vr0[V_TILE_BYTES], vr1[V_TILE_BYTES], vr2[V_TILE_BYTES],
@@ -151,9 +180,28 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     const int l32 = lane & 31;   // this lane's query row inside the wave
 
     // Heaviest row tiles first under the causal mask (their key range is longest).
-    const int bid = blockIdx.x;
-    const int rt = causal ? (n_row_tiles - 1 - bid / BH) : bid / BH;
-    const int bh = bid % BH;
+    int rt, bh, sp = 0;
+    if constexpr (SPLIT) {
+        // Groups of row tiles with j ranges, j = splits down to 1; inside a group row tiles descend, then heads,
+        // then ranges.  Every launched workgroup falls in some group (the host sized the grid as their sum).
+        int rem = (int)blockIdx.x, j = ks.splits, hi = n_row_tiles;
+        if (causal) {
+            for (; j > 1; --j) {
+                const int lo = first_row_tile_with(j, ks.kt_split, n_row_tiles);
+                const int cnt = (hi - lo) * BH * j;
+                if (rem < cnt) break;
+                rem -= cnt;
+                hi = lo;
+            }
+        }
+        rt = hi - 1 - rem / (BH * j);
+        bh = rem % (BH * j) / j;
+        sp = rem % j;
+    } else {
+        const int bid = (int)blockIdx.x;
+        rt = causal ? (n_row_tiles - 1 - bid / BH) : bid / BH;
+        bh = bid % BH;
+    }
     const int q0 = rt * BM;
     const int q0w = q0 + wave * 32;
 
@@ -186,7 +234,9 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
 
     const int q_last = min(N, q0 + BM) - 1;
     const int n_tiles = causal ? (q_last / BN + 1) : (N + BN - 1) / BN;
-
+    // Key tiles of this workgroup: all of the row tile's, or one split's share.
+    const int kt0 = SPLIT ? sp * ks.kt_split : 0;
+    const int kt_end = SPLIT ? min(n_tiles, kt0 + ks.kt_split) : n_tiles;
     // Direct loads: each wave moves one 1 KiB piece per tile and tensor role.  K1 and K2 tiles (4 KiB each) are 8
     // pieces, the V tile (8 KiB) another 8; piece x of a tile covers its bytes [1024 x, 1024 x + 1024) and lane L
     // writes position 16 L of it.  Loads are issued unconditionally, also for tiles past the end: those buffer loads
@@ -269,12 +319,12 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     // into the slot that tile t - 1 left (every wave has passed the barrier after reading it), and computes tile t.
     // At its end it waits for everything but the loads of this iteration and the previous one, so tile t + 1 has
     // landed and a load has two whole iterations to land.
-    issue_k(Slot<0>{}, 0);
-    issue_v(Slot<0>{}, 0);
-    issue_k(Slot<1>{}, 1);
-    issue_v(Slot<1>{}, 1);
-    issue_k(Slot<2>{}, 2);
-    issue_v(Slot<2>{}, 2);
+    issue_k(Slot<0>{}, kt0);
+    issue_v(Slot<0>{}, kt0);
+    issue_k(Slot<1>{}, kt0 + 1);
+    issue_v(Slot<1>{}, kt0 + 1);
+    issue_k(Slot<2>{}, kt0 + 2);
+    issue_v(Slot<2>{}, kt0 + 2);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * (K_PIECES_PER_WAVE + V_PIECES_PER_WAVE)));
     lds_barrier();
     // Two transposing reads make one V^T fragment (the 8 keys of one accumulator position block).
@@ -345,15 +395,40 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * (K_PIECES_PER_WAVE + V_PIECES_PER_WAVE)));
         lds_barrier();
     };
-    step(Slot<0>{}, Flag<true>{}, 0);
-    for (int t = 1; t < n_tiles; t += 4) {
+    // A split's first tile may hide every key from some rows, so it takes the general path (which keeps such rows'
+    // states empty without NaN); a whole row tile's first tile shows every row its first key.
+    step(Slot<0>{}, Flag<!SPLIT>{}, kt0);
+    for (int t = kt0 + 1; t < kt_end; t += 4) {
         step(Slot<1>{}, Flag<false>{}, t);
-        if (t + 1 < n_tiles) step(Slot<2>{}, Flag<false>{}, t + 1);
-        if (t + 2 < n_tiles) step(Slot<3>{}, Flag<false>{}, t + 2);
-        if (t + 3 < n_tiles) step(Slot<0>{}, Flag<false>{}, t + 3);
+        if (t + 1 < kt_end) step(Slot<2>{}, Flag<false>{}, t + 1);
+        if (t + 2 < kt_end) step(Slot<3>{}, Flag<false>{}, t + 2);
+        if (t + 3 < kt_end) step(Slot<0>{}, Flag<false>{}, t + 3);
     }
     // Drain the trailing prefetches before the workgroup can retire (their LDS writes must not outlive it).
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+
+    if constexpr (SPLIT) {
+        // Partial state of each row for this key range: offsets (log2 units of the scaled scores), sums at those
+        // offsets (l = 0 and offset -inf for a row that saw no key here), unnormalised O1 and O2.
+        const float l1 = pair_sum(st1.l), l2 = pair_sum(st2.l);
+        const int q = q0w + l32;
+        if (q < N) {
+            float* dst = ks.part + ((size_t)bh * N + q) * ks.splits * PARTIAL_FLOATS + (size_t)sp * PARTIAL_FLOATS;
+            if (h == 0)
+                *(f32x4*)dst = f32x4{l1 > 0.f ? st1.ml : -INFINITY, l1, l2 > 0.f ? st2.ml : -INFINITY, l2};
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int ch = cb * 32 + 8 * g4 + 4 * h;
+                    *(f32x4*)(dst + 4 + ch) = f32x4{o1[cb][4 * g4], o1[cb][4 * g4 + 1], o1[cb][4 * g4 + 2],
+                                                    o1[cb][4 * g4 + 3]};
+                    *(f32x4*)(dst + 4 + DV + ch) = f32x4{o2[cb][4 * g4], o2[cb][4 * g4 + 1], o2[cb][4 * g4 + 2],
+                                                         o2[cb][4 * g4 + 3]};
+                }
+        }
+        return;
+    }
 
     // Epilogue: lane owns query row q0w + l32 and channels cb*32 + 8*(i/4) + 4h + i%4.
     const float l1 = pair_sum(st1.l);
@@ -420,6 +495,33 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
     }
 }
 
+// One wave per query row, four rows per workgroup: the row's non-empty ranges merged (merge_partial_row) into the
+// dense [BH][N][DV] output.
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
+                                                            int BH, int N, int causal, int splits, int kt_split,
+                                                            int n_row_tiles, Epilogue ep) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (int64_t)BH * N) return;
+    const int q = (int)(row % N);
+    const int n = causal ? ranges_of(q / BM, kt_split, n_row_tiles, (N + BN - 1) / BN) : splits;
+    merge_partial_row(part + row * splits * PARTIAL_FLOATS, n, ep, (int)(row / N), out + row * DV,
+                      (int)(threadIdx.x & 63));
+}
+
+// Workgroups of a split launch: the non-empty (row tile, head, range) items, counted by group as the kernel walks
+// them.
+int64_t split_items(int64_t BH, int n_row_tiles, int splits, int kt_split, int causal) {
+    if (!causal) return (int64_t)n_row_tiles * BH * splits;
+    int64_t n = 0;
+    int hi = n_row_tiles;
+    for (int j = splits; j >= 1; --j) {
+        const int lo = j > 1 ? first_row_tile_with(j, kt_split, n_row_tiles) : 0;
+        n += (int64_t)(hi - lo) * BH * j;
+        hi = lo;
+    }
+    return n;
+}
+
 }  // namespace
 
 hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
@@ -429,12 +531,129 @@ hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const
     const int n_row_tiles = (int)((N + BM - 1) / BM);
     const int64_t blocks = (int64_t)n_row_tiles * BH;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const KeySplit none{1, 0, nullptr};
     if (saved)
-        hipLaunchKernelGGL(prefill_bf16_d64_kernel<true>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1,
-                           q2, k2, v, out, (int)BH, (int)H, (int)N, n_row_tiles, causal ? 1 : 0, st, ep, saved);
+        hipLaunchKernelGGL((prefill_bf16_d64_kernel<true, false>), dim3((unsigned)blocks), dim3(THREADS), 0, stream,
+                           q1, k1, q2, k2, v, out, (int)BH, (int)H, (int)N, n_row_tiles, causal ? 1 : 0, st, ep, saved,
+                           none);
     else
-        hipLaunchKernelGGL(prefill_bf16_d64_kernel<false>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1,
-                           q2, k2, v, out, (int)BH, (int)H, (int)N, n_row_tiles, causal ? 1 : 0, st, ep, saved);
+        hipLaunchKernelGGL((prefill_bf16_d64_kernel<false, false>), dim3((unsigned)blocks), dim3(THREADS), 0, stream,
+                           q1, k1, q2, k2, v, out, (int)BH, (int)H, (int)N, n_row_tiles, causal ? 1 : 0, st, ep, saved,
+                           none);
+    return hipGetLastError();
+}
+
+namespace {
+
+constexpr int SPLIT_SLOTS = 512;        // workgroup slots of the GPU for this kernel: two per CU, 256 CUs
+constexpr int SPLIT_MAX_ITEMS = 1024;   // plans with more items than this are not considered
+
+// Modelled time (us) of a split launch with s ranges of kt key tiles and n items, fitted to measured times of
+// forced split counts on this GPU (causal and not, B*H 1..32, N 512..32768; rms error 7.5%).  Items go to the slots
+// in grid order, each to the slot that frees first (greedy list scheduling, as the dispatcher does).  An item costs
+// 7.2 us (prologue, epilogue) plus, per key tile, max(0.76 us, r * 16 KiB / 6.7 TB/s) with r = min(n, slots) items
+// running: the tile's compute, or every running item's K and V tile at the rate the caches and HBM sustain.  With
+// s > 1 the merge adds 8.8 us plus the item's 128 rows of 1040-byte states read at 3.3 TB/s.
+double split_plan_us(int64_t BH, int R, int K, int s, int kt, int causal, int64_t n) {
+    const double tile_us = fmax(0.76, (double)(n < SPLIT_SLOTS ? n : SPLIT_SLOTS) * 16384.0 / 6.7e6);
+    double slot[SPLIT_SLOTS] = {};   // min-heap of the slots' free times
+    const auto later = [](double a, double b) { return a > b; };
+    double end = 0.0;
+    auto run = [&](int tiles, int64_t count) {
+        const double cost = 7.2 + tiles * tile_us;
+        for (int64_t c = 0; c < count; ++c) {
+            std::pop_heap(slot, slot + SPLIT_SLOTS, later);
+            slot[SPLIT_SLOTS - 1] += cost;
+            end = fmax(end, slot[SPLIT_SLOTS - 1]);
+            std::push_heap(slot, slot + SPLIT_SLOTS, later);
+        }
+    };
+    int hi = R;
+    for (int j = s; j >= 1; --j) {   // the kernel's item order (one group of all row tiles when not causal)
+        const int lo = !causal ? 0 : j > 1 ? first_row_tile_with(j, kt, R) : 0;
+        for (int rt = hi - 1; rt >= lo; --rt) {
+            const int kend = !causal || rt == R - 1 ? K : (rt + 1) * (BM / BN);
+            for (int64_t bh = 0; bh < BH; ++bh)
+                for (int sp = 0; sp < j; ++sp) run(min(kend, (sp + 1) * kt) - sp * kt, 1);
+        }
+        hi = lo;
+        if (!causal) break;
+    }
+    if (s > 1) end += 8.8 + (double)n * BM * 1040.0 / 3.3e6;
+    return end;
+}
+
+int plan_key_splits(int64_t BH, int64_t N, int causal) {
+    const int64_t rows = (N + BM - 1) / BM;
+    const int R = (int)rows, K = (int)((N + BN - 1) / BN);
+    int best = 1, last = 1;
+    double best_t = split_plan_us(BH, R, K, 1, K, causal, rows * BH);
+    for (int s0 = 2; s0 <= 16 && s0 <= K; ++s0) {
+        const int kt = (K + s0 - 1) / s0, s = (K + kt - 1) / kt;   // as many splits as that share of key tiles needs
+        if (s == last) continue;
+        last = s;
+        const int64_t n = split_items(BH, R, s, kt, causal);
+        if (n > SPLIT_MAX_ITEMS) continue;
+        const double t = split_plan_us(BH, R, K, s, kt, causal, n);
+        if (t < best_t) {
+            best_t = t;
+            best = s;
+        }
+    }
+    return best;
+}
+
+}  // namespace
+
+// Key splits per row tile: the plan of least modelled time (split_plan_us) among 1..16 splits.  Launches whose row
+// tiles alone fill the slots take 1.  The plan picked was within 15% of the fastest measured in every case measured
+// (3.9% on average).  Plans are kept for the last few shapes, as the model takes up to a few hundred microseconds.
+int prefill_key_splits(int64_t BH, int64_t N, int causal) {
+    if (BH <= 0 || N <= 0 || BH * ((N + BM - 1) / BM) >= SPLIT_SLOTS) return 1;
+    struct Plan {
+        int64_t BH, N;
+        int causal, splits;
+    };
+    static std::mutex mu;
+    static Plan kept[16];
+    static int kept_n = 0, next = 0;
+    causal = causal ? 1 : 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < kept_n; ++i)
+            if (kept[i].BH == BH && kept[i].N == N && kept[i].causal == causal) return kept[i].splits;
+    }
+    const int splits = plan_key_splits(BH, N, causal);
+    std::lock_guard<std::mutex> lock(mu);
+    kept[next] = Plan{BH, N, causal, splits};
+    next = (next + 1) % 16;
+    kept_n = kept_n < 16 ? kept_n + 1 : 16;
+    return splits;
+}
+
+int prefill_key_splits_max(int64_t BH, int64_t N) {
+    const int a = prefill_key_splits(BH, N, 0), b = prefill_key_splits(BH, N, 1);
+    return a > b ? a : b;
+}
+
+hipError_t launch_prefill_split_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2,
+                                         const uint16_t* k2, const uint16_t* v, uint16_t* out, int64_t B, int64_t H,
+                                         int64_t N, int causal, Epilogue ep, float* part, hipStream_t stream) {
+    const int64_t BH = B * H;
+    const int splits = prefill_key_splits(BH, N, causal);
+    const Strides st = contiguous_strides(H, N, D);
+    if (splits <= 1) return launch_prefill_bf16_d64(q1, k1, q2, k2, v, out, B, H, N, causal, st, ep, nullptr, stream);
+    const int n_row_tiles = (int)((N + BM - 1) / BM);
+    const int key_tiles = (int)((N + BN - 1) / BN);
+    const KeySplit ks{splits, (key_tiles + splits - 1) / splits, part};
+    const int64_t blocks = split_items(BH, n_row_tiles, splits, ks.kt_split, causal);
+    if (blocks > 0x7fffffff || BH * N > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_bf16_d64_kernel<false, true>), dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1,
+                       k1, q2, k2, v, out, (int)BH, (int)H, (int)N, n_row_tiles, causal ? 1 : 0, st, ep, nullptr, ks);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prefill_merge_kernel, dim3((unsigned)((BH * N + 3) / 4)), dim3(256), 0, stream,
+                       (const float*)part, out, (int)BH, (int)N, causal ? 1 : 0, splits, ks.kt_split, n_row_tiles, ep);
     return hipGetLastError();
 }
 

@@ -53,7 +53,7 @@ enum diffattn_status {
     DIFFATTN_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
     DIFFATTN_ERR_LAYER = -5,       /* layer < 0 */
     DIFFATTN_ERR_LAMBDA = -6,      /* lambda is NaN or infinite */
-    DIFFATTN_ERR_WORKSPACE = -7,   /* decode workspace NULL or smaller than diffattn_decode_workspace_bytes() */
+    DIFFATTN_ERR_WORKSPACE = -7,   /* workspace NULL or smaller than the entry point's *_workspace_bytes() */
     DIFFATTN_ERR_ALIAS = -8,       /* out or workspace overlaps an input (or each other) */
     DIFFATTN_ERR_HIP = -9          /* the HIP runtime reported an error at launch */
 };
@@ -132,6 +132,29 @@ int diffattn_decode_heads(const void *q1, const void *k1, const void *q2, const 
 int diffattn_fwd_strided(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
                          int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda, const float *lambda_heads,
                          int layer, int causal, const int64_t *strides, void *stream);
+
+/*
+ * Split-key prefill (bf16, d = 64, dense tensors as for diffattn_fwd): the same operation ([U] worked example and
+ * the paragraph after it) for launches whose B * H * ceil(N / 128) row tiles are too few to fill the GPU (fewer
+ * than 512 workgroup slots: few heads, or long rows with one or two heads).  The key range of every row tile is cut
+ * into up to 16 ranges handled by separate workgroups (a causal row tile only has the ranges up to its diagonal);
+ * each writes its rows' partial softmax states (per map: offset, sum and unnormalised output) to `workspace`, and a
+ * second kernel merges each row's states by log-sum-exp and applies the epilogue, as the split decode does.  The
+ * split count is the one of least modelled time (the longest range's key loop, memory traffic of the running
+ * workgroups and the merge's reads, fitted to measured launches), and may be 1.  The result equals diffattn_fwd's
+ * up to rounding (the sums are taken in another order), not bit for bit.
+ *   diffattn_fwd_split_workspace_bytes: bytes of workspace the call needs: B*H*N*splits*1040 with the larger
+ *     split count of the causal and the non-causal plan, or 0 when neither splits (then the call runs
+ *     diffattn_fwd's kernel and reads no workspace) or the shape is unsupported.
+ *   workspace: device, 16-byte aligned, >= that size, overlapping no input or out (contents on entry ignored; the
+ *     call leaves partial states in it).  Calls that overlap in time must use different workspaces.
+ *   Errors as for diffattn_fwd; dtype other than bf16 or d != 64 -> DIFFATTN_ERR_UNSUPPORTED; a missing or small
+ *   workspace -> DIFFATTN_ERR_WORKSPACE; a workspace overlapping a tensor -> DIFFATTN_ERR_ALIAS.
+ */
+size_t diffattn_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int d);
+int diffattn_fwd_split(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
+                       int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda, int layer, int causal,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Variable-length and multi-token decode (bf16, d = 64).  Each sequence b has a cache of lens[b] valid rows in a

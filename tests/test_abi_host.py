@@ -162,6 +162,47 @@ def test_lambda_heads_4_byte_alignment_is_enough(lib):
     assert fwd_heads(lib, lh=A[7] + 4, out=A[7]) == E_ALIAS
 
 
+# B1 H2 N1000 takes 8 key splits (causal), so its calls need a workspace.
+def fwd_split(lib, ws=A[6], ws_bytes=None, out=A[5], B=1, H=2, N=1000, d=64, dtype=BF16, lam=0.5, layer=1):
+    if ws_bytes is None:
+        ws_bytes = lib.diffattn_fwd_split_workspace_bytes(B, H, N, d)
+    return lib.diffattn_fwd_split(A[0], A[1], A[2], A[3], A[4], out, B, H, N, d, dtype, lam, layer, 1, ws, ws_bytes,
+                                  None)
+
+
+def test_fwd_split_workspace_sizes(lib):
+    # The plan (least modelled time among 1..16 splits) for the larger of the two masks sizes the workspace: 1040
+    # bytes of partial state per row and split.  B1 H8 N1024: 4 splits causal, 1 not.
+    assert lib.diffattn_fwd_split_workspace_bytes(1, 8, 1024, 64) == 8 * 1024 * 4 * 1040
+    # B1 H1 N8192: 9 splits causal (29 key tiles each), 5 not
+    assert lib.diffattn_fwd_split_workspace_bytes(1, 1, 8192, 64) == 8192 * 9 * 1040
+    # B1 H1 N2049: 11 splits either way
+    assert lib.diffattn_fwd_split_workspace_bytes(1, 1, 2049, 64) == 2049 * 11 * 1040
+    # B1 H2 N64: too little work to gain from a merge -> no split, no workspace
+    assert lib.diffattn_fwd_split_workspace_bytes(1, 2, 64, 64) == 0
+    # B2 H8 N2048 (256 row tiles): splitting is modelled slower
+    assert lib.diffattn_fwd_split_workspace_bytes(2, 8, 2048, 64) == 0
+    # row tiles fill the 512 workgroup slots (B8 H8 N1024, B4 H12 N4096) -> no split; N <= 32: one key tile
+    assert lib.diffattn_fwd_split_workspace_bytes(8, 8, 1024, 64) == 0
+    assert lib.diffattn_fwd_split_workspace_bytes(4, 12, 4096, 64) == 0
+    assert lib.diffattn_fwd_split_workspace_bytes(1, 1, 32, 64) == 0
+    for bad in ((1, 1, 64, 8), (-1, 1, 64, 64), (1, 1, (1 << 23) + 1, 64)):
+        assert lib.diffattn_fwd_split_workspace_bytes(*bad) == 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(), OK), (dict(ws=None), E_WS), (dict(ws_bytes=1024), E_WS), (dict(ws=A[6] + 8), E_ALIGN),
+    (dict(ws=A[4]), E_ALIAS), (dict(ws=A[5] - 64), E_ALIAS), (dict(out=A[0] + 128), E_ALIAS),
+    (dict(dtype=F32), E_UNSUP), (dict(d=8), E_UNSUP), (dict(N=0), OK), (dict(B=-1), E_SHAPE),
+    (dict(layer=-1), E_LAYER), (dict(lam=float("nan")), E_LAMBDA),
+    (dict(B=4, H=12, N=4096, ws=None, ws_bytes=0), OK),   # fills the GPU without splits: no workspace needed
+])
+def test_fwd_split_validation(lib, case, expect):
+    if expect == OK and case.get("N", 1) != 0:
+        pytest.skip("valid calls would launch kernels (no GPU here)")
+    assert fwd_split(lib, **case) == expect
+
+
 def fwd_train(lib, saved=A[6], saved_bytes=None, out=A[5], B=1, H=2, N=64, d=64, dtype=BF16, lam=0.5, lh=None,
               layer=1):
     if saved_bytes is None:

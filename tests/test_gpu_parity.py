@@ -18,6 +18,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("gpu")]
 F32_TOL = 1e-5
 BF16_MAX, BF16_MEAN = 2e-2, 2e-3
 RAW_MAX, RAW_MEAN = BF16_MAX / 0.8, BF16_MEAN / 0.8   # raw outputs, relative to each row's RMS (see check_bf16)
+BOUNDS = (BF16_MAX, BF16_MEAN, RAW_MAX, RAW_MEAN)
 
 
 def torch_mod():
@@ -56,11 +57,13 @@ def lam_of(spec):
     return float(np.float32(spec))
 
 
-def check_bf16(got, ref, what, raw=False):
+def check_bf16(got, ref, what, raw=False, scale=1.0):
     """bf16 bounds.  Normalised outputs: absolute.  Raw (layer 0) outputs: every row against its own RMS, as the
     layer-1 normalisation (RMS norm, then the scale 1 - lambda_init(1) = 0.8) would see it, so the normalised bounds
     become 2e-2 / 0.8 and 2e-3 / 0.8 relative to the row's RMS (rows whose RMS is below 1e-3 of the tensor's are
-    measured against that floor)."""
+    measured against that floor).  `scale` multiplies every bound: 2 when two results that each meet the bounds
+    against the exact values are compared with one another."""
+    BF16_MAX, BF16_MEAN, RAW_MAX, RAW_MEAN = (scale * b for b in BOUNDS)
     got = np.asarray(got, dtype=np.float64)
     err = np.abs(got - ref)
     assert np.isfinite(got).all(), what
@@ -179,6 +182,49 @@ def test_prefill_n65536_sampled():
     ref = oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam, c["layer"], True, rows=rows)
     sub = got.reshape(B * H * N, 2 * d)[rows]
     check_bf16(sub, ref, "prefill N65536 sampled")
+
+
+@pytest.mark.parametrize("B,H,N,causal,layer", [
+    (1, 8, 1024, True, 1),     # the small benchmarked prefill: 4 key splits per row tile
+    (1, 2, 1000, True, 0),     # 8 splits of 128 keys, ragged tail
+    (2, 1, 1000, False, 2),    # not causal: every row tile has all 8 splits
+    (1, 3, 4097, True, 1),     # 5 splits of 832 keys: split boundaries inside row tiles, a one-row tail
+    (1, 1, 1500, False, 3),
+    (1, 4, 777, True, 2),      # 7 splits of 128 keys
+    (1, 1, 2049, True, 0),     # 11 splits of 192 keys
+    (1, 1, 8192, True, 2),     # one head: 9 splits
+])
+def test_prefill_split_vs_oracle(B, H, N, causal, layer):
+    """Split-key prefill (diffattn_fwd_split): row tiles whose keys are split across workgroups, including causal
+    rows that see no key of a split inside their row tile, merged by log-sum-exp; against the oracle, and against
+    diffattn_fwd (the parts are summed in another order)."""
+    torch = torch_mod()
+    assert da.diffattn_fwd_split_workspace_bytes(B, H, N, 64) > 0   # the case really splits
+    inp = di.prefill_bf16(B, H, N, 64, seed=1100 + N)
+    say(f"case: prefill split B{B} H{H} N{N} causal={causal} layer={layer}")
+    lam = float(np.float32(0.8 if layer == 0 else oracle.lambda_init(layer)))
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    got = da.diffattn_fwd_split(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], lam, layer, causal)
+    full = da.diffattn_fwd(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], lam, layer, causal)
+    torch.cuda.synchronize()
+    f = widen(inp)
+    ref = oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam, layer, causal)
+    check_bf16(host_bf16(got), ref, f"prefill split N{N}", raw=layer == 0)
+    # Both meet the bounds against the exact values, so they are within twice the bounds of each other.
+    check_bf16(host_bf16(got), host_bf16(full), f"prefill split N{N} vs diffattn_fwd", raw=layer == 0, scale=2.0)
+
+
+def test_prefill_split_without_split_is_fwd():
+    """When the query tiles fill the GPU the split entry point runs diffattn_fwd's kernel: identical bits."""
+    torch = torch_mod()
+    B, H, N = 4, 12, 4096
+    assert da.diffattn_fwd_split_workspace_bytes(B, H, N, 64) == 0
+    inp = {k: dev_bf16(v) for k, v in di.prefill_bf16(B, H, N, 64, seed=1200).items()}
+    lam = float(np.float32(oracle.lambda_init(12)))
+    a = da.diffattn_fwd_split(inp["q1"], inp["k1"], inp["q2"], inp["k2"], inp["v"], lam, 12, True)
+    b = da.diffattn_fwd(inp["q1"], inp["k1"], inp["q2"], inp["k2"], inp["v"], lam, 12, True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 @pytest.mark.parametrize("B,H,N,causal,layer", [
