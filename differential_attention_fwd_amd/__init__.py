@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
     L.diffattn_fwd_strided.restype = c_int
     L.diffattn_fwd_split_workspace_bytes.argtypes = [i64, i64, i64, c_int]
     L.diffattn_fwd_split_workspace_bytes.restype = ctypes.c_size_t
-    L.diffattn_fwd_split.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, c_int, c_int, P,
+    L.diffattn_fwd_split.argtypes = [P, P, P, P, P, P, i64, i64, i64, c_int, c_int, c_float, P, c_int, c_int, P,
                                      ctypes.c_size_t, P]
     L.diffattn_fwd_split.restype = c_int
     L.diffattn_decode_varlen_workspace_bytes.argtypes = [i64, i64, i64, i64, c_int]
@@ -161,11 +161,10 @@ def diffattn_fwd_split_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(lib().diffattn_fwd_split_workspace_bytes(int(B), int(H), int(N), int(d)))
 
 
-def diffattn_fwd_split(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool, out=None, workspace=None,
-                       stream=None):
+def diffattn_fwd_split(q1, k1, q2, k2, v, lam, layer: int, causal: bool, out=None, workspace=None, stream=None):
     """Split-key prefill (bf16, d = 64, dense): diffattn_fwd's result up to rounding, for launches too small to fill
-    the GPU.  `workspace`: a GPU tensor of at least diffattn_fwd_split_workspace_bytes(B, H, N, d) bytes (allocated
-    here if None)."""
+    the GPU.  lam: a number, or a float32 GPU tensor of shape (H,) holding one lambda per head.  `workspace`: a GPU
+    tensor of at least diffattn_fwd_split_workspace_bytes(B, H, N, d) bytes (allocated here if None)."""
     import torch
     _check_tensors((q1, k1, q2, k2, v))
     B, H, N, d = q1.shape
@@ -179,8 +178,9 @@ def diffattn_fwd_split(q1, k1, q2, k2, v, lam: float, layer: int, causal: bool, 
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
     _check_tensors((workspace,))
+    lam_f, lam_p = _lambda_args(lam, H, q1.device)
     st = lib().diffattn_fwd_split(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(),
-                                  out.data_ptr(), B, H, N, d, _dtype_code(q1), float(lam), int(layer),
+                                  out.data_ptr(), B, H, N, d, _dtype_code(q1), lam_f, lam_p, int(layer),
                                   int(bool(causal)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                   _stream_handle(stream, q1.device))
     if st != 0:

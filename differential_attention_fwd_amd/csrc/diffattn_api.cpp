@@ -242,14 +242,14 @@ size_t diffattn_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int d
 }
 
 int diffattn_fwd_split(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, void* out,
-                       int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda, int layer, int causal,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda, const float* lambda_heads,
+                       int layer, int causal, void* workspace, size_t workspace_bytes, void* stream) {
     if (B < 0 || H < 0 || N < 0 || N > DIFFATTN_MAX_LEN) return DIFFATTN_ERR_SHAPE;
     int st = check_dtype_d(dtype, d);
     if (st) return st;
     if (dtype != DIFFATTN_BF16 || d != 64) return DIFFATTN_ERR_UNSUPPORTED;
     Epilogue ep;
-    st = make_epilogue(lambda, layer, &ep);
+    st = make_epilogue(lambda_heads ? 0.0f : lambda, layer, &ep);
     if (st) return st;
     int64_t BH, rows, qk_elems, v_elems;
     if (!mul_ok(B, H, &BH) || BH > INT32_MAX || !mul_ok(BH, N, &rows) || rows > INT32_MAX ||
@@ -266,6 +266,12 @@ int diffattn_fwd_split(const void* q1, const void* k1, const void* q2, const voi
                          {(uintptr_t)v, (uintptr_t)v + v_bytes}};
     for (const Span& s : ins)
         if (overlaps(o, s)) return DIFFATTN_ERR_ALIAS;
+    if (lambda_heads) {
+        st = check_lambda_heads(lambda_heads, H, o);
+        if (st) return st;
+        ep.lambda_heads = lambda_heads;
+        ep.heads = (int)H;
+    }
     const size_t need = diffattn_fwd_split_workspace_bytes(B, H, N, d);
     if (need > 0) {
         if (!workspace) return DIFFATTN_ERR_WORKSPACE;
@@ -275,6 +281,9 @@ int diffattn_fwd_split(const void* q1, const void* k1, const void* q2, const voi
         if (overlaps(w, o)) return DIFFATTN_ERR_ALIAS;
         for (const Span& s : ins)
             if (overlaps(w, s)) return DIFFATTN_ERR_ALIAS;
+        if (lambda_heads &&
+            overlaps(w, Span{(uintptr_t)lambda_heads, (uintptr_t)lambda_heads + (size_t)H * sizeof(float)}))
+            return DIFFATTN_ERR_ALIAS;
     }
     return hip_status(diffattn::launch_prefill_split_bf16_d64(
         (const uint16_t*)q1, (const uint16_t*)k1, (const uint16_t*)q2, (const uint16_t*)k2, (const uint16_t*)v,

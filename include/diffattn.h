@@ -146,6 +146,8 @@ int diffattn_fwd_strided(const void *q1, const void *k1, const void *q2, const v
  *   diffattn_fwd_split_workspace_bytes: bytes of workspace the call needs: B*H*N*splits*1040 with the larger
  *     split count of the causal and the non-causal plan, or 0 when neither splits (then the call runs
  *     diffattn_fwd's kernel and reads no workspace) or the shape is unsupported.
+ *   lambda / lambda_heads: as for diffattn_fwd_strided (lambda_heads NULL = one lambda for all heads; it must
+ *     not overlap out or the workspace).
  *   workspace: device, 16-byte aligned, >= that size, overlapping no input or out (contents on entry ignored; the
  *     call leaves partial states in it).  Calls that overlap in time must use different workspaces.
  *   Errors as for diffattn_fwd; dtype other than bf16 or d != 64 -> DIFFATTN_ERR_UNSUPPORTED; a missing or small
@@ -153,8 +155,8 @@ int diffattn_fwd_strided(const void *q1, const void *k1, const void *q2, const v
  */
 size_t diffattn_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int d);
 int diffattn_fwd_split(const void *q1, const void *k1, const void *q2, const void *k2, const void *v, void *out,
-                       int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda, int layer, int causal,
-                       void *workspace, size_t workspace_bytes, void *stream);
+                       int64_t B, int64_t H, int64_t N, int d, int dtype, float lambda, const float *lambda_heads,
+                       int layer, int causal, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Variable-length and multi-token decode (bf16, d = 64).  Each sequence b has a cache of lens[b] valid rows in a

@@ -163,11 +163,12 @@ def test_lambda_heads_4_byte_alignment_is_enough(lib):
 
 
 # B1 H2 N1000 takes 8 key splits (causal), so its calls need a workspace.
-def fwd_split(lib, ws=A[6], ws_bytes=None, out=A[5], B=1, H=2, N=1000, d=64, dtype=BF16, lam=0.5, layer=1):
+def fwd_split(lib, ws=A[6], ws_bytes=None, out=A[5], B=1, H=2, N=1000, d=64, dtype=BF16, lam=0.5, lh=None,
+              layer=1):
     if ws_bytes is None:
         ws_bytes = lib.diffattn_fwd_split_workspace_bytes(B, H, N, d)
-    return lib.diffattn_fwd_split(A[0], A[1], A[2], A[3], A[4], out, B, H, N, d, dtype, lam, layer, 1, ws, ws_bytes,
-                                  None)
+    return lib.diffattn_fwd_split(A[0], A[1], A[2], A[3], A[4], out, B, H, N, d, dtype, lam, lh, layer, 1, ws,
+                                  ws_bytes, None)
 
 
 def test_fwd_split_workspace_sizes(lib):
@@ -196,6 +197,8 @@ def test_fwd_split_workspace_sizes(lib):
     (dict(dtype=F32), E_UNSUP), (dict(d=8), E_UNSUP), (dict(N=0), OK), (dict(B=-1), E_SHAPE),
     (dict(layer=-1), E_LAYER), (dict(lam=float("nan")), E_LAMBDA),
     (dict(B=4, H=12, N=4096, ws=None, ws_bytes=0), OK),   # fills the GPU without splits: no workspace needed
+    (dict(lh=A[7] + 2), E_ALIGN), (dict(lh=A[5] + 4), E_ALIAS), (dict(lh=A[6] + 64), E_ALIAS),   # lambda per head
+    (dict(lh=A[7], lam=float("nan"), out=A[0] + 128), E_ALIAS),   # lambda_heads: the scalar lambda is not checked
 ])
 def test_fwd_split_validation(lib, case, expect):
     if expect == OK and case.get("N", 1) != 0:

@@ -448,6 +448,22 @@ def test_prefill_bf16_lambda_per_head(N, causal, layer):
     check_bf16(host_bf16(out), ref, f"prefill per-head N{N}", raw=layer == 0)
 
 
+@pytest.mark.parametrize("N,causal,layer", [(1000, True, 2), (777, False, 0)])
+def test_prefill_split_lambda_per_head(N, causal, layer):
+    """diffattn_fwd_split with one lambda per head (B1 H3: 8 or 5 key splits), against the oracle."""
+    torch = torch_mod()
+    inp = di.prefill_bf16(1, 3, N, 64, seed=420 + N)
+    assert da.diffattn_fwd_split_workspace_bytes(1, 3, N, 64) > 0
+    say(f"case: prefill split per-head lambda B1 H3 N{N} causal={causal} layer={layer}")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    out = da.diffattn_fwd_split(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], dev_lam(LAM_HEADS), layer,
+                                causal)
+    torch.cuda.synchronize()
+    f = widen(inp)
+    ref = oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], LAM_HEADS.astype(np.float64), layer, causal)
+    check_bf16(host_bf16(out), ref, f"prefill split per-head N{N}", raw=layer == 0)
+
+
 def test_f32_lambda_per_head():
     torch = torch_mod()
     inp = di.prefill_f32(2, 3, 37, 8, seed=410)
