@@ -270,6 +270,29 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
                       (int)threadIdx.x);
 }
 
+// First level of the merge for many splits: wave (item, g) merges splits [g group, (g + 1) group) of its item
+// (item = bh * T + t) into one state at ws2[item][g]; decode_merge_kernel then merges the groups' states.
+__global__ __launch_bounds__(64) void decode_merge_groups_kernel(const float* __restrict__ ws, float* __restrict__ ws2,
+                                                                 int splits, int group, int groups) {
+    const int64_t item = blockIdx.x / groups;
+    const int g = (int)(blockIdx.x % groups);
+    const int s0 = g * group;
+    merge_partial_state(ws + (item * splits + s0) * PART_FLOATS, min(group, splits - s0),
+                        ws2 + (item * groups + g) * PART_FLOATS, (int)threadIdx.x);
+}
+
+// Splits per item merged by one wave in one pass; beyond that, two levels of about sqrt(splits) states each.
+constexpr int MERGE_DIRECT_MAX = 32;
+struct MergePlan {
+    int group, groups;   // splits per first-level group, groups per item (1: a single merge pass)
+};
+MergePlan merge_plan(int splits) {
+    if (splits <= MERGE_DIRECT_MAX) return MergePlan{splits, 1};
+    int g = 1;
+    while (g * g < splits) ++g;
+    return MergePlan{g, (splits + g - 1) / g};
+}
+
 template <bool V> struct Flag { static constexpr bool value = V; };
 
 // Multi-token split on the matrix cores: one wave per (head, key split), all T <= 16 queries of the head as the 16
@@ -549,7 +572,9 @@ SplitPlan plan_call(int64_t BH, int64_t L, int T) {
 size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L, int T) {
     if (BH <= 0 || L <= 0 || T < 1 || T > MAX_T) return 0;
     const SplitPlan p = plan_call(BH, L, T);
-    return (size_t)BH * (size_t)T * (size_t)p.splits * PART_FLOATS * sizeof(float);
+    const MergePlan m = merge_plan(p.splits);
+    const size_t states = (size_t)p.splits + (m.groups > 1 ? (size_t)m.groups : 0);
+    return (size_t)BH * (size_t)T * states * PART_FLOATS * sizeof(float);
 }
 
 hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
@@ -579,8 +604,21 @@ hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(BH * T)), dim3(64), 0, stream, (const float*)ws, out,
-                       p.splits, T, ep);
+    const MergePlan m = merge_plan(p.splits);
+    if (m.groups == 1) {
+        hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(BH * T)), dim3(64), 0, stream, (const float*)ws, out,
+                           p.splits, T, ep);
+    } else {
+        // The groups' states follow the splits' states in the workspace.
+        float* ws2 = ws + (size_t)BH * T * p.splits * PART_FLOATS;
+        if (BH * T * m.groups > 0x7fffffff) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(decode_merge_groups_kernel, dim3((unsigned)(BH * T * m.groups)), dim3(64), 0, stream,
+                           (const float*)ws, ws2, p.splits, m.group, m.groups);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(BH * T)), dim3(64), 0, stream, (const float*)ws2, out,
+                           m.groups, T, ep);
+    }
     return hipGetLastError();
 }
 

@@ -60,38 +60,89 @@ hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const
 // row that saw no key), [1] l1, [3] l2 their sums at those offsets, then the unnormalised O1 and O2 (128 each).
 constexpr int PARTIAL_FLOATS = 4 + 2 * 128;
 
-// Merge the n partial states at `part` (consecutive, PARTIAL_FLOATS apart) of one row by log-sum-exp, apply the
-// epilogue of (batch, head) unit bh and store the row's 128 outputs in bf16.  One wave per row: lane owns channels
-// 2 lane and 2 lane + 1.  At least one state must hold a key (finite offsets).
+// Log-sum-exp merge of the n partial states at `part` (consecutive, PARTIAL_FLOATS apart) of one row, in one wave:
+// lane owns channels 2 lane and 2 lane + 1 of O1 and O2.  The maxima are taken with the lanes striding over the
+// states; the sums then run over the states in order, four states' loads in flight at a time.  M1 or M2 is -inf
+// only when no state holds a key for that map (then every weight is taken against 0, and the sums stay 0).
+struct MergedRow {
+    float M1, M2, L1, L2, o1a, o1b, o2a, o2b;
+};
+__device__ __forceinline__ MergedRow merge_states(const float* __restrict__ part, int n, int lane) {
+    typedef float f32x4m __attribute__((ext_vector_type(4)));
+    typedef float f32x2m __attribute__((ext_vector_type(2)));
+    float m1 = -INFINITY, m2 = -INFINITY;
+    for (int s = lane; s < n; s += 64) {
+        m1 = fmaxf(m1, part[s * PARTIAL_FLOATS + 0]);
+        m2 = fmaxf(m2, part[s * PARTIAL_FLOATS + 2]);
+    }
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) {
+        m1 = fmaxf(m1, __shfl_xor(m1, x));
+        m2 = fmaxf(m2, __shfl_xor(m2, x));
+    }
+    MergedRow r{m1, m2, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const float b1 = m1 == -INFINITY ? 0.f : m1, b2 = m2 == -INFINITY ? 0.f : m2;
+    auto add = [&](const f32x4m& hd, const f32x2m& a, const f32x2m& b) {
+        const float w1 = __builtin_amdgcn_exp2f(hd[0] - b1);
+        const float w2 = __builtin_amdgcn_exp2f(hd[2] - b2);
+        r.L1 += w1 * hd[1];
+        r.L2 += w2 * hd[3];
+        r.o1a += w1 * a[0];
+        r.o1b += w1 * a[1];
+        r.o2a += w2 * b[0];
+        r.o2b += w2 * b[1];
+    };
+    int s = 0;
+    for (; s + 4 <= n; s += 4) {
+        f32x4m hd[4];
+        f32x2m a[4], b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float* p = part + (s + u) * PARTIAL_FLOATS;
+            hd[u] = *(const f32x4m*)p;
+            a[u] = *(const f32x2m*)(p + 4 + 2 * lane);
+            b[u] = *(const f32x2m*)(p + 4 + 128 + 2 * lane);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) add(hd[u], a[u], b[u]);
+    }
+    for (; s < n; ++s) {
+        const float* p = part + s * PARTIAL_FLOATS;
+        add(*(const f32x4m*)p, *(const f32x2m*)(p + 4 + 2 * lane), *(const f32x2m*)(p + 4 + 128 + 2 * lane));
+    }
+    return r;
+}
+
+// The n states merged into one state of the same format at `dst` (a level of a merge tree).
+__device__ __forceinline__ void merge_partial_state(const float* __restrict__ part, int n, float* __restrict__ dst,
+                                                    int lane) {
+    typedef float f32x2m __attribute__((ext_vector_type(2)));
+    const MergedRow r = merge_states(part, n, lane);
+    if (lane == 0) {
+        dst[0] = r.M1;
+        dst[1] = r.L1;
+        dst[2] = r.M2;
+        dst[3] = r.L2;
+    }
+    *(f32x2m*)(dst + 4 + 2 * lane) = f32x2m{r.o1a, r.o1b};
+    *(f32x2m*)(dst + 4 + 128 + 2 * lane) = f32x2m{r.o2a, r.o2b};
+}
+
+// The n states merged, the epilogue of (batch, head) unit bh applied, and the row's 128 outputs stored in bf16.
+// At least one state must hold a key for each map.
 __device__ __forceinline__ void merge_partial_row(const float* __restrict__ part, int n, const Epilogue& ep, int bh,
                                                   uint16_t* __restrict__ out_row, int lane) {
-    float M1 = -INFINITY, M2 = -INFINITY;
-    for (int s = 0; s < n; ++s) {
-        M1 = fmaxf(M1, part[s * PARTIAL_FLOATS + 0]);
-        M2 = fmaxf(M2, part[s * PARTIAL_FLOATS + 2]);
-    }
-    float L1 = 0.f, L2 = 0.f, o1a = 0.f, o1b = 0.f, o2a = 0.f, o2b = 0.f;
-    for (int s = 0; s < n; ++s) {
-        const float* p = part + s * PARTIAL_FLOATS;
-        const float w1 = __builtin_amdgcn_exp2f(p[0] - M1);
-        const float w2 = __builtin_amdgcn_exp2f(p[2] - M2);
-        L1 += w1 * p[1];
-        L2 += w2 * p[3];
-        o1a += w1 * p[4 + 2 * lane];
-        o1b += w1 * p[4 + 2 * lane + 1];
-        o2a += w2 * p[4 + 128 + 2 * lane];
-        o2b += w2 * p[4 + 128 + 2 * lane + 1];
-    }
-    const float inv1 = 1.f / L1, inv2 = lambda_of(ep, bh) / L2;
-    float ya = o1a * inv1 - o2a * inv2;
-    float yb = o1b * inv1 - o2b * inv2;
+    const MergedRow r = merge_states(part, n, lane);
+    const float inv1 = 1.f / r.L1, inv2 = lambda_of(ep, bh) / r.L2;
+    float ya = r.o1a * inv1 - r.o2a * inv2;
+    float yb = r.o1b * inv1 - r.o2b * inv2;
     if (ep.normalise) {
         float ss = ya * ya + yb * yb;
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-        const float r = __builtin_amdgcn_rsqf(ss * (1.f / 128) + 1e-5f) * ep.out_scale;
-        ya *= r;
-        yb *= r;
+        const float rr = __builtin_amdgcn_rsqf(ss * (1.f / 128) + 1e-5f) * ep.out_scale;
+        ya *= rr;
+        yb *= rr;
     }
     const unsigned w = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)ya) |
                        ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)yb) << 16);

@@ -270,13 +270,24 @@ def split_plan(BH, L, max_keys, min_grid):
     return -(-L // keys)
 
 
-@pytest.mark.parametrize("B,H,L", [(64, 16, 8192), (1, 2, 8192), (4, 8, 100000), (2, 3, 777), (128, 16, 65536)])
+def merge_groups(splits):
+    """States of the merge's first level per item: none up to 32 splits (one pass), else ceil(splits / g) groups of
+    g = ceil(sqrt(splits)) splits."""
+    if splits <= 32:
+        return 0
+    g = math.isqrt(splits - 1) + 1
+    return -(-splits // g)
+
+
+@pytest.mark.parametrize("B,H,L", [(64, 16, 8192), (1, 2, 8192), (4, 8, 100000), (2, 3, 777), (128, 16, 65536),
+                                   (1, 1, 1 << 20)])
 def test_decode_split_plans(lib, B, H, L):
     """One token: splits of at most 1024 keys and ~2048 workgroups; several tokens: at most 8192 keys and ~1024 waves
-    (workspace = B H T splits x 1040 bytes: m, l and O of both maps per split)."""
+    (workspace = B H T (splits + first-level groups) x 1040 bytes: m, l and O of both maps per state)."""
     for T, max_keys, grid in ((1, 1024, 2048), (4, 8192, 1024), (16, 8192, 1024)):
         splits = split_plan(B * H, L, max_keys, grid)
-        assert lib.diffattn_decode_varlen_workspace_bytes(B, H, T, L, 64) == B * H * T * splits * 1040, (T, splits)
+        states = splits + merge_groups(splits)
+        assert lib.diffattn_decode_varlen_workspace_bytes(B, H, T, L, 64) == B * H * T * states * 1040, (T, splits)
     # the benchmarked multi-token size: one 8192-key split per head
     assert split_plan(64 * 16, 8192, 8192, 1024) == 1
 

@@ -536,6 +536,7 @@ def varlen_inputs(B, H, T, L, seed):
     (2, 1, 5, 5, None, 1),
     (2, 3, 7, 4500, [4500, 9], 3),
     (1, 2, 2, 20000, [19999], 1),
+    (2, 1, 1, 20000, [20000, 5], 1),   # 313 splits, merged in two levels; the short sequence's later groups are empty
 ])
 def test_decode_varlen_vs_oracle(B, H, T, L, lens, layer):
     torch = torch_mod()
