@@ -1,22 +1,19 @@
 // Split-K differential attention decode for gfx950 (bf16 caches, fp32 math, d = 64, 2d = 128).
 //
-// Operation (Ultralytics glossary "Differential Transformer", section on how differential attention works): one
-// query token per (batch, head) attends to the whole cache with the two softmax maps; output
+// Operation (Ultralytics glossary "Differential Transformer", section on how differential attention works): each
+// new query token of a (batch, head) attends to the cache with the two softmax maps; output
 // sum_j (a_j - lambda b_j) v_j, then optionally the per-head RMS normalisation and the (1 - lambda_init) scale.
 //
 // The pass is HBM-bound (each cached byte is read once, 1.5 FLOP per byte), so the design is about streaming:
-//   * decode_split: one workgroup per (head, key split).  Phase 1 reads K1 and K2 rows with 16-byte loads, eight
-//     lanes per 128-byte row so every wave-wide load covers 1 KiB of contiguous cache, and keeps the split's
-//     scores in LDS.  Phase 2 takes the split's exact maximum and sum per map.  Phase 3 streams V rows (sixteen
-//     lanes per 256-byte row) and accumulates both maps' partial outputs in fp32.  The split's state
-//     (m, l, O[128]) per map goes to the workspace.
-//   * decode_merge: one wave per head merges the splits by log-sum-exp and applies the epilogue.
+//   * decode_multi_mfma: one wave per (head, key split) holds the T <= 16 new tokens of the head (T = 1 for plain
+//     decode) in the 16 columns of 16x16x32 MFMA tiles: scores K Q^T and outputs V^T P^T on the matrix cores, an
+//     online softmax per query in between (see the kernel).  New token t sits at cache position len - T + t and
+//     sees the keys up to its own position.  The split's state (m, l, O[128]) per map and query goes to the
+//     workspace.
+//   * decode_merge: one wave per (head, query) merges the splits by log-sum-exp and applies the epilogue; with
+//     many splits, decode_merge_groups first merges groups of them.
 //   * Ragged caches: with a per-sequence length array, sequence b uses the first lens[b] cache rows (the cache is
 //     padded to L rows); splits past its end write an empty state (max -inf, sum 0), which the merge weighs by 0.
-//   * decode_multi_mfma: T > 1 new tokens per sequence (T <= 16), query t at cache position len - T + t seeing
-//     keys up to its own position.  One wave per (head, key split) puts the T queries in the 16 columns of
-//     16x16x32 MFMA tiles: scores K Q^T and outputs V^T P^T on the matrix cores, an online softmax per query in
-//     between (see the kernel).
 //   * Paged caches (template flag PAGED): a sequence's rows live in fixed-size pages of a pool shared by all
 //     sequences, found through a per-sequence block table.  A split first copies its page indices into LDS
 //     (stage_pages); every row address then goes through cache_elem.
@@ -33,43 +30,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 64;
 constexpr int DV = 128;
-constexpr int THREADS = 256;
-constexpr int MAX_SPLIT_KEYS = 1024;          // one token: keys per split (scores of both maps fit in 8 KiB of LDS)
-constexpr int MULTI_MAX_SPLIT_KEYS = 8192;    // several tokens: keys per split (the kernel keeps no per-key state)
-constexpr int PT_MAX = 128;                   // page-table entries staged per split (one token)
-constexpr int MULTI_PT_MAX = 520;             // the same for several tokens
-static_assert(MAX_SPLIT_KEYS / 16 + 2 <= PT_MAX, "a split spans at most keys / 16 + 2 pages of the smallest size");
+constexpr int MULTI_MAX_SPLIT_KEYS = 8192;    // keys per split (the kernel keeps no per-key state)
+constexpr int MULTI_PT_MAX = 520;             // page-table entries staged per split
 static_assert(MULTI_MAX_SPLIT_KEYS / 16 + 2 <= MULTI_PT_MAX, "a split spans at most keys / 16 + 2 pages");
 constexpr int PART_FLOATS = 4 + 2 * DV;       // m1, l1, m2, l2, O1[128], O2[128]
 static_assert(PART_FLOATS == PARTIAL_FLOATS, "the decode's split states are the shared partial-state format");
 constexpr int MAX_T = 16;                     // new tokens per sequence in multi-token decode
 constexpr float LOG2E = 1.4426950408889634f;
-
-__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Note: the vector element is copied to a scalar before __builtin_bit_cast; bit-casting a subscripted vector
-// element directly (bit_cast(T, v[k])) compiles to element 0 for every k with this compiler.
-__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const unsigned ak = a[k], bk = b[k];
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ak), __builtin_bit_cast(bf16x2, bk), acc,
-                                              false);
-    }
-    return acc;
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
-    return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) x += __shfl_xor(x, s);
-    return x;
-}
 
 struct SplitPlan {
     int splits;      // key splits per head
@@ -89,7 +56,7 @@ __host__ __device__ inline SplitPlan plan_splits(int64_t BH, int64_t L, int64_t 
     return SplitPlan{(int)s, (int)keys};
 }
 
-// Paged caches: copy the block-table entries of the pages that hold rows [j0, j0 + MAX_SPLIT_KEYS) of sequence b
+// Paged caches: copy the block-table entries of ENTRIES pages of sequence b, from the one holding row j0 on,
 // into ptab (clamped to the pool; positions past the table repeat its last entry), so that a row's page is an LDS
 // read rather than a dependent global load.  Returns the first staged page.  The caller makes the writes visible
 // (a barrier, or the same wave's later reads).
@@ -127,139 +94,6 @@ __device__ __forceinline__ int seq_len(const int* lens, int b, int lo, int L) {
 
 // 16-byte nontemporal load (cache policy "nt": streamed data that will not be read again).
 __device__ __forceinline__ u32x4 ldnt(const uint16_t* p) { return __builtin_nontemporal_load((const u32x4*)p); }
-
-__device__ __forceinline__ void write_empty(float* dst, int tid) {
-    if (tid == 0) {
-        dst[0] = -INFINITY;
-        dst[1] = 0.f;
-        dst[2] = -INFINITY;
-        dst[3] = 0.f;
-    }
-    for (int k = tid; k < 2 * DV; k += THREADS) dst[4 + k] = 0.f;
-}
-
-template <bool PAGED>
-__global__ __launch_bounds__(THREADS) void decode_split_kernel(const uint16_t* __restrict__ gq1,
-                                                               const uint16_t* __restrict__ gk1,
-                                                               const uint16_t* __restrict__ gq2,
-                                                               const uint16_t* __restrict__ gk2,
-                                                               const uint16_t* __restrict__ gv,
-                                                               float* __restrict__ ws, int L, int splits,
-                                                               int split_keys, const int* __restrict__ lens, int H,
-                                                               DecodePages pg, CacheStrides cs) {
-    __shared__ float sc1[MAX_SPLIT_KEYS], sc2[MAX_SPLIT_KEYS];
-    __shared__ float red[4][8];
-    __shared__ float part[4][2 * DV];
-    __shared__ int ptab[PAGED ? PT_MAX : 1];   // paged caches: the split's page indices
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int bh = blockIdx.x / splits;
-    const int sp = blockIdx.x % splits;
-    const int j0 = sp * split_keys;
-    const int n = min(seq_len(lens, bh / H, 1, L), j0 + split_keys) - j0;
-    if (n <= 0) {   // past this sequence's end (ragged caches only)
-        write_empty(ws + ((size_t)bh * splits + sp) * PART_FLOATS, tid);
-        return;
-    }
-    const float c = LOG2E * 0.125f;  // log2(e) / sqrt(64)
-    const int hh = bh % H, bb = bh / H;
-    const int pg0 = stage_pages<PAGED, PT_MAX>(pg, bb, j0, ptab, tid, THREADS);
-    if constexpr (PAGED) __syncthreads();
-
-    // Phase 1: scores.  Lane handles 16-byte chunk (lane % 8) of row (lane / 8) of an 8-row group; the workgroup
-    // covers 32 rows per step.
-    const int ch = lane & 7;
-    const u32x4 qa = *(const u32x4*)(gq1 + (size_t)bh * D + ch * 8);
-    const u32x4 qb = *(const u32x4*)(gq2 + (size_t)bh * D + ch * 8);
-    float mx1 = -INFINITY, mx2 = -INFINITY;
-    const int r_in = wave * 8 + (lane >> 3);
-    for (int r0 = 0; r0 < n; r0 += 32) {
-        const int r = r0 + r_in;
-        const int rr = min(r, n - 1);
-        // Cache rows are read once: nontemporal loads stream them without displacing other data in the caches.
-        const u32x4 ka = ldnt(gk1 + cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, j0 + rr, C_K1, D) + ch * 8);
-        const u32x4 kb = ldnt(gk2 + cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, j0 + rr, C_K2, D) + ch * 8);
-        float s1 = dot8(qa, ka, 0.f), s2 = dot8(qb, kb, 0.f);
-        s1 += __shfl_xor(s1, 1); s2 += __shfl_xor(s2, 1);
-        s1 += __shfl_xor(s1, 2); s2 += __shfl_xor(s2, 2);
-        s1 += __shfl_xor(s1, 4); s2 += __shfl_xor(s2, 4);
-        s1 *= c;
-        s2 *= c;
-        if (r < n) {
-            if (ch == 0) { sc1[r] = s1; sc2[r] = s2; }
-            mx1 = fmaxf(mx1, s1);
-            mx2 = fmaxf(mx2, s2);
-        }
-    }
-    // Phase 2: exact split maximum and sum per map.
-    mx1 = wave_max(mx1);
-    mx2 = wave_max(mx2);
-    if (lane == 0) { red[wave][0] = mx1; red[wave][1] = mx2; }
-    __syncthreads();
-    const float m1 = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
-    const float m2 = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1]));
-    float z1 = 0.f, z2 = 0.f;
-    for (int r = tid; r < n; r += THREADS) {
-        const float p1 = __builtin_amdgcn_exp2f(sc1[r] - m1);
-        const float p2 = __builtin_amdgcn_exp2f(sc2[r] - m2);
-        sc1[r] = p1;
-        sc2[r] = p2;
-        z1 += p1;
-        z2 += p2;
-    }
-    z1 = wave_sum(z1);
-    z2 = wave_sum(z2);
-    if (lane == 0) { red[wave][2] = z1; red[wave][3] = z2; }
-    __syncthreads();
-
-    // Phase 3: partial outputs.  Lane handles channels 8*(lane % 16) .. +7 of row (lane / 16) of a 4-row group;
-    // the workgroup covers 16 rows per step.
-    const int vc = lane & 15;
-    const int vr_in = wave * 4 + (lane >> 4);
-    float a1[8], a2[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) { a1[k] = 0.f; a2[k] = 0.f; }
-#pragma unroll 4
-    for (int r0 = 0; r0 < n; r0 += 16) {
-        const int r = r0 + vr_in;
-        if (r < n) {
-            const u32x4 w = ldnt(gv + cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, j0 + r, C_V, DV) + vc * 8);
-            const float p1 = sc1[r], p2 = sc2[r];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float lo = bf_lo(w[k]), hi = bf_hi(w[k]);
-                a1[2 * k] = __builtin_fmaf(p1, lo, a1[2 * k]);
-                a1[2 * k + 1] = __builtin_fmaf(p1, hi, a1[2 * k + 1]);
-                a2[2 * k] = __builtin_fmaf(p2, lo, a2[2 * k]);
-                a2[2 * k + 1] = __builtin_fmaf(p2, hi, a2[2 * k + 1]);
-            }
-        }
-    }
-    // Reduce the 4 row slots of the wave (lanes vc, vc+16, vc+32, vc+48), then the 4 waves through LDS.
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        a1[k] += __shfl_xor(a1[k], 16);
-        a1[k] += __shfl_xor(a1[k], 32);
-        a2[k] += __shfl_xor(a2[k], 16);
-        a2[k] += __shfl_xor(a2[k], 32);
-    }
-    if (lane < 16) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            part[wave][vc * 8 + k] = a1[k];
-            part[wave][DV + vc * 8 + k] = a2[k];
-        }
-    }
-    __syncthreads();
-    float* dst = ws + ((size_t)bh * splits + sp) * PART_FLOATS;
-    if (tid == 0) {
-        dst[0] = m1;
-        dst[1] = red[0][2] + red[1][2] + red[2][2] + red[3][2];
-        dst[2] = m2;
-        dst[3] = red[0][3] + red[1][3] + red[2][3] + red[3][3];
-    }
-    for (int k = tid; k < 2 * DV; k += THREADS) dst[4 + k] = part[0][k] + part[1][k] + part[2][k] + part[3][k];
-}
 
 // One wave per (head, query): blockIdx.x = bh * T + t.  Every query sees at least one key, so some split is
 // non-empty and the merged maxima are finite.
@@ -558,13 +392,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     }
 }
 
-// Split plan of a call.  The single-token kernel takes splits of at most 1024 keys (its scores live in LDS) and at
-// least ~2048 workgroups.  The multi-token kernel keeps no per-key state, so its splits may be long: at least
-// ceil(L / 8192) per head, more only to keep ~1024 waves in the grid (four per CU).  Fewer, longer splits stream
-// faster than more, shorter ones (B64 H16, ragged caches of 4K-8K rows, T = 4: splits of 1024 keys 5.1 TB/s, 2048
-// 5.7, 4096 5.85, one 8192-key split per head 5.93).
+// Split plan of a call.  The kernel keeps no per-key state, so splits may be long; fewer, longer splits stream
+// faster than many short ones, down to about a wave per SIMD.  Measured at one token on full caches (4 GiB at
+// B64 H16 L8192 or B16 H16 L32768, 0.5 GiB at B1 H16 L65536, B1 H1 L1M or B8 H16 L8192): splits of at most 4096
+// keys with at least ~512 waves were the fastest or within 1% of it (B64 H16 L8192: 640 us against 652 for one
+// 8192-key split per head; B1 H16 L65536: 89 us against 94 for at least 1024 waves).  Several tokens on ragged
+// caches take splits of up to 8192 keys and ~1024 waves (B64 H16, caches of 4K-8K rows, T = 4: splits of 1024 keys
+// 5.1 TB/s, 2048 5.7, 4096 5.85, one 8192-key split per head 5.93): a split's waves stop at its sequence's end.
 SplitPlan plan_call(int64_t BH, int64_t L, int T) {
-    return T == 1 ? plan_splits(BH, L, MAX_SPLIT_KEYS, 2048) : plan_splits(BH, L, MULTI_MAX_SPLIT_KEYS, 1024);
+    return T == 1 ? plan_splits(BH, L, 4096, 512) : plan_splits(BH, L, MULTI_MAX_SPLIT_KEYS, 1024);
 }
 
 }  // namespace
@@ -587,21 +423,12 @@ hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const 
     if (pages && ((int64_t)pages->max_pages << pages->log2_page) != L) return hipErrorInvalidValue;
     float* ws = (float*)workspace;
     const DecodePages pg = pages ? *pages : DecodePages{nullptr, 0, 0, 0};
-    if (T == 1) {
-        if (pages)
-            hipLaunchKernelGGL(decode_split_kernel<true>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1, q2,
-                               k2, v, ws, (int)L, p.splits, p.split_keys, lens, (int)H, pg, cs);
-        else
-            hipLaunchKernelGGL(decode_split_kernel<false>, dim3((unsigned)blocks), dim3(THREADS), 0, stream, q1, k1,
-                               q2, k2, v, ws, (int)L, p.splits, p.split_keys, lens, (int)H, pg, cs);
-    } else {
-        if (pages)
-            hipLaunchKernelGGL(decode_multi_mfma_kernel<true>, dim3((unsigned)blocks), dim3(64), 0, stream, q1, k1,
-                               q2, k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg, cs);
-        else
-            hipLaunchKernelGGL(decode_multi_mfma_kernel<false>, dim3((unsigned)blocks), dim3(64), 0, stream, q1, k1,
-                               q2, k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg, cs);
-    }
+    if (pages)
+        hipLaunchKernelGGL(decode_multi_mfma_kernel<true>, dim3((unsigned)blocks), dim3(64), 0, stream, q1, k1, q2, k2,
+                           v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg, cs);
+    else
+        hipLaunchKernelGGL(decode_multi_mfma_kernel<false>, dim3((unsigned)blocks), dim3(64), 0, stream, q1, k1, q2,
+                           k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg, cs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const MergePlan m = merge_plan(p.splits);

@@ -293,7 +293,7 @@ int diffattn_bwd_strided(const void *q1, const void *k1, const void *q2, const v
  * until the process ends) instead of a caller workspace.  The call itself allocates nothing.
  *   Arguments, layouts, results and errors as for diffattn_decode; the call must need at most
  *   DIFFATTN_NOALLOC_SCRATCH_BYTES of partials (diffattn_decode_workspace_bytes(B, H, L, d); for example B = 64,
- *   H = 16 up to L = 15360), else DIFFATTN_ERR_WORKSPACE before any HIP call.  The partials are fully rewritten by
+ *   H = 16 up to L = 61440), else DIFFATTN_ERR_WORKSPACE before any HIP call.  The partials are fully rewritten by
  *   every call (no state is carried between calls).  All calls on one GPU share its array: calls that may overlap
  *   in time on one GPU (different streams, or threads) race and must be serialised by the caller.  Results are bit
  *   for bit those of diffattn_decode.  The first call on a GPU, with that GPU current, looks up the array's device

@@ -282,9 +282,10 @@ def merge_groups(splits):
 @pytest.mark.parametrize("B,H,L", [(64, 16, 8192), (1, 2, 8192), (4, 8, 100000), (2, 3, 777), (128, 16, 65536),
                                    (1, 1, 1 << 20)])
 def test_decode_split_plans(lib, B, H, L):
-    """One token: splits of at most 1024 keys and ~2048 workgroups; several tokens: at most 8192 keys and ~1024 waves
-    (workspace = B H T (splits + first-level groups) x 1040 bytes: m, l and O of both maps per state)."""
-    for T, max_keys, grid in ((1, 1024, 2048), (4, 8192, 1024), (16, 8192, 1024)):
+    """One token: splits of at most 4096 keys, more of them (down to 64 keys) to keep ~512 waves; several tokens: at
+    most 8192 keys and ~1024 waves (workspace = B H T (splits + first-level groups) x 1040 bytes: m, l and O of both
+    maps per state)."""
+    for T, max_keys, grid in ((1, 4096, 512), (4, 8192, 1024), (16, 8192, 1024)):
         splits = split_plan(B * H, L, max_keys, grid)
         states = splits + merge_groups(splits)
         assert lib.diffattn_decode_varlen_workspace_bytes(B, H, T, L, 64) == B * H * T * states * 1040, (T, splits)
@@ -499,8 +500,9 @@ def test_fwd_train_strided_validation(lib, case, expect):
 def test_decode_noalloc_rejects_oversized_partials(lib):
     """Partials beyond the library's scratch array are DIFFATTN_ERR_WORKSPACE before any HIP call; shape errors are
     reported as for diffattn_decode."""
-    B, H, L = 64, 16, 16384
+    B, H, L = 64, 16, 65536   # 16 splits of 4096 keys per head: 17.0 MB of partials
     assert lib.diffattn_decode_workspace_bytes(B, H, L, 64) > da.NOALLOC_SCRATCH_BYTES
+    assert lib.diffattn_decode_workspace_bytes(B, H, 61440, 64) <= da.NOALLOC_SCRATCH_BYTES
     assert lib.diffattn_decode_noalloc(A[0], A[1], A[2], A[3], A[4], A[5], B, H, L, 64, BF16, 0.8, 1, 1,
                                        None) == E_WS
     assert lib.diffattn_decode_noalloc(A[0], A[1], A[2], A[3], A[4], A[5], 1, 1, 0, 64, BF16, 0.8, 1, 1,
