@@ -177,7 +177,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict_
                    const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
                    const uint16_t* __restrict__ gv, const uint16_t* __restrict__ gdo,
                    const float* __restrict__ stats, uint16_t* __restrict__ dq1, uint16_t* __restrict__ dq2,
-                   int BH, int N, int n_blocks, int causal, int H, BwdStrides gs, Epilogue ep) {
+                   int BH, int N, int n_blocks, int causal, int H, BwdStrides gs, Epilogue ep, int xcd_group) {
     constexpr int K_TILE = TILE * D * 2, V_TILE = TILE * DV * 2;
     __shared__ __attribute__((aligned(16))) unsigned char kr0[2 * K_TILE], kr1[2 * K_TILE], kr2[2 * K_TILE],
         kr3[2 * K_TILE];
@@ -186,9 +186,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict_
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
-    const int bid = blockIdx.x;
-    const int qb = causal ? (n_blocks - 1 - bid / BH) : bid / BH;   // heaviest query blocks first
-    const int bh = bid % BH;
+    int r, bh;   // heaviest query blocks first; each XCD's heads a group at a time (xcd_item)
+    xcd_item((int)blockIdx.x, BH, n_blocks, xcd_group, r, bh);
+    const int qb = causal ? (n_blocks - 1 - r) : r;
     const int q0 = qb * BLOCK, q0w = q0 + TILE * wave;
     const size_t hv = (size_t)bh * N * DV;   // the workspace's dO rows
     const int64_t b_ = bh / H, h_ = bh % H;
@@ -409,15 +409,17 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restric
                      const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
                      const uint16_t* __restrict__ gv, const uint16_t* __restrict__ gdo,
                      const float* __restrict__ stats, uint16_t* __restrict__ dk1, uint16_t* __restrict__ dk2,
-                     uint16_t* __restrict__ dv, int BH, int N, int causal, int H, BwdStrides gs, Epilogue ep) {
+                     uint16_t* __restrict__ dv, int BH, int N, int causal, int H, BwdStrides gs, Epilogue ep,
+                     int xcd_group) {
     __shared__ __attribute__((aligned(16))) unsigned char sl0[SLOT_BYTES], sl1[SLOT_BYTES], sl2[SLOT_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, l16 = lane & 15;
-    const int bid = blockIdx.x;
-    const int kb = bid / BH;   // key blocks in order: the first ones see the most queries under the causal mask
-    const int bh = bid % BH;
+    // Key blocks in order (the first ones see the most queries under the causal mask); each XCD's heads a group at
+    // a time (xcd_item).
+    int kb, bh;
+    xcd_item((int)blockIdx.x, BH, (N + KBLK - 1) / KBLK, xcd_group, kb, bh);
     const int k0 = kb * KBLK, k0w = k0 + KW * wave;
     const size_t hv = (size_t)bh * N * DV;   // the workspace's dO rows
     const int64_t b_ = bh / H, h_ = bh % H;
@@ -696,10 +698,15 @@ hipError_t launch_bwd_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uin
     }
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)pre_blocks), dim3(THREADS), 0, stream, dy, saved, dO, stats,
                        dl_rows, rows, (int)N, (int)H, gs, ep);
+    // Group sizes for the grid order (xcd_head_group); a block's fixed cost taken as 1.5 of the units by which
+    // consecutive blocks' work differs, as measured for the forward's row tiles.  dQ runs two workgroups per CU,
+    // dK/dV three.
+    const int xg_q = xcd_head_group(BH, n_blocks, causal, 1.5, 64);
+    const int xg_kv = xcd_head_group(BH, (N + KBLK - 1) / KBLK, causal, 1.5, 96);
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)grid), dim3(THREADS), 0, stream, q1, k1, q2, k2, v, dO, stats,
-                       dq1, dq2, (int)BH, (int)N, n_blocks, causal ? 1 : 0, (int)H, gs, ep);
+                       dq1, dq2, (int)BH, (int)N, n_blocks, causal ? 1 : 0, (int)H, gs, ep, xg_q);
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_grid), dim3(THREADS), 0, stream, q1, k1, q2, k2, v, dO,
-                       stats, dk1, dk2, dv, (int)BH, (int)N, causal ? 1 : 0, (int)H, gs, ep);
+                       stats, dk1, dk2, dv, (int)BH, (int)N, causal ? 1 : 0, (int)H, gs, ep, xg_kv);
     hipLaunchKernelGGL(bwd_dlambda_kernel, dim3((unsigned)H), dim3(DL_THREADS), 0, stream, dl_rows, dlambda, (int)B,
                        (int)H, (int)N);
     return hipGetLastError();

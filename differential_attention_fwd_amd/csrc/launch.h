@@ -149,6 +149,30 @@ __device__ __forceinline__ void merge_partial_row(const float* __restrict__ part
     *(unsigned*)(out_row + 2 * lane) = w;
 }
 
+// Grid order for launches of many (block, head) items, heaviest block first.  The hardware deals workgroups to the
+// 8 XCDs in turn, so with 8 | B*H the plain order (r = bid / BH, bh = bid % BH) gives XCD x the heads bh = x
+// (mod 8), all of them at once.  With a group size g > 0, XCD x takes its heads g at a time instead (all blocks of
+// a group, heaviest first, before the next group), so fewer heads' K and V (or Q and dO) compete for its 4 MiB L2.
+// Workgroup bid's item: r = 0 for the heaviest block, and its (batch, head) unit bh.
+__device__ __forceinline__ void xcd_item(int bid, int BH, int R, int g, int& r, int& bh) {
+    if (g > 0) {
+        const int x = bid & 7, i = bid >> 3;
+        const int per_group = g * R;
+        const int q = i / per_group, rem = i - q * per_group;
+        r = rem / g;
+        bh = 8 * (q * g + rem - r * g) + x;
+    } else {
+        r = bid / BH;
+        bh = bid % BH;
+    }
+}
+// The group size for BH heads of R blocks each (0: the plain order): the smallest divisor of the XCD's head count
+// BH / 8 whose modelled schedule ends within 0.5% of the plain order's.  The model dispatches the XCD's items in
+// grid order to whichever of its `slots` workgroup slots (workgroups per CU x 32 CUs) frees first; block r costs
+// fixed_units + (R - r) units when causal (the heaviest first), fixed_units + R otherwise, a unit being the work
+// that shrinks from one block to the next.
+int xcd_head_group(int64_t BH, int64_t R, int causal, double fixed_units, int slots);
+
 // Split-key prefill for launches too small to fill the GPU (see prefill_key_splits): each row tile's key range is
 // cut into splits handled by separate workgroups, which write per-row partial states; a merge kernel then combines
 // each row's non-empty ones and applies the epilogue.

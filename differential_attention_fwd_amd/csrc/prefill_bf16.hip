@@ -197,22 +197,10 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* _
         rt = hi - 1 - rem / (BH * j);
         bh = rem % (BH * j) / j;
         sp = rem % j;
-    } else if (xcd_group > 0) {
-        // Workgroups are dealt to the 8 XCDs in turn, so XCD x runs blockIdx.x = x, x + 8, ...: give it the heads
-        // bh = x (mod 8), xcd_group of them at a time (heaviest row tiles first within each group), so that fewer
-        // heads' K and V compete for its L2.  The host picked xcd_group (head_group_of) and checked that 8 and
-        // xcd_group divide the head count.
-        const int bid = (int)blockIdx.x;
-        const int x = bid & 7, i = bid >> 3;
-        const int per_group = xcd_group * n_row_tiles;
-        const int q = i / per_group, rem = i - q * per_group;
-        const int r = rem / xcd_group, hj = rem - r * xcd_group;
-        rt = causal ? (n_row_tiles - 1 - r) : r;
-        bh = 8 * (q * xcd_group + hj) + x;
     } else {
-        const int bid = (int)blockIdx.x;
-        rt = causal ? (n_row_tiles - 1 - bid / BH) : bid / BH;
-        bh = bid % BH;
+        int r;
+        xcd_item((int)blockIdx.x, BH, n_row_tiles, xcd_group, r, bh);
+        rt = causal ? (n_row_tiles - 1 - r) : r;
     }
     const int q0 = rt * BM;
     const int q0w = q0 + wave * 32;
@@ -538,41 +526,39 @@ int64_t split_items(int64_t BH, int n_row_tiles, int splits, int kt_split, int c
 
 namespace {
 
-// Heads per group on one XCD (the kernel's xcd_group), or 0 for the plain order (heaviest row tiles first, heads
-// innermost).  With 8 | B*H the plain order already gives XCD x the heads bh = x (mod 8), but all of them at once: at
-// B4 H12 N4096 six heads, 9 MiB of K and V against a 4 MiB L2, and the K/V tiles of one launch were read from beyond
-// the L2 2.0 times over.  Taking them a group at a time cuts that (three heads: 297 -> 200 MB per launch measured),
-// as long as the XCD's 64 workgroup slots stay as evenly loaded as in the plain order: the group size is the
-// smallest divisor of the XCD's head count whose modelled schedule (greedy dispatch of the XCD's items in grid
-// order onto 64 slots; a workgroup costs 14.0 K + 2262 cycles per key tile, fitted to per-workgroup timestamps)
-// ends within 0.5% of the plain order's.  Measured at B4 H12 N4096: groups of 3 heads time-neutral against the plain
-// order, groups of 2 (modelled 19% longer) 5% slower.
-double xcd_makespan(int heads, int R, int K, int causal, int group) {
-    constexpr int SLOTS = 64;   // two workgroups on each of an XCD's 32 CUs
-    double slot[SLOTS] = {};
+// Modelled end of one XCD's schedule (see xcd_head_group in launch.h).
+double xcd_makespan(int heads, int R, int causal, double fixed, int group, int slots) {
+    constexpr int SLOTS_MAX = 256;
+    const int ns = slots < 1 ? 1 : slots > SLOTS_MAX ? SLOTS_MAX : slots;
+    double slot[SLOTS_MAX] = {};
     const auto later = [](double a, double b) { return a > b; };
     double end = 0.0;
     for (int q = 0; q < heads / group; ++q)
         for (int r = 0; r < R; ++r) {
-            const int rt = causal ? R - 1 - r : r;
-            const int tiles = causal && rt < R - 1 ? (rt + 1) * (BM / BN) : K;
+            const double cost = fixed + (causal ? R - r : R);
             for (int hj = 0; hj < group; ++hj) {
-                std::pop_heap(slot, slot + SLOTS, later);
-                slot[SLOTS - 1] += 14000.0 + 2262.0 * tiles;
-                end = fmax(end, slot[SLOTS - 1]);
-                std::push_heap(slot, slot + SLOTS, later);
+                std::pop_heap(slot, slot + ns, later);
+                slot[ns - 1] += cost;
+                end = fmax(end, slot[ns - 1]);
+                std::push_heap(slot, slot + ns, later);
             }
         }
     return end;
 }
 
-int head_group_of(int64_t BH, int64_t N, int causal) {
-    if (BH <= 0 || N <= 0 || (BH & 7) != 0) return 0;
-    const int64_t heads = BH / 8, R = (N + BM - 1) / BM, K = (N + BN - 1) / BN;
+}  // namespace
+
+// At B4 H12 N4096 the prefill's six heads per XCD read K and V from beyond the L2 2.0 times over (297 MB per launch
+// against 151 MB of inputs); three heads at a time: 197 MB, time-neutral; two heads (modelled 19% longer): 5% slower.
+int xcd_head_group(int64_t BH, int64_t R, int causal, double fixed_units, int slots) {
+    if (BH <= 0 || R <= 0 || (BH & 7) != 0) return 0;
+    const int64_t heads = BH / 8;
     if (heads * R > (1 << 16)) return 0;   // the model's cost grows with the items; such launches keep the plain order
     struct Plan {
-        int64_t BH, N;
-        int causal, group;
+        int64_t BH, R;
+        int causal;
+        double fixed;
+        int slots, group;
     };
     static std::mutex mu;
     static Plan kept[16];
@@ -581,23 +567,23 @@ int head_group_of(int64_t BH, int64_t N, int causal) {
     {
         std::lock_guard<std::mutex> lock(mu);
         for (int i = 0; i < kept_n; ++i)
-            if (kept[i].BH == BH && kept[i].N == N && kept[i].causal == causal) return kept[i].group;
+            if (kept[i].BH == BH && kept[i].R == R && kept[i].causal == causal && kept[i].fixed == fixed_units &&
+                kept[i].slots == slots)
+                return kept[i].group;
     }
-    const double plain = xcd_makespan((int)heads, (int)R, (int)K, causal, (int)heads);
+    const double plain = xcd_makespan((int)heads, (int)R, causal, fixed_units, (int)heads, slots);
     int group = 0;
     for (int g = 1; g < heads; ++g)
-        if (heads % g == 0 && xcd_makespan((int)heads, (int)R, (int)K, causal, g) <= 1.005 * plain) {
+        if (heads % g == 0 && xcd_makespan((int)heads, (int)R, causal, fixed_units, g, slots) <= 1.005 * plain) {
             group = g;
             break;
         }
     std::lock_guard<std::mutex> lock(mu);
-    kept[next] = Plan{BH, N, causal, group};
+    kept[next] = Plan{BH, R, causal, fixed_units, slots, group};
     next = (next + 1) % 16;
     kept_n = kept_n < 16 ? kept_n + 1 : 16;
     return group;
 }
-
-}  // namespace
 
 hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
                                    const uint16_t* v, uint16_t* out, int64_t B, int64_t H, int64_t N, int causal,
@@ -607,7 +593,9 @@ hipError_t launch_prefill_bf16_d64(const uint16_t* q1, const uint16_t* k1, const
     const int64_t blocks = (int64_t)n_row_tiles * BH;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const KeySplit none{1, 0, nullptr};
-    const int xg = head_group_of(BH, N, causal);
+    // A row tile's fixed cost (prologue, diagonal tiles, epilogue: 14.0 K cycles) in units of the 4 key tiles
+    // (4 x 2262 cycles) by which consecutive row tiles differ.
+    const int xg = xcd_head_group(BH, n_row_tiles, causal, 14000.0 / (4 * 2262.0), 64);   // two workgroups per CU
     if (saved)
         hipLaunchKernelGGL((prefill_bf16_d64_kernel<true, false>), dim3((unsigned)blocks), dim3(THREADS), 0, stream,
                            q1, k1, q2, k2, v, out, (int)BH, (int)H, (int)N, n_row_tiles, causal ? 1 : 0, st, ep, saved,
