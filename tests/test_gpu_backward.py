@@ -117,6 +117,8 @@ def test_training_forward_matches_inference_forward():
     (1, 2, 1, True, 1, 0.8),
     (1, 1, 1000, True, 12, 0.7778701),
     (1, 2, 300, False, 0, 0.25),
+    (2, 8, 600, True, 1, 0.6),      # 16 heads: the dQ and dK/dV grids take each XCD's two heads one at a time
+    (4, 8, 256, False, 2, 0.4),     # 32 heads, not causal
 ])
 def test_backward_vs_oracle(B, H, N, causal, layer, lam):
     say(f"case: backward B{B} H{H} N{N} causal={causal} layer={layer} lambda={lam}")

@@ -185,6 +185,23 @@ def test_prefill_n65536_sampled():
 
 
 @pytest.mark.parametrize("B,H,N,causal,layer", [
+    (2, 8, 1000, True, 1),   # 16 heads: each XCD takes its two heads one at a time
+    (3, 8, 700, False, 0),   # 24 heads, not causal
+    (4, 8, 2048, True, 2),   # 32 heads
+])
+def test_prefill_xcd_head_groups(B, H, N, causal, layer):
+    """Grids whose head count is a multiple of 8 take each XCD's heads a group at a time (a different order of the
+    same items): every row against the oracle."""
+    inp = di.prefill_bf16(B, H, N, 64, seed=1300 + N)
+    say(f"case: prefill head groups B{B} H{H} N{N} causal={causal} layer={layer}")
+    lam = float(np.float32(0.8 if layer == 0 else oracle.lambda_init(layer)))
+    got = run_prefill_bf16(inp, lam, layer, causal)
+    f = widen(inp)
+    ref = oracle.diffattn(f["q1"], f["k1"], f["q2"], f["k2"], f["v"], lam, layer, causal)
+    check_bf16(got, ref, f"prefill head groups N{N}", raw=layer == 0)
+
+
+@pytest.mark.parametrize("B,H,N,causal,layer", [
     (1, 8, 1024, True, 1),     # the small benchmarked prefill: 4 key splits per row tile
     (1, 2, 1000, True, 0),     # 8 splits of 128 keys, ragged tail
     (2, 1, 1000, False, 2),    # not causal: every row tile has all 8 splits
