@@ -418,8 +418,9 @@ hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const 
                                   const int* lens, const DecodePages* pages, const CacheStrides& cs, Epilogue ep,
                                   void* workspace, hipStream_t stream) {
     const SplitPlan p = plan_call(BH, L, T);
+    const MergePlan m = merge_plan(p.splits);
     const int64_t blocks = BH * (int64_t)p.splits;
-    if (blocks > 0x7fffffff || BH * T > 0x7fffffff || T < 1 || T > MAX_T) return hipErrorInvalidValue;
+    if (blocks > 0x7fffffff || BH * T * m.groups > 0x7fffffff || T < 1 || T > MAX_T) return hipErrorInvalidValue;
     if (pages && ((int64_t)pages->max_pages << pages->log2_page) != L) return hipErrorInvalidValue;
     float* ws = (float*)workspace;
     const DecodePages pg = pages ? *pages : DecodePages{nullptr, 0, 0, 0};
@@ -431,14 +432,12 @@ hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const 
                            k2, v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg, cs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const MergePlan m = merge_plan(p.splits);
     if (m.groups == 1) {
         hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(BH * T)), dim3(64), 0, stream, (const float*)ws, out,
                            p.splits, T, ep);
     } else {
         // The groups' states follow the splits' states in the workspace.
         float* ws2 = ws + (size_t)BH * T * p.splits * PART_FLOATS;
-        if (BH * T * m.groups > 0x7fffffff) return hipErrorInvalidValue;
         hipLaunchKernelGGL(decode_merge_groups_kernel, dim3((unsigned)(BH * T * m.groups)), dim3(64), 0, stream,
                            (const float*)ws, ws2, p.splits, m.group, m.groups);
         e = hipGetLastError();
