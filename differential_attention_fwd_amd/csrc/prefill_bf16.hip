@@ -29,7 +29,8 @@
 //     issued between map 1's value MFMAs.
 //   * Epilogue: O1/l1 - lambda O2/l2, RMS over the 128 channels (pair-reduced), scale, bf16 round-to-nearest-even.
 //   * Causal: row tiles are launched heaviest first; tiles wholly above a wave's rows are skipped by that wave,
-//     and only diagonal or ragged-tail tiles pay for masking.
+//     and only diagonal or ragged-tail tiles pay for masking.  Each XCD takes its heads a few at a time (xcd_item),
+//     so that fewer heads' K and V compete for its L2.
 //
 // This translation unit is compiled with -fno-honor-nans: no NaN can arise (inputs are finite, masked scores are
 // -inf, the running offsets start at -FLT_MAX rather than -inf, and every processed row has a visible key in its
@@ -161,6 +162,7 @@ __device__ __host__ inline int ranges_of(int rt, int kt_split, int n_row_tiles, 
 
 // SAVE: also write each row's training statistics (SAVED_* in launch.h) for the backward pass.
 // SPLIT: cover one key range of the row tile and write partial states (KeySplit).
+// xcd_group: without SPLIT, the heads each XCD takes at a time (xcd_item in launch.h; 0: all of them).
 template <bool SAVE, bool SPLIT>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_d64_kernel(const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1,
