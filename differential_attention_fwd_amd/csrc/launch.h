@@ -62,7 +62,7 @@ constexpr int PARTIAL_FLOATS = 4 + 2 * 128;
 
 // Log-sum-exp merge of the n partial states at `part` (consecutive, PARTIAL_FLOATS apart) of one row, in one wave:
 // lane owns channels 2 lane and 2 lane + 1 of O1 and O2.  The maxima are taken with the lanes striding over the
-// states; the sums then run over the states in order, four states' loads in flight at a time.  M1 or M2 is -inf
+// states; the sums then run over the states in order, eight states' loads in flight at a time.  M1 or M2 is -inf
 // only when no state holds a key for that map (then every weight is taken against 0, and the sums stay 0).
 struct MergedRow {
     float M1, M2, L1, L2, o1a, o1b, o2a, o2b;
@@ -93,18 +93,19 @@ __device__ __forceinline__ MergedRow merge_states(const float* __restrict__ part
         r.o2b += w2 * b[1];
     };
     int s = 0;
-    for (; s + 4 <= n; s += 4) {
-        f32x4m hd[4];
-        f32x2m a[4], b[4];
+    constexpr int IN_FLIGHT = 8;
+    for (; s + IN_FLIGHT <= n; s += IN_FLIGHT) {
+        f32x4m hd[IN_FLIGHT];
+        f32x2m a[IN_FLIGHT], b[IN_FLIGHT];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < IN_FLIGHT; ++u) {
             const float* p = part + (s + u) * PARTIAL_FLOATS;
             hd[u] = *(const f32x4m*)p;
             a[u] = *(const f32x2m*)(p + 4 + 2 * lane);
             b[u] = *(const f32x2m*)(p + 4 + 128 + 2 * lane);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) add(hd[u], a[u], b[u]);
+        for (int u = 0; u < IN_FLIGHT; ++u) add(hd[u], a[u], b[u]);
     }
     for (; s < n; ++s) {
         const float* p = part + s * PARTIAL_FLOATS;
