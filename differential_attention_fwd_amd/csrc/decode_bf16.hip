@@ -30,9 +30,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 64;
 constexpr int DV = 128;
-constexpr int MULTI_MAX_SPLIT_KEYS = 8192;    // keys per split (the kernel keeps no per-key state)
-constexpr int MULTI_PT_MAX = 520;             // page-table entries staged per split
-static_assert(MULTI_MAX_SPLIT_KEYS / 16 + 2 <= MULTI_PT_MAX, "a split spans at most keys / 16 + 2 pages");
+constexpr int MAX_SPLIT_KEYS = 8192;   // keys per split (the kernel keeps no per-key state)
+constexpr int PT_MAX = 520;            // page-table entries staged per split
+static_assert(MAX_SPLIT_KEYS / 16 + 2 <= PT_MAX, "a split spans at most keys / 16 + 2 pages");
 constexpr int PART_FLOATS = 4 + 2 * DV;       // m1, l1, m2, l2, O1[128], O2[128]
 static_assert(PART_FLOATS == PARTIAL_FLOATS, "the decode's split states are the shared partial-state format");
 constexpr int MAX_T = 16;                     // new tokens per sequence in multi-token decode
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
                                                                int split_keys, const int* __restrict__ lens, int H,
                                                                DecodePages pg, CacheStrides cs) {
     __shared__ __attribute__((aligned(16))) unsigned char vs[MV_TILE];   // the V tile being used
-    __shared__ int ptab[PAGED ? MULTI_PT_MAX : 1];   // paged caches: the split's page indices
+    __shared__ int ptab[PAGED ? PT_MAX : 1];   // paged caches: the split's page indices
 
     const int lane = threadIdx.x;
     const int g = lane >> 4, l16 = lane & 15;
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     // Cache row index of absolute row r of this sequence.  Paged caches read the page index from the split's staged
     // table (LDS), so no global load stands in front of a tile's loads.  One wave: its own later reads see the table.
     const int hh = bh % H, bb = bh / H;
-    const int pg0 = stage_pages<PAGED, MULTI_PT_MAX>(pg, bb, j0, ptab, lane, 64);
+    const int pg0 = stage_pages<PAGED, PT_MAX>(pg, bb, j0, ptab, lane, 64);
     auto elem = [&](int r, int t, int width) __attribute__((always_inline)) -> int64_t {
         return cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, r, t, width);
     };
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 // caches take splits of up to 8192 keys and ~1024 waves (B64 H16, caches of 4K-8K rows, T = 4: splits of 1024 keys
 // 5.1 TB/s, 2048 5.7, 4096 5.85, one 8192-key split per head 5.93): a split's waves stop at its sequence's end.
 SplitPlan plan_call(int64_t BH, int64_t L, int T) {
-    return T == 1 ? plan_splits(BH, L, 4096, 512) : plan_splits(BH, L, MULTI_MAX_SPLIT_KEYS, 1024);
+    return T == 1 ? plan_splits(BH, L, MAX_SPLIT_KEYS / 2, 512) : plan_splits(BH, L, MAX_SPLIT_KEYS, 1024);
 }
 
 }  // namespace
