@@ -20,14 +20,15 @@ events recorded on the stream it is launched on.  Prints ONE JSON line.
             does; tflops_exec counts the 1792 the kernels execute (the dQ kernel recomputes both score maps and dP and
             forms dQ1, dQ2: 768; the dK/dV kernel recomputes them and forms dV, dK1, dK2: 1024)
   prefill_n1024  (not part of the step) the small causal prefill B1 H8 N1024 (layer 1), reported, not gated (64 row
-            tiles for 256 CUs), and the oracle's time on the whole problem, all host threads and one
+            tiles for 256 CUs), through diffattn_fwd and (split) through diffattn_fwd_split, and the oracle's time on
+            the whole problem, all host threads and one
   prefill_n65536  (not part of the step) the causal prefill at B1 H16 N65536 (layer 24): TFLOP/s with its roofline, and
             the oracle's time on 256 sampled rows with the full-problem time extrapolated from them (labelled so)
   clock     the GPU clock and socket power the box reports (amdsmi GPU metrics) while the prefill runs back to back
             for about two seconds, and the prefill rate over that window
   context   the same box's bf16 GEMM rate (torch.matmul 8192^3, random data), torch's streaming read (a sum over a
-            4 GiB tensor), and the best streaming read of a plain probe kernel (16-byte nontemporal loads, the decode
-            kernels' access pattern; libstreamprobe.so): what this machine reaches, next to the nominal peaks
+            4 GiB tensor), and the best streaming read of a plain probe kernel (16-byte nontemporal loads, as the decode
+            kernel reads its V rows; libstreamprobe.so): what this machine reaches, next to the nominal peaks
 Each timed kernel reports the median over its repetitions (the headline value uses the median), with the mean and
 the minimum beside it.
 Every roofline's "traffic" is the HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
