@@ -19,6 +19,8 @@
 //     (stage_pages); every row address then goes through cache_elem.
 //   * Padded caches are addressed through per-tensor batch, head and row strides (dense ones included), so K1, K2
 //     and V may be views of token-major or packed buffers.
+#include <algorithm>
+
 #include "launch.h"
 
 namespace diffattn {
@@ -211,40 +213,19 @@ __device__ __forceinline__ bf16x8 multi_softmax(const f32x4 (&s)[2], MultiMap& s
     return __builtin_bit_cast(bf16x8, w);
 }
 
+// The states of one split: keys [j0, j0 + n) (n >= 1) of head bh (sequence bb, head hh; Lb cache rows, the T new
+// tokens at positions Lb - T ..) against the T queries.  Query t's state goes to dst0[(t stride + sp) PART_FLOATS ..].
+// vs and ptab are the calling wave's LDS (the V tile and the staged page indices).
 template <bool PAGED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_multi_mfma_kernel(const uint16_t* __restrict__ gq1,
-                                                               const uint16_t* __restrict__ gk1,
-                                                               const uint16_t* __restrict__ gq2,
-                                                               const uint16_t* __restrict__ gk2,
-                                                               const uint16_t* __restrict__ gv,
-                                                               float* __restrict__ ws, int L, int T, int splits,
-                                                               int split_keys, const int* __restrict__ lens, int H,
-                                                               DecodePages pg, CacheStrides cs) {
-    __shared__ __attribute__((aligned(16))) unsigned char vs[MV_TILE];   // the V tile being used
-    __shared__ int ptab[PAGED ? PT_MAX : 1];   // paged caches: the split's page indices
-
+__device__ __forceinline__ void split_states(const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1,
+                                             const uint16_t* __restrict__ gq2, const uint16_t* __restrict__ gk2,
+                                             const uint16_t* __restrict__ gv, float* __restrict__ dst0, int stride,
+                                             int sp, int bh, int bb, int hh, int H, int Lb, int j0, int n, int T,
+                                             const DecodePages& pg, const CacheStrides& cs, unsigned char* vs,
+                                             int* ptab) {
     const int lane = threadIdx.x;
     const int g = lane >> 4, l16 = lane & 15;
-    const int bh = blockIdx.x / splits;
-    const int sp = blockIdx.x % splits;
-    const int Lb = seq_len(lens, bh / H, T, L);
-    const int j0 = sp * split_keys;
-    const int n = min(Lb, j0 + split_keys) - j0;
     const int pos0 = Lb - T;                                 // cache position of query 0
-    float* dst0 = ws + (size_t)bh * T * splits * PART_FLOATS;
-    if (n <= 0) {
-        for (int t = 0; t < T; ++t) {
-            float* dst = dst0 + ((size_t)t * splits + sp) * PART_FLOATS;
-            if (lane == 0) {
-                dst[0] = -INFINITY;
-                dst[1] = 0.f;
-                dst[2] = -INFINITY;
-                dst[3] = 0.f;
-            }
-            for (int k = lane; k < 2 * DV; k += 64) dst[4 + k] = 0.f;
-        }
-        return;
-    }
     const float c = LOG2E * 0.125f;
     const int t_col = l16;                                   // this lane's query column
     const bool t_ok = t_col < T;
@@ -269,7 +250,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
     // Cache row index of absolute row r of this sequence.  Paged caches read the page index from the split's staged
     // table (LDS), so no global load stands in front of a tile's loads.  One wave: its own later reads see the table.
-    const int hh = bh % H, bb = bh / H;
     const int pg0 = stage_pages<PAGED, PT_MAX>(pg, bb, j0, ptab, lane, 64);
     auto elem = [&](int r, int t, int width) __attribute__((always_inline)) -> int64_t {
         return cache_elem<PAGED>(pg, cs, ptab, pg0, bb, hh, H, r, t, width);
@@ -377,7 +357,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     // 16 cb + 4 g + i of its column).
     const float l1 = col_sum(st1.l), l2 = col_sum(st2.l);
     if (t_ok) {
-        float* dst = dst0 + ((size_t)t_col * splits + sp) * PART_FLOATS;
+        float* dst = dst0 + ((size_t)t_col * stride + sp) * PART_FLOATS;
         if (g == 0) {
             dst[0] = l1 > 0.f ? st1.m : -INFINITY;
             dst[1] = l1;
@@ -392,6 +372,151 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     }
 }
 
+// Fixed split plan: one wave per (head, key split) = (blockIdx.x / splits, blockIdx.x % splits); splits past their
+// sequence's end write an empty state (max -inf, sum 0), which the merge weighs by 0.
+template <bool PAGED>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_multi_mfma_kernel(
+    const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1, const uint16_t* __restrict__ gq2,
+    const uint16_t* __restrict__ gk2, const uint16_t* __restrict__ gv, float* __restrict__ ws, int L, int T,
+    int splits, int split_keys, const int* __restrict__ lens, int H, DecodePages pg, CacheStrides cs) {
+    __shared__ __attribute__((aligned(16))) unsigned char vs[MV_TILE];   // the V tile being used
+    __shared__ int ptab[PAGED ? PT_MAX : 1];   // paged caches: the split's page indices
+    const int lane = threadIdx.x;
+    const int bh = blockIdx.x / splits;
+    const int sp = blockIdx.x % splits;
+    const int Lb = seq_len(lens, bh / H, T, L);
+    const int j0 = sp * split_keys;
+    const int n = min(Lb, j0 + split_keys) - j0;
+    float* dst0 = ws + (size_t)bh * T * splits * PART_FLOATS;
+    if (n <= 0) {
+        for (int t = 0; t < T; ++t) {
+            float* dst = dst0 + ((size_t)t * splits + sp) * PART_FLOATS;
+            if (lane == 0) {
+                dst[0] = -INFINITY;
+                dst[1] = 0.f;
+                dst[2] = -INFINITY;
+                dst[3] = 0.f;
+            }
+            for (int k = lane; k < 2 * DV; k += 64) dst[4 + k] = 0.f;
+        }
+        return;
+    }
+    split_states<PAGED>(gq1, gk1, gq2, gk2, gv, dst0, splits, sp, bh, bh / H, bh % H, H, Lb, j0, n, T, pg, cs, vs,
+                        ptab);
+}
+
+// Balanced plan for ragged caches.  The W = H * sum_b len_b keys of all (sequence, head) items, taken item by item
+// (bh = b H + h) and in key order within an item, are cut into ranges of `chunk` keys, one per wave: wave w takes
+// keys [w chunk, (w + 1) chunk) of that order, which may end one item and start the next, so every wave streams the
+// same number of keys whatever the lengths.  Item bh starts at P = H pre[b] + h len_b (pre: the lengths' exclusive
+// prefix sums); waves P / chunk .. (P + len_b - 1) / chunk hold its keys, and wave w writes its state for the item
+// to slot w - P / chunk.  chunk >= chunk_min = ceil(L / (RAGGED_SLOTS - 1)) bounds the slots per item by
+// (L - 1) / chunk_min + 2 <= RAGGED_SLOTS.  The split and merge kernels derive the same cut from the lengths.
+constexpr int RAGGED_MAX_B = 512;     // sequences: one wave scans their lengths (8 per lane)
+constexpr int RAGGED_MIN_BH = 128;    // fewer items: the fixed plan's many short splits keep more waves busy
+constexpr int RAGGED_WAVES = 1024;    // waves of the cut (one per SIMD), more if chunks would exceed MAX_SPLIT_KEYS
+constexpr int RAGGED_SLOTS = MERGE_DIRECT_MAX;
+struct RaggedCut {
+    int64_t total, chunk;   // keys of all items, keys per wave
+};
+// By one wave: pre[0..B] (LDS) and the cut.  The caller makes pre visible before reading it (a barrier).
+__device__ __forceinline__ RaggedCut ragged_cut(const int* __restrict__ lens, int B, int H, int T, int L, int waves,
+                                                int chunk_min, int* pre) {
+    const int lane = threadIdx.x;
+    int carry = 0;   // at most RAGGED_MAX_B * L keys: fits
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int b = b0 + lane;
+        int x = b < B ? seq_len(lens, b, T, L) : 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        if (b < B) pre[b + 1] = carry + x;
+        carry += __shfl(x, 63);
+    }
+    if (lane == 0) pre[0] = 0;
+    const int64_t total = (int64_t)H * carry;
+    return RaggedCut{total, max((total + waves - 1) / waves, (int64_t)chunk_min)};
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_ragged_mfma_kernel(
+    const uint16_t* __restrict__ gq1, const uint16_t* __restrict__ gk1, const uint16_t* __restrict__ gq2,
+    const uint16_t* __restrict__ gk2, const uint16_t* __restrict__ gv, float* __restrict__ ws, int L, int T, int B,
+    int H, int waves, int chunk_min, int slots, const int* __restrict__ lens, DecodePages pg, CacheStrides cs) {
+    __shared__ __attribute__((aligned(16))) unsigned char vs[MV_TILE];
+    __shared__ int ptab[PAGED ? PT_MAX : 1];
+    __shared__ int pre[RAGGED_MAX_B + 1];
+    const RaggedCut cut = ragged_cut(lens, B, H, T, L, waves, chunk_min, pre);
+    __syncthreads();
+    const int w = blockIdx.x;
+    const int64_t start = (int64_t)w * cut.chunk;
+    if (start >= cut.total) return;
+    const int64_t end = min(start + cut.chunk, cut.total);
+    // The item holding key `start`: the last sequence b with H pre[b] <= start, then the head and the offset.
+    int b = 0;
+    for (int hi = B - 1; b < hi;) {
+        const int mid = (b + hi + 1) >> 1;
+        if ((int64_t)H * pre[mid] <= start) b = mid;
+        else hi = mid - 1;
+    }
+    int64_t item0 = (int64_t)H * pre[b];
+    int len = pre[b + 1] - pre[b];
+    int h = (int)((start - item0) / len);
+    int off = (int)(start - item0 - (int64_t)h * len);
+    for (int64_t pos = start;;) {
+        const int n = (int)min((int64_t)(len - off), end - pos);
+        const int64_t P = item0 + (int64_t)h * len;
+        const int bh = b * H + h;
+        split_states<PAGED>(gq1, gk1, gq2, gk2, gv, ws + (size_t)bh * T * slots * PART_FLOATS, slots,
+                            (int)(w - P / cut.chunk), bh, b, h, H, len, off, n, T, pg, cs, vs, ptab);
+        pos += n;
+        if (pos >= end) break;
+        // More keys in this wave's range: the next item (there is one, since pos < total).
+        off = 0;
+        if (++h == H) {
+            h = 0;
+            ++b;
+            item0 = (int64_t)H * pre[b];
+            len = pre[b + 1] - pre[b];
+        }
+    }
+}
+
+// One wave per (head, query) item = bh * T + t: its slots of the balanced cut merged as decode_merge_kernel does.
+__global__ __launch_bounds__(64) void decode_ragged_merge_kernel(const float* __restrict__ ws, uint16_t* __restrict__ gout,
+                                                                 int L, int T, int B, int H, int waves, int chunk_min,
+                                                                 int slots, const int* __restrict__ lens, Epilogue ep) {
+    __shared__ int pre[RAGGED_MAX_B + 1];
+    const RaggedCut cut = ragged_cut(lens, B, H, T, L, waves, chunk_min, pre);
+    __syncthreads();
+    const int item = blockIdx.x;
+    const int bh = item / T, b = bh / H, h = bh % H;
+    const int len = pre[b + 1] - pre[b];
+    const int64_t P = (int64_t)H * pre[b] + (int64_t)h * len;
+    const int nseg = (int)((P + len - 1) / cut.chunk - P / cut.chunk + 1);
+    merge_partial_row(ws + (size_t)item * slots * PART_FLOATS, nseg, ep, bh, gout + (size_t)item * DV,
+                      (int)threadIdx.x);
+}
+
+struct RaggedPlan {
+    int waves, chunk_min, slots;
+};
+// The balanced plan's launch, or false where the fixed plan serves (too many sequences to scan, too few items, or
+// caches so long that chunk_min would exceed MAX_SPLIT_KEYS).
+bool ragged_plan(int64_t BH, int64_t H, int64_t L, RaggedPlan& rp) {
+    if (BH <= 0 || H <= 0 || L <= 0) return false;
+    if (BH / H > RAGGED_MAX_B || BH < RAGGED_MIN_BH) return false;
+    const int64_t chunk_min = (L + RAGGED_SLOTS - 2) / (RAGGED_SLOTS - 1);
+    if (chunk_min > MAX_SPLIT_KEYS) return false;
+    const int64_t waves = std::max<int64_t>(RAGGED_WAVES, (BH * L + MAX_SPLIT_KEYS - 1) / MAX_SPLIT_KEYS);
+    if (waves > 0x7fffffff) return false;
+    rp = RaggedPlan{(int)waves, (int)chunk_min, (int)((L - 1) / chunk_min + 2)};
+    return true;
+}
+static_assert(RAGGED_SLOTS <= MERGE_DIRECT_MAX, "one merge pass per item");
+
 // Split plan of a call.  The kernel keeps no per-key state, so splits may be long; fewer, longer splits stream
 // faster than many short ones, down to about a wave per SIMD.  Measured at one token on full caches (4 GiB at
 // B64 H16 L8192 or B16 H16 L32768, 0.5 GiB at B1 H16 L65536, B1 H1 L1M or B8 H16 L8192): splits of at most 4096
@@ -405,25 +530,45 @@ SplitPlan plan_call(int64_t BH, int64_t L, int T) {
 
 }  // namespace
 
-size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L, int T) {
+size_t decode_bf16_workspace_bytes(int64_t BH, int64_t H, int64_t L, int T, bool ragged) {
     if (BH <= 0 || L <= 0 || T < 1 || T > MAX_T) return 0;
     const SplitPlan p = plan_call(BH, L, T);
     const MergePlan m = merge_plan(p.splits);
     const size_t states = (size_t)p.splits + (m.groups > 1 ? (size_t)m.groups : 0);
-    return (size_t)BH * (size_t)T * states * PART_FLOATS * sizeof(float);
+    size_t bytes = (size_t)BH * (size_t)T * states * PART_FLOATS * sizeof(float);
+    RaggedPlan rp;
+    if (ragged && ragged_plan(BH, H, L, rp))
+        bytes = std::max(bytes, (size_t)BH * (size_t)T * (size_t)rp.slots * PART_FLOATS * sizeof(float));
+    return bytes;
 }
 
 hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,
                                   const uint16_t* v, uint16_t* out, int64_t BH, int64_t H, int64_t L, int T,
                                   const int* lens, const DecodePages* pages, const CacheStrides& cs, Epilogue ep,
                                   void* workspace, hipStream_t stream) {
-    const SplitPlan p = plan_call(BH, L, T);
-    const MergePlan m = merge_plan(p.splits);
-    const int64_t blocks = BH * (int64_t)p.splits;
-    if (blocks > 0x7fffffff || BH * T * m.groups > 0x7fffffff || T < 1 || T > MAX_T) return hipErrorInvalidValue;
+    if (T < 1 || T > MAX_T || BH * T > 0x7fffffff) return hipErrorInvalidValue;
     if (pages && ((int64_t)pages->max_pages << pages->log2_page) != L) return hipErrorInvalidValue;
     float* ws = (float*)workspace;
     const DecodePages pg = pages ? *pages : DecodePages{nullptr, 0, 0, 0};
+    RaggedPlan rp;
+    if (lens && ragged_plan(BH, H, L, rp)) {
+        const int B = (int)(BH / H);
+        if (pages)
+            hipLaunchKernelGGL(decode_ragged_mfma_kernel<true>, dim3((unsigned)rp.waves), dim3(64), 0, stream, q1, k1,
+                               q2, k2, v, ws, (int)L, T, B, (int)H, rp.waves, rp.chunk_min, rp.slots, lens, pg, cs);
+        else
+            hipLaunchKernelGGL(decode_ragged_mfma_kernel<false>, dim3((unsigned)rp.waves), dim3(64), 0, stream, q1, k1,
+                               q2, k2, v, ws, (int)L, T, B, (int)H, rp.waves, rp.chunk_min, rp.slots, lens, pg, cs);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(decode_ragged_merge_kernel, dim3((unsigned)(BH * T)), dim3(64), 0, stream,
+                           (const float*)ws, out, (int)L, T, B, (int)H, rp.waves, rp.chunk_min, rp.slots, lens, ep);
+        return hipGetLastError();
+    }
+    const SplitPlan p = plan_call(BH, L, T);
+    const MergePlan m = merge_plan(p.splits);
+    const int64_t blocks = BH * (int64_t)p.splits;
+    if (blocks > 0x7fffffff || BH * T * m.groups > 0x7fffffff) return hipErrorInvalidValue;
     if (pages)
         hipLaunchKernelGGL(decode_multi_mfma_kernel<true>, dim3((unsigned)blocks), dim3(64), 0, stream, q1, k1, q2, k2,
                            v, ws, (int)L, T, p.splits, p.split_keys, lens, (int)H, pg, cs);

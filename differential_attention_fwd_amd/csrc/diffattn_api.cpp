@@ -294,7 +294,7 @@ size_t diffattn_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int d) {
     int64_t BH;
     if (B < 0 || H < 0 || L <= 0 || L > DIFFATTN_MAX_LEN || d != 64 || !mul_ok(B, H, &BH) || BH > INT32_MAX)
         return 0;
-    return diffattn::decode_bf16_workspace_bytes(BH, L, 1);
+    return diffattn::decode_bf16_workspace_bytes(BH, H, L, 1, false);
 }
 
 size_t diffattn_decode_varlen_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t L, int d) {
@@ -302,7 +302,7 @@ size_t diffattn_decode_varlen_workspace_bytes(int64_t B, int64_t H, int64_t T, i
     if (B < 0 || H < 0 || T < 1 || T > DIFFATTN_MAX_NEW_TOKENS || L < T || L > DIFFATTN_MAX_LEN || d != 64 ||
         !mul_ok(B, H, &BH) || BH > INT32_MAX)
         return 0;
-    return diffattn::decode_bf16_workspace_bytes(BH, L, (int)T);
+    return diffattn::decode_bf16_workspace_bytes(BH, H, L, (int)T, true);
 }
 
 }  // extern "C"
@@ -377,7 +377,7 @@ int decode_impl(const void* q1, const void* k1, const void* q2, const void* k2, 
                                                     (const float*)k2, (const float*)v, (float*)out, BH, 1, L, d, 1, ep,
                                                     s));
 
-    const size_t need = diffattn::decode_bf16_workspace_bytes(BH, L, (int)T);
+    const size_t need = diffattn::decode_bf16_workspace_bytes(BH, H, L, (int)T, lens != nullptr);
     if (!workspace || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return DIFFATTN_ERR_ALIGN;
     const Span w{(uintptr_t)workspace, (uintptr_t)workspace + need};
@@ -513,7 +513,7 @@ int diffattn_decode_paged(const void* q1, const void* k1_pages, const void* q2, 
         ep.lambda_heads = lambda_heads;
         ep.heads = (int)H;
     }
-    const size_t need = diffattn::decode_bf16_workspace_bytes(BH, L, (int)T);
+    const size_t need = diffattn::decode_bf16_workspace_bytes(BH, H, L, (int)T, lens != nullptr);
     if (!workspace || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return DIFFATTN_ERR_ALIGN;
     const Span w{(uintptr_t)workspace, (uintptr_t)workspace + need};

@@ -253,7 +253,9 @@ inline CacheStrides dense_cache_strides(int64_t H, int64_t L, int64_t d) {
     return s;
 }
 
-size_t decode_bf16_workspace_bytes(int64_t BH, int64_t L, int T);
+// Workspace bytes of a decode call; `ragged`: the call may pass a length array, which for some shapes selects the
+// balanced plan (its states per item may exceed the fixed plan's).
+size_t decode_bf16_workspace_bytes(int64_t BH, int64_t H, int64_t L, int T, bool ragged);
 // pages == nullptr: padded caches addressed through cs (cache row r of head (b, h) of tensor t at element
 // b cs.b[t] + h cs.h[t] + r cs.n[t]); otherwise the page pools.
 hipError_t launch_decode_bf16_d64(const uint16_t* q1, const uint16_t* k1, const uint16_t* q2, const uint16_t* k2,

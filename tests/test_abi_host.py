@@ -287,15 +287,47 @@ def test_decode_split_plans(lib, B, H, L):
     maps per state)."""
     for T, max_keys, grid in ((1, 4096, 512), (4, 8192, 1024), (16, 8192, 1024)):
         splits = split_plan(B * H, L, max_keys, grid)
-        states = splits + merge_groups(splits)
+        states = max(splits + merge_groups(splits), ragged_slots(B, H, L))
         assert lib.diffattn_decode_varlen_workspace_bytes(B, H, T, L, 64) == B * H * T * states * 1040, (T, splits)
-    # the benchmarked multi-token size: one 8192-key split per head
+        if ragged_slots(B, H, L) == 0:   # no balanced plan: a length array changes nothing in the size
+            assert lib.diffattn_decode_varlen_workspace_bytes(B, H, T, L, 64) == B * H * T * (
+                splits + merge_groups(splits)) * 1040
+    # the benchmarked multi-token size: one 8192-key split per head without lengths, 32 balanced slots with them
     assert split_plan(64 * 16, 8192, 8192, 1024) == 1
+    assert ragged_slots(64, 16, 8192) == 32
+
+
+def ragged_slots(B, H, L):
+    """States per (head, token) of the balanced plan for ragged caches (0 where the fixed plan serves): at most 512
+    sequences, at least 128 (sequence, head) items, keys per wave at least ceil(L / 31) and at most 8192."""
+    chunk_min = -(-L // 31)
+    if B > 512 or B * H < 128 or chunk_min > 8192:
+        return 0
+    return (L - 1) // chunk_min + 2
+
+
+def test_ragged_plan_edges(lib):
+    """The balanced plan's eligibility edges in the workspace size: 512 vs 513 sequences, 128 vs 127 items, and the
+    longest cache (31 x 8192 rows) whose keys per wave stay within 8192."""
+    def ws(B, H, T, L):
+        return lib.diffattn_decode_varlen_workspace_bytes(B, H, T, L, 64)
+    assert ragged_slots(512, 1, 40) == 21 and ws(512, 1, 1, 40) == 512 * 21 * 1040
+    assert ws(513, 1, 1, 40) == 513 * (split_plan(513, 40, 4096, 512)) * 1040
+    assert ws(128, 1, 2, 1000) == 128 * 2 * 32 * 1040
+    s = split_plan(127, 1000, 8192, 1024)
+    assert ws(127, 1, 2, 1000) == 127 * 2 * (s + merge_groups(s)) * 1040
+    assert ragged_slots(8, 16, 31 * 8192) == 32 and ragged_slots(8, 16, 31 * 8192 + 1) == 0
+    s = split_plan(128, 31 * 8192, 4096, 512)   # 62 splits and 8 groups: more than the balanced plan's 32
+    assert ws(8, 16, 1, 31 * 8192) == 128 * max(s + merge_groups(s), 32) * 1040
 
 
 def test_varlen_workspace_sizes(lib):
-    one = lib.diffattn_decode_varlen_workspace_bytes(64, 16, 1, 8192, 64)
-    assert one == lib.diffattn_decode_workspace_bytes(64, 16, 8192, 64)
+    # Without the balanced plan (fewer than 128 heads) the varlen size of one token is the decode's; with it, the
+    # larger of the two plans.
+    assert (lib.diffattn_decode_varlen_workspace_bytes(1, 16, 1, 8192, 64) ==
+            lib.diffattn_decode_workspace_bytes(1, 16, 8192, 64))
+    assert (lib.diffattn_decode_varlen_workspace_bytes(64, 16, 1, 8192, 64) ==
+            max(lib.diffattn_decode_workspace_bytes(64, 16, 8192, 64), 64 * 16 * 32 * 1040))
     assert lib.diffattn_decode_varlen_workspace_bytes(2, 2, 16, 1000, 64) % (2 * 2 * 16 * 1040) == 0
     for bad in ((2, 2, 0, 100, 64), (2, 2, 17, 100, 64), (2, 2, 8, 7, 64), (2, 2, 4, 100, 8)):
         assert lib.diffattn_decode_varlen_workspace_bytes(*bad) == 0

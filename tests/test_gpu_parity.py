@@ -567,6 +567,49 @@ def test_decode_varlen_vs_oracle(B, H, T, L, lens, layer):
     check_bf16(host_bf16(out), ref, f"decode varlen T{T} L{L}", raw=layer == 0)
 
 
+def ragged_lens(rng, B, T, L, lo):
+    """Seeded ragged lengths in [lo, L]: a mix of the shortest, the longest and uniform draws, plus (lo = T only)
+    values outside [T, L], which the device clamps."""
+    lens = rng.integers(lo, L + 1, size=B)
+    pick = rng.random(B)
+    lens[pick < 0.15] = lo
+    lens[(pick >= 0.15) & (pick < 0.3)] = L
+    lens[(pick >= 0.3) & (pick < 0.35)] = L + 7
+    if lo == T:
+        lens[(pick >= 0.35) & (pick < 0.4)] = -3
+    return lens.astype(np.int32)
+
+
+@pytest.mark.parametrize("B,H,T,L,lo,layer", [
+    (8, 16, 4, 1000, 4, 1),      # 128 items: the balanced cut, several waves per sequence
+    (128, 1, 1, 700, 1, 0),      # short sequences: waves spanning many items
+    (16, 8, 16, 2048, 16, 2),
+    (130, 1, 3, 65, 11, 1),      # lengths scanned in three rounds of 64 lanes
+    (512, 1, 1, 40, 1, 1),       # the most sequences the balanced cut takes
+    (513, 1, 2, 40, 2, 1),       # one more: the fixed plan
+])
+def test_decode_ragged_balanced_vs_oracle(B, H, T, L, lo, layer):
+    """Ragged caches with at least 128 (sequence, head) items take the balanced plan: the keys of all items cut into
+    equal ranges, one per wave, merged per item.  Against the oracle, every item.
+
+    The B130 case draws lengths of at least 11, so that every query sees 9 keys or more: with T = 3 and lengths of 3,
+    a query that sees two keys under nearly equal maps (a = 0.42 / 0.58, b = 0.44 / 0.56 at this seed) has a raw
+    output of RMS 0.13, and the normalisation magnifies the bf16 rounding of its probabilities to 2.13e-2, above the
+    2e-2 bound, on the fixed plan as on the balanced one; a CPU model of the kernel's rounding (bf16 probabilities,
+    fp32 sums, bf16 output) gives the same 2.13e-2."""
+    torch = torch_mod()
+    rng = np.random.default_rng(640 + B + T)
+    lens = ragged_lens(rng, B, T, L, lo)
+    inp = varlen_inputs(B, H, T, L, seed=650 + B + T)
+    say(f"case: decode ragged balanced B{B} H{H} T{T} L{L} lens {lens.min()}..{lens.max()} layer={layer}")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    ldev = torch.from_numpy(lens).to("cuda:0")
+    out = da.diffattn_decode_varlen(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.8, layer, lens=ldev)
+    torch.cuda.synchronize()
+    ref = varlen_reference(widen(inp), T, L, lens, float(np.float32(0.8)), layer)
+    check_bf16(host_bf16(out), ref, f"decode ragged balanced B{B} T{T} L{L}", raw=layer == 0)
+
+
 def test_decode_varlen_per_head_lambda():
     torch = torch_mod()
     inp = varlen_inputs(2, 3, 3, 640, seed=650)
@@ -600,6 +643,7 @@ def strided_caches(dev, layout):
     ("token", 2, 2, 4, 1500, None),
     ("packed", 3, 2, 1, 1100, None),
     ("packed", 2, 2, 5, 4100, [4100, 31]),
+    ("token", 8, 16, 2, 600, [600, 2, 599, 300, 45, 600, 128, 1]),   # 128 heads: the balanced plan
 ])
 def test_decode_strided_equals_contiguous(layout, B, H, T, L, lens):
     """Strided caches read in place give the contiguous call's bits (same kernels, same split plan)."""
@@ -792,6 +836,7 @@ def paged_case(B, H, T, P, max_pages, lens, seed, bad_entries=False):
     (2, 2, 16, 128, 9, [1100, 17], 2, False),
     (4, 2, 3, 256, 33, [8448, 5000, 3, 100], 1, False),
     (2, 2, 2, 32, 10, [320, 200], 1, True),
+    (8, 16, 4, 16, 20, [320, 4, 100, 17, 319, 64, 250, 200], 1, False),   # 128 heads: the balanced plan
 ])
 def test_decode_paged(B, H, T, P, max_pages, lens, layer, bad):
     torch = torch_mod()
@@ -815,15 +860,15 @@ def test_decode_paged(B, H, T, P, max_pages, lens, layer, bad):
 
 def test_decode_multi_token_long_splits():
     """Multi-token decode at the benchmarked size (B64 H16 T4, caches padded to 8192 rows with seeded ragged lengths
-    in [4096, 8192]), where the split plan gives each head one split of 8192 keys: padded and paged (16-row pages,
-    so one split spans 512 pages of a shuffled pool) give identical bits, and sampled sequences match the oracle."""
+    in [4096, 8192]), where the balanced plan cuts the keys of all 1024 heads into 2048 equal ranges of about 3100
+    keys (up to 32 states per head in the workspace): padded and paged (16-row pages of a shuffled pool) give
+    identical bits, and sampled sequences match the oracle."""
     torch = torch_mod()
     B, H, T, L, P = 64, 16, 4, 8192, 16
     inp = varlen_inputs(B, H, T, L, seed=880)
     lens = np.random.default_rng(881).integers(L // 2, L + 1, size=B).astype(np.int32)
     say(f"case: decode multi-token long splits B{B} H{H} T{T} L{L} lens {lens.min()}..{lens.max()} page {P}")
-    splits = da.diffattn_decode_varlen_workspace_bytes(B, H, T, L, 64) // (B * H * T * 1040)
-    assert splits == 1
+    assert da.diffattn_decode_varlen_workspace_bytes(B, H, T, L, 64) == B * H * T * 32 * 1040
     dev = {k: dev_bf16(v) for k, v in inp.items()}
     ldev = torch.from_numpy(lens).to("cuda:0")
     out = da.diffattn_decode_varlen(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.8, 1, lens=ldev)
