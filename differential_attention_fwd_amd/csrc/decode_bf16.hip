@@ -13,7 +13,9 @@
 //   * decode_merge: one wave per (head, query) merges the splits by log-sum-exp and applies the epilogue; with
 //     many splits, decode_merge_groups first merges groups of them.
 //   * Ragged caches: with a per-sequence length array, sequence b uses the first lens[b] cache rows (the cache is
-//     padded to L rows); splits past its end write an empty state (max -inf, sum 0), which the merge weighs by 0.
+//     padded to L rows).  With enough (sequence, head) items the keys of all of them are cut into equal ranges, one
+//     per wave, whatever the lengths (decode_ragged_mfma, decode_ragged_merge); otherwise the fixed split plan runs,
+//     and its splits past a sequence's end write an empty state (max -inf, sum 0), which the merge weighs by 0.
 //   * Paged caches (template flag PAGED): a sequence's rows live in fixed-size pages of a pool shared by all
 //     sequences, found through a per-sequence block table.  A split first copies its page indices into LDS
 //     (stage_pages); every row address then goes through cache_elem.
@@ -414,7 +416,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 // (L - 1) / chunk_min + 2 <= RAGGED_SLOTS.  The split and merge kernels derive the same cut from the lengths.
 constexpr int RAGGED_MAX_B = 512;     // sequences: one wave scans their lengths (8 per lane)
 constexpr int RAGGED_MIN_BH = 128;    // fewer items: the fixed plan's many short splits keep more waves busy
-constexpr int RAGGED_WAVES = 1024;    // waves of the cut (one per SIMD), more if chunks would exceed MAX_SPLIT_KEYS
+// Waves of the cut: one per SIMD, more if chunks would exceed MAX_SPLIT_KEYS.  Measured at B64 H16 on caches of
+// 4K-8K rows: 512, 768 and 1024 waves within 1% of each other (T = 4: 515 us), 1536 3% and 2048 5% slower.
+constexpr int RAGGED_WAVES = 1024;
 constexpr int RAGGED_SLOTS = MERGE_DIRECT_MAX;
 struct RaggedCut {
     int64_t total, chunk;   // keys of all items, keys per wave
@@ -521,9 +525,10 @@ static_assert(RAGGED_SLOTS <= MERGE_DIRECT_MAX, "one merge pass per item");
 // faster than many short ones, down to about a wave per SIMD.  Measured at one token on full caches (4 GiB at
 // B64 H16 L8192 or B16 H16 L32768, 0.5 GiB at B1 H16 L65536, B1 H1 L1M or B8 H16 L8192): splits of at most 4096
 // keys with at least ~512 waves were the fastest or within 1% of it (B64 H16 L8192: 640 us against 652 for one
-// 8192-key split per head; B1 H16 L65536: 89 us against 94 for at least 1024 waves).  Several tokens on ragged
-// caches take splits of up to 8192 keys and ~1024 waves (B64 H16, caches of 4K-8K rows, T = 4: splits of 1024 keys
-// 5.1 TB/s, 2048 5.7, 4096 5.85, one 8192-key split per head 5.93): a split's waves stop at its sequence's end.
+// 8192-key split per head; B1 H16 L65536: 89 us against 94 for at least 1024 waves).  Several tokens
+// take splits of up to 8192 keys and ~1024 waves.  On ragged caches this fixed plan leaves waves of unequal length
+// (B64 H16, caches of 4K-8K rows, T = 4: splits of 1024 keys 5.1 TB/s, 2048 5.7, 4096 5.85, one 8192-key split per
+// head 5.93); the balanced plan (ragged_plan) serves those calls where it applies: 6.4 TB/s there.
 SplitPlan plan_call(int64_t BH, int64_t L, int T) {
     return T == 1 ? plan_splits(BH, L, MAX_SPLIT_KEYS / 2, 512) : plan_splits(BH, L, MAX_SPLIT_KEYS, 1024);
 }
