@@ -423,7 +423,8 @@ constexpr int RAGGED_SLOTS = MERGE_DIRECT_MAX;
 struct RaggedCut {
     int64_t total, chunk;   // keys of all items, keys per wave
 };
-// By one wave: pre[0..B] (LDS) and the cut.  The caller makes pre visible before reading it (a barrier).
+// By one wave: pre[0..B] (LDS) and the cut.  The caller makes pre visible before reading it (a barrier), and reads
+// it through pre_at, so that the values, uniform across the wave, stay scalar (cache addresses derive from them).
 __device__ __forceinline__ RaggedCut ragged_cut(const int* __restrict__ lens, int B, int H, int T, int L, int waves,
                                                 int chunk_min, int* pre) {
     const int lane = threadIdx.x;
@@ -437,12 +438,14 @@ __device__ __forceinline__ RaggedCut ragged_cut(const int* __restrict__ lens, in
             if (lane >= o) x += y;
         }
         if (b < B) pre[b + 1] = carry + x;
-        carry += __shfl(x, 63);
+        carry += __builtin_amdgcn_readlane(x, 63);
     }
     if (lane == 0) pre[0] = 0;
     const int64_t total = (int64_t)H * carry;
     return RaggedCut{total, max((total + waves - 1) / waves, (int64_t)chunk_min)};
 }
+
+__device__ __forceinline__ int pre_at(const int* pre, int i) { return __builtin_amdgcn_readfirstlane(pre[i]); }
 
 template <bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_ragged_mfma_kernel(
@@ -462,11 +465,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     int b = 0;
     for (int hi = B - 1; b < hi;) {
         const int mid = (b + hi + 1) >> 1;
-        if ((int64_t)H * pre[mid] <= start) b = mid;
+        if ((int64_t)H * pre_at(pre, mid) <= start) b = mid;
         else hi = mid - 1;
     }
-    int64_t item0 = (int64_t)H * pre[b];
-    int len = pre[b + 1] - pre[b];
+    int64_t item0 = (int64_t)H * pre_at(pre, b);
+    int len = pre_at(pre, b + 1) - pre_at(pre, b);
     int h = (int)((start - item0) / len);
     int off = (int)(start - item0 - (int64_t)h * len);
     for (int64_t pos = start;;) {
@@ -482,8 +485,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         if (++h == H) {
             h = 0;
             ++b;
-            item0 = (int64_t)H * pre[b];
-            len = pre[b + 1] - pre[b];
+            item0 = (int64_t)H * pre_at(pre, b);
+            len = pre_at(pre, b + 1) - pre_at(pre, b);
         }
     }
 }
@@ -497,8 +500,8 @@ __global__ __launch_bounds__(64) void decode_ragged_merge_kernel(const float* __
     __syncthreads();
     const int item = blockIdx.x;
     const int bh = item / T, b = bh / H, h = bh % H;
-    const int len = pre[b + 1] - pre[b];
-    const int64_t P = (int64_t)H * pre[b] + (int64_t)h * len;
+    const int len = pre_at(pre, b + 1) - pre_at(pre, b);
+    const int64_t P = (int64_t)H * pre_at(pre, b) + (int64_t)h * len;
     const int nseg = (int)((P + len - 1) / cut.chunk - P / cut.chunk + 1);
     merge_partial_row(ws + (size_t)item * slots * PART_FLOATS, nseg, ep, bh, gout + (size_t)item * DV,
                       (int)threadIdx.x);
