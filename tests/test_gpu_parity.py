@@ -623,6 +623,28 @@ def test_decode_varlen_per_head_lambda():
     check_bf16(host_bf16(out), ref, "decode varlen per-head")
 
 
+def test_decode_ragged_balanced_per_head_lambda():
+    """Per-head lambda on the balanced plan (B4 H32: 128 items), one value per head from 0 to 0.95, against the oracle;
+    and the scalar entry point's bits when every head holds the same value."""
+    torch = torch_mod()
+    B, H, T, L = 4, 32, 2, 900
+    inp = varlen_inputs(B, H, T, L, seed=660)
+    lens = np.array([900, 37, 512, 899], dtype=np.int32)
+    lam_h = np.linspace(0.0, 0.95, H).astype(np.float32)
+    say(f"case: decode ragged balanced per-head lambda B{B} H{H} T{T} L{L} lens {lens.tolist()}")
+    dev = {k: dev_bf16(v) for k, v in inp.items()}
+    ldev = torch.from_numpy(lens).to("cuda:0")
+    out = da.diffattn_decode_varlen(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], dev_lam(lam_h), 2,
+                                    lens=ldev)
+    one = da.diffattn_decode_varlen(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"],
+                                    dev_lam(np.full(H, 0.6, dtype=np.float32)), 2, lens=ldev)
+    scalar = da.diffattn_decode_varlen(dev["q1"], dev["k1"], dev["q2"], dev["k2"], dev["v"], 0.6, 2, lens=ldev)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), scalar.view(torch.int16))
+    ref = varlen_reference(widen(inp), T, L, lens, lam_h.astype(np.float64), 2)
+    check_bf16(host_bf16(out), ref, "decode ragged balanced per-head")
+
+
 def strided_caches(dev, layout):
     """Views of the same cache rows in another memory layout: 'token' = each cache token-major ([B][L][H][w]);
     'packed' = K1, K2 and V of a row side by side in one [B][L][H][d + d + 2d] buffer."""
